@@ -1,0 +1,345 @@
+"""Pins for the CPU oracle: closed forms, invariants, brute force and the
+hand-worked fixtures under tests/golden/.  None of these re-types an oracle
+formula; each checks the oracle against something the pages or the
+mathematics fix independently.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + math.exp(-x))
+
+
+# ---------------------------------------------------------------------------
+# window score (ZigZagkv page, Eq. 7)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G,w,n,d,q_pos0", [(2, 8, 512, 64, 504), (4, 3, 37, 16, 34),
+                                             (1, 1, 9, 8, 100), (3, 5, 20, 8, 2)])
+def test_score_mass_sums_to_rows(G, w, n, d, q_pos0):
+    # every softmax row sums to one, so the scores of one KV head sum to G*w
+    r = np.random.default_rng(1)
+    s = oracle.window_scores(r.standard_normal((G, w, d)), r.standard_normal((n, d)),
+                             1 / math.sqrt(d), q_pos0)
+    assert s.shape == (n,)
+    assert abs(s.sum() - G * w) < 1e-10
+    assert (s >= 0).all()
+    # keys no window row can see get nothing
+    assert np.all(s[np.arange(n) > q_pos0 + w - 1] == 0)
+
+
+def test_score_zero_query_is_uniform_over_visible_keys():
+    # q = 0 makes every visible logit equal: row i puts 1/(q_pos0+i+1) on keys 0..q_pos0+i
+    G, w, n, d = 3, 4, 11, 5
+    q_pos0 = n - w
+    s = oracle.window_scores(np.zeros((G, w, d)), np.random.default_rng(2).standard_normal((n, d)),
+                             0.37, q_pos0)
+    want = np.zeros(n)
+    for i in range(w):
+        want[:q_pos0 + i + 1] += G / (q_pos0 + i + 1)
+    np.testing.assert_allclose(s, want, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("a,c,scale", [(1.5, 2.0, 0.125), (-0.7, 3.0, 1 / math.sqrt(128)),
+                                       (4.0, -1.0, 1.0)])
+def test_score_two_key_logistic(a, c, scale):
+    # two keys, one query: logits (scale*a*c, 0) give weights sigmoid(+-scale*a*c)
+    d = 4
+    k = np.zeros((2, d)); k[0, 1] = a
+    q = np.zeros((1, 1, d)); q[0, 0, 1] = c
+    s = oracle.window_scores(q, k, scale, q_pos0=1)
+    x = scale * a * c
+    assert abs(s[0] - _sigmoid(x)) < 1e-15
+    assert abs(s[1] - _sigmoid(-x)) < 1e-15
+
+
+def test_score_gqa_heads_add():
+    # head 0 has q = 0 (uniform 1/n), head 1 points at key 2 with logit x
+    n, d, x = 6, 3, 2.5
+    k = np.zeros((n, d)); k[2, 0] = 1.0
+    q = np.zeros((2, 1, d)); q[1, 0, 0] = x
+    s = oracle.window_scores(q, k, 1.0, q_pos0=n - 1)
+    den = math.exp(x) + n - 1
+    want = np.full(n, 1.0 / n + 1.0 / den)
+    want[2] = 1.0 / n + math.exp(x) / den
+    np.testing.assert_allclose(s, want, rtol=0, atol=1e-15)
+
+
+def test_score_causal_boundary():
+    # the first window row must not see the key right after its own position
+    n, d = 8, 2
+    k = np.zeros((n, d)); k[5, 0] = 50.0     # a key that would dominate if visible
+    q = np.zeros((1, 2, d)); q[0, :, 0] = 1.0
+    s = oracle.window_scores(q, k, 1.0, q_pos0=4)   # rows at positions 4 and 5
+    # row 0 (pos 4) is uniform over keys 0..4; row 1 (pos 5) is almost all on key 5
+    den = math.exp(50.0) + 5
+    want = np.zeros(n)
+    want[:5] = 1 / 5 + 1 / den
+    want[5] = math.exp(50.0) / den
+    np.testing.assert_allclose(s, want, rtol=1e-15, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# LMBA (ZigZagkv page, Eq. 3)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", list(range(1, 41)) + [100, 1000])
+def test_lmba_uniform_row_is_ceil_nine_tenths(n):
+    assert oracle.lmba_row(np.full(n, 1.0 / n)) == math.ceil(Fraction(9, 10) * n)
+
+
+@pytest.mark.parametrize("n,hot", [(1, 0), (7, 3), (512, 511)])
+def test_lmba_one_hot(n, hot):
+    row = np.zeros(n); row[hot] = 1.0
+    assert oracle.lmba_row(row) == 1
+
+
+def test_lmba_golden_rows():
+    g = _load("lmba.json")
+    mass = Fraction(g["mass"])
+    for case in g["rows"]:
+        row = [Fraction(v) for v in case["row"]]
+        assert oracle.lmba_row(row, mass) == case["expect"], case
+
+
+def test_layer_lmba_mean_of_rows():
+    rows = [np.full(10, 0.1), np.array([1.0, 0, 0]), np.array([0.5, 0.3, 0.2])]
+    assert oracle.layer_lmba(rows) == pytest.approx((9 + 1 + 3) / 3, abs=0)
+
+
+# ---------------------------------------------------------------------------
+# bounded budgets (ZigZagkv page, Eq. 4 + Eq. 6)
+# ---------------------------------------------------------------------------
+
+def test_budgets_golden():
+    for case in _load("zigzag_budgets.json")["cases"]:
+        got = oracle.zigzag_budgets(case["profile"], case["n"], case["avg_budget"],
+                                    case["floor_budget"])
+        assert got.tolist() == case["expect"], case["name"]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_budgets_sum_floor_cap(seed):
+    r = np.random.default_rng(seed)
+    L = int(r.integers(1, 40))
+    n = int(r.integers(50, 40000))
+    B = int(r.integers(1, n + 1))
+    F = int(r.integers(0, B + 1))
+    prof = r.lognormal(0, float(r.uniform(0.1, 2.0)), size=L)
+    b = oracle.zigzag_budgets(prof, n, B, F)
+    assert b.sum() == L * B
+    assert (b >= F).all() and (b <= n).all()
+    # more uncertain layers never get fewer tokens (Eq. 6 is increasing in u_l),
+    # up to the one unit the rounding can move
+    order = np.argsort(prof, kind="stable")
+    assert np.all(np.diff(b[order]) >= -1)
+
+
+def test_budgets_c2_shape():
+    # C2: 32 layers, n = 32768, mean 20 % (6553) and floor 5 % (1639)
+    import kvsynth
+    cfg = kvsynth.get_config(2)
+    b = oracle.zigzag_budgets(kvsynth.zigzag_profile(cfg), cfg.n, cfg.avg_budget,
+                              cfg.floor_budget)
+    assert cfg.avg_budget == 6553 and cfg.floor_budget == 1639
+    assert b.sum() == 32 * 6553 and b.min() >= 1639 and b.max() <= 32768
+    assert len(set(b.tolist())) > 10          # genuinely non-uniform
+
+
+def test_budgets_reject_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.zigzag_budgets([1, 2], 100, 10, 11)      # floor above average
+    with pytest.raises(ValueError):
+        oracle.zigzag_budgets([1, 2], 100, 101, 0)      # average above n
+    with pytest.raises(ValueError):
+        oracle.zigzag_budgets([1, 0], 100, 10, 1)       # non-positive profile
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+def _brute_topb(scores, B):
+    """Among all B-subsets take the max-sum one, ties broken by the
+    lexicographically smallest sorted index tuple (integer scores: exact)."""
+    n = len(scores)
+    B = min(B, n)
+    best = None
+    for sub in itertools.combinations(range(n), B):
+        key = (-sum(scores[j] for j in sub), sub)
+        if best is None or key < best:
+            best = key
+    return list(best[1]) if best else []
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_topb_brute_force_with_ties(seed):
+    r = np.random.default_rng(100 + seed)
+    n = int(r.integers(1, 11))
+    scores = [int(v) for v in r.integers(0, 4, size=n)]   # small ints force ties
+    B = int(r.integers(0, n + 2))
+    got = oracle.select_topb(np.array(scores, np.float64), B).tolist()
+    assert got == _brute_topb(scores, B)
+
+
+def test_topb_golden():
+    for case in _load("select.json")["topb"]:
+        s = np.array([float(v) for v in case["scores"]])
+        assert oracle.select_topb(s, case["budget"]).tolist() == case["expect"], case["why"]
+
+
+def test_topb_budget_n_keeps_all():
+    s = np.random.default_rng(5).standard_normal(300)
+    assert oracle.select_topb(s, 300).tolist() == list(range(300))
+
+
+def _chunk_properties(cs, ends, target, kept):
+    starts = np.concatenate([[0], ends[:-1]])
+    lens = ends - starts
+    chosen = sorted({int(np.searchsorted(ends, t, side="right")) for t in kept})
+    # whole chunks
+    want = np.concatenate([np.arange(starts[c], ends[c]) for c in chosen]) if chosen else []
+    assert list(kept) == list(want)
+    if target <= 0:
+        assert not chosen
+        return
+    tot = int(lens[chosen].sum())
+    assert tot >= min(target, int(lens.sum()))
+    # every chosen chunk ranks above every unchosen one (score desc, index asc)
+    rank = lambda c: (-cs[c], c)
+    unchosen = [c for c in range(len(cs)) if c not in chosen]
+    if unchosen:
+        assert max(rank(c) for c in chosen) < min(rank(c) for c in unchosen)
+    # minimal: dropping the lowest-ranked chosen chunk falls short
+    worst = max(chosen, key=rank)
+    assert tot - lens[worst] < target
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_chunk_selection_properties(seed):
+    r = np.random.default_rng(200 + seed)
+    nc = int(r.integers(1, 30))
+    ends = np.cumsum(r.integers(1, 9, size=nc)).astype(np.int64)
+    cs = r.integers(0, 5, size=nc).astype(np.float64)
+    target = int(r.integers(0, ends[-1] + 3))
+    kept = oracle.select_chunks(cs, ends, target)
+    _chunk_properties(cs, ends, target, kept)
+
+
+def test_chunk_golden():
+    for case in _load("select.json")["chunk"]:
+        got = oracle.select_chunks(np.array(case["chunk_scores"], float),
+                                   np.array(case["chunk_end"]), case["keep_tokens"])
+        assert got.tolist() == case["expect"], case["why"]
+
+
+def test_policy_golden():
+    kinds = {"global": oracle.HEAD_GLOBAL, "local": oracle.HEAD_LOCAL,
+             "special": oracle.HEAD_SPECIAL}
+    for case in _load("select.json")["policy"]:
+        got = oracle.select_policy(kinds[case["kind"]], case["n"], case["local_window"],
+                                   case["special_pos"])
+        assert got.tolist() == case["expect"]
+
+
+# ---------------------------------------------------------------------------
+# compaction
+# ---------------------------------------------------------------------------
+
+def test_compact_identity_and_empty():
+    r = np.random.default_rng(3)
+    K = r.integers(0, 65535, size=(20, 8), dtype=np.uint16)
+    V = r.integers(0, 65535, size=(20, 8), dtype=np.uint16)
+    Kc, Vc = oracle.compact(K, V, np.arange(20))
+    assert np.array_equal(Kc, K) and np.array_equal(Vc, V)
+    Kc, Vc = oracle.compact(K, V, np.zeros(0, np.int64))
+    assert Kc.shape == (0, 8) and Vc.shape == (0, 8)
+    Kc, _ = oracle.compact(K, V, np.array([19, 0]))
+    assert np.array_equal(Kc[0], K[19]) and np.array_equal(Kc[1], K[0])
+
+
+# ---------------------------------------------------------------------------
+# decode attention (RAP page, Fig. 2 / Eq. 2) and the split combine
+# ---------------------------------------------------------------------------
+
+def test_decode_one_row_returns_that_value():
+    r = np.random.default_rng(4)
+    v = r.standard_normal((1, 16))
+    out = oracle.decode_attention(r.standard_normal(16), r.standard_normal((1, 16)), v, 0.3)
+    np.testing.assert_array_equal(out, v[0])
+
+
+def test_decode_identical_keys_average_values():
+    r = np.random.default_rng(5)
+    k = np.tile(r.standard_normal(8), (9, 1))
+    V = r.standard_normal((9, 8))
+    out = oracle.decode_attention(r.standard_normal(8), k, V, 0.5)
+    np.testing.assert_allclose(out, V.mean(0), rtol=0, atol=1e-14)
+
+
+def test_decode_two_key_logistic():
+    d, a, c, scale = 4, 1.25, -2.0, 0.25
+    K = np.zeros((2, d)); K[1, 3] = a
+    q = np.zeros(d); q[3] = c
+    V = np.array([[1.0, 0, 0, 0], [0, 0, 0, 1.0]])
+    out = oracle.decode_attention(q, K, V, scale)
+    p1 = _sigmoid(scale * a * c)
+    np.testing.assert_allclose(out, [1 - p1, 0, 0, p1], rtol=0, atol=1e-15)
+
+
+def test_decode_empty_cache_is_zero():
+    out = oracle.decode_attention(np.ones(8), np.zeros((0, 8)), np.zeros((0, 8)), 1.0)
+    assert out.shape == (8,) and not out.any()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_split_combine_matches_unsplit(seed):
+    r = np.random.default_rng(300 + seed)
+    n, d = int(r.integers(2, 400)), 32
+    q = 3 * r.standard_normal(d)
+    K, V = r.standard_normal((n, d)), r.standard_normal((n, d))
+    cuts = np.sort(r.choice(np.arange(1, n), size=min(n - 1, int(r.integers(1, 6))),
+                            replace=False))
+    parts = [oracle.decode_partial(q, K[a:b], V[a:b], 0.2)
+             for a, b in zip(np.r_[0, cuts], np.r_[cuts, n])]
+    np.testing.assert_allclose(oracle.combine_partials(parts),
+                               oracle.decode_attention(q, K, V, 0.2), rtol=0, atol=1e-12)
+
+
+def test_full_budget_reproduces_full_attention():
+    # budget = n keeps every token, so decode over the compacted cache is full attention
+    r = np.random.default_rng(6)
+    n, d = 50, 16
+    K, V, q = r.standard_normal((n, d)), r.standard_normal((n, d)), r.standard_normal(d)
+    s = oracle.window_scores(r.standard_normal((2, 3, d)), K, 0.25, n - 3)
+    idx = oracle.select_topb(s, n)
+    Kc, Vc = oracle.compact(K, V, idx)
+    full = oracle.decode_attention(q, K, V, 0.25)
+    np.testing.assert_array_equal(oracle.decode_attention(q, Kc, Vc, 0.25), full)
+    # and against softmax written with the log-sum-exp identity on the uncompacted cache
+    logits = 0.25 * K @ q
+    lse = np.log(np.sum(np.exp(logits - logits.max()))) + logits.max()
+    np.testing.assert_allclose(full, np.exp(logits - lse) @ V, rtol=0, atol=1e-12)
+
+
+def test_bf16_widening_exact():
+    words = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x8000, 0x7F7F], np.uint16)
+    got = oracle.to_f64(words)
+    assert got.tolist()[:5] == [1.0, -1.0, 3.140625, 0.0, -0.0]
+    assert got[5] == 255 * 2.0 ** 120          # largest finite bf16, (2 - 2^-7) * 2^127
