@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = the whole hot path over the 32-layer, 32K-context,
+batch-4 Llama-3-8B-shaped workload with per-layer bounded budgets:
+
+  per layer   window score -> top-B select -> gather-compact
+  then        one decode step through all 32 layers over the compacted caches
+  (plus the host-side per-layer budget computation)
+
+Inputs are synthetic (seeded generator), resident in HBM before timing.  HIP
+events around every entry point give per-stage times; the reported value is
+the decode attention's algorithmic HBM bandwidth.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+METRIC = "compacted decode-attn HBM GB/s (% peak) + select-and-compact µs/layer, 32K ctx"
+COUNTERS = os.path.join(ROOT, "profiles", "decode_c2_counters.json")
+DECODE_SRC = os.path.join(ROOT, "sparse_decode_attention_window_amd", "csrc", "decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(cfg, budgets, seconds: float) -> dict:
+    """The oracle, as it is, on whole segments of layer 0 until `seconds` pass."""
+    import kvsynth
+    import oracle
+    G, w, d, n = cfg.G, cfg.w, cfg.d, cfg.n
+    t_stage = {"score": 0.0, "select": 0.0, "compact": 0.0, "decode": 0.0}
+    dec_bytes = 0
+    segs = 0
+    t_start = time.perf_counter()
+    for s in range(cfg.batch * cfg.hkv):
+        b, kvh = divmod(s, cfg.hkv)
+        x = kvsynth.segment_inputs(cfg, 0, b, kvh)
+        B = int(budgets[0])
+        t = time.perf_counter()
+        sc = oracle.window_scores(oracle.to_f64(x["q_win"]), oracle.to_f64(x["K"]), cfg.scale,
+                                  n - w)
+        t_stage["score"] += time.perf_counter() - t
+        t = time.perf_counter()
+        keep = oracle.select_topb(sc, B)
+        t_stage["select"] += time.perf_counter() - t
+        t = time.perf_counter()
+        Kc, Vc = oracle.compact(x["K"], x["V"], keep)
+        t_stage["compact"] += time.perf_counter() - t
+        t = time.perf_counter()
+        Kc64, Vc64 = oracle.to_f64(Kc), oracle.to_f64(Vc)
+        qd = oracle.to_f64(x["q_dec"])
+        for g in range(G):
+            oracle.decode_attention(qd[g], Kc64, Vc64, cfg.scale)
+        t_stage["decode"] += time.perf_counter() - t
+        dec_bytes += keep.size * d * cfg.es * 2 + G * d * (cfg.es + 4)
+        segs += 1
+        if time.perf_counter() - t_start >= seconds:
+            break
+    segs_per_layer = cfg.batch * cfg.hkv
+    return {
+        "value": dec_bytes / t_stage["decode"] / 1e9,
+        "unit": "GB/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle on {segs} whole (batch, KV head) segment(s) of layer 0 "
+                   f"(score, select, compact, decode of {G} query heads each); decode GB/s over "
+                   f"the same algorithmic bytes as the GPU; host os.cpu_count()={os.cpu_count()}"),
+        "select_and_compact_us_per_layer_est": (t_stage["select"] + t_stage["compact"]) / segs
+        * segs_per_layer * 1e6,
+        "stage_s_per_segment": {k: v / segs for k, v in t_stage.items()},
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path needs no collective; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import kvsynth
+    import sparse_decode_attention_window_amd as kvsel
+    from sparse_decode_attention_window_amd import pipeline
+
+    kvsel.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = kvsynth.get_config(2)
+    L = cfg.layers
+    profile = kvsynth.zigzag_profile(cfg)
+    budgets = kvsel.kvsel_zigzag_budgets(profile, cfg.n, cfg.avg_budget, cfg.floor_budget)
+
+    log(f"[bench] generating {cfg.name}: {L} layers x batch {cfg.batch} x {cfg.hkv} KV heads "
+        f"x {cfg.n} tokens x d {cfg.d} ({cfg.dtype})")
+    t0 = time.perf_counter()
+    layers = []
+    for l in range(L):
+        inputs = kvsynth.layer_inputs(cfg, l)
+        layers.append(pipeline.build_layer(cfg, inputs, budget=budgets[l]))
+        del inputs
+        if l % 4 == 3:
+            log(f"[bench] layer {l + 1}/{L} resident ({time.perf_counter() - t0:.1f} s)")
+    torch.cuda.synchronize()
+
+    def step(ev):
+        bud = kvsel.kvsel_zigzag_budgets(profile, cfg.n, cfg.avg_budget, cfg.floor_budget)
+        assert bud == budgets
+        for l, run in enumerate(layers):
+            ev[l][0].record()
+            run.score()
+            ev[l][1].record()
+            run.select()
+            ev[l][2].record()
+            run.compact()
+            ev[l][3].record()
+        for l, run in enumerate(layers):
+            ev[l][4].record()
+            run.decode()
+            ev[l][5].record()
+
+    def events():
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
+
+    for i in range(args.warmup):
+        step(events())
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    evs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"[bench] timed {args.steps} steps in {wall:.3f} s")
+
+    # per-stage GPU times (ms), summed over layers, averaged over steps
+    st = {"score": 0.0, "select": 0.0, "compact": 0.0, "decode": 0.0}
+    for ev in evs:
+        for l in range(L):
+            st["score"] += ev[l][0].elapsed_time(ev[l][1])
+            st["select"] += ev[l][1].elapsed_time(ev[l][2])
+            st["compact"] += ev[l][2].elapsed_time(ev[l][3])
+            st["decode"] += ev[l][4].elapsed_time(ev[l][5])
+    launches = args.steps * L
+    us = {k: v / launches * 1e3 for k, v in st.items()}       # µs per layer launch
+
+    es, d, B, hq, hkv, n = cfg.es, cfg.d, cfg.batch, cfg.hq, cfg.hkv, cfg.n
+    rows = [int(layers[l].seg_len.sum().item()) for l in range(L)]
+    assert rows == [B * hkv * b for b in budgets]
+    mean_rows = sum(rows) / L
+    dec_bytes = mean_rows * d * es * 2 + B * hq * d * (es + 4)
+    cmp_bytes = mean_rows * (d * es * 4 + 4)
+    sc_bytes = B * hkv * n * d * es + B * hq * cfg.w * d * es + B * hkv * n * 4
+    sel_bytes = B * hkv * n * 4 + mean_rows * 4
+    sc_flops_alg = 2.0 * B * hq * cfg.w * n * d
+    gbs = lambda b, t_us: b / (t_us * 1e-6) / 1e9
+
+    dec_gbs = gbs(dec_bytes, us["decode"])
+    traffic = None
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as f:
+            cnt = json.load(f)
+        if cnt.get("source_sha256_16") == src_hash(DECODE_SRC):
+            traffic = cnt.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator: planted sink + per-layer heavy hitters + recency; "
+                "lognormal(0,0.5) layer-uncertainty profile)",
+        "config": {"workload": cfg.name, "layers": L, "batch": B, "hq": hq, "hkv": hkv,
+                   "head_dim": d, "context": n, "window": cfg.w,
+                   "avg_budget": cfg.avg_budget, "floor_budget": cfg.floor_budget,
+                   "parallelism": "single GPU"},
+        "pct_peak_hbm": round(100 * dec_gbs / PEAK_HBM_GBS, 1),
+        "select_and_compact_us_per_layer": round(us["select"] + us["compact"], 2),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": "kvsel_decode_attn (split + combine)",
+                     "algorithmic_bytes_per_launch": int(dec_bytes),
+                     "avg_launch_us": round(us["decode"], 3)},
+        "stages_us_per_layer": {k: round(v, 3) for k, v in us.items()},
+        "stages_roofline": {
+            "score": {"bound": "hbm", "GB/s": round(gbs(sc_bytes, us["score"]), 1),
+                      "frac": round(gbs(sc_bytes, us["score"]) / PEAK_HBM_GBS, 4),
+                      "mfma_TFLOP/s_2pass": round(2 * sc_flops_alg / (us["score"] * 1e-6) / 1e12, 1),
+                      "mfma_frac_2pass": round(2 * sc_flops_alg / (us["score"] * 1e-6) / 1e12
+                                               / PEAK_BF16_TFLOPS, 4),
+                      "algorithmic_bytes": int(sc_bytes)},
+            "select": {"GB/s": round(gbs(sel_bytes, us["select"]), 1),
+                       "algorithmic_bytes": int(sel_bytes)},
+            "compact": {"bound": "hbm", "GB/s": round(gbs(cmp_bytes, us["compact"]), 1),
+                        "frac": round(gbs(cmp_bytes, us["compact"]) / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes": int(cmp_bytes)},
+            "decode": {"bound": "hbm", "GB/s": round(dec_gbs, 1),
+                       "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                       "algorithmic_bytes": int(dec_bytes)},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, budgets, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

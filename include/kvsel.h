@@ -1,0 +1,185 @@
+/*
+ * kvsel.h -- attention-mass KV selection and compacted decode attention on
+ * AMD Instinct MI355X (gfx950).  C ABI; every entry point is asynchronous on
+ * the HIP stream it is given.
+ *
+ * Pipeline (one transformer layer, per batch element b and KV head kvh;
+ * "segment" s = b * hkv + kvh):
+ *
+ *   kvsel_score        window-mass score of every cached key
+ *   kvsel_select       keep tokens per segment (top-B, chunk top-k or head policy)
+ *   kvsel_compact      gather kept K/V rows into a packed variable-length cache
+ *   kvsel_decode_attn  single-token GQA decode attention over that cache
+ *   kvsel_zigzag_budgets  (host) bounded per-layer budgets
+ *
+ * Sources, cited by page title and the equation / section on it:
+ *   ZigZagkv: Dynamic KV Cache Compression for Long-context Modeling based on
+ *     Layer Uncertainty (arXiv 2412.09036): Eq. 7 token score, Eq. 4 and
+ *     Eq. 6 bounded layer budgets.
+ *   Model Tells You What to Discard: Adaptive KV Cache Compression for LLMs
+ *     (arXiv 2310.01801): local / special-token / global head policies.
+ *   ChunkLLM: A Lightweight Pluggable Framework for Accelerating LLMs
+ *     Inference (arXiv 2510.02361): §2.2 Eq. 3 chunk attention over
+ *     compressed chunk keys; only top-k chunks stay in the KV cache.
+ *   RAP: KV-Cache Compression via RoPE-Aligned Pruning (arXiv 2602.02599):
+ *     Fig. 2 / Eq. 2 decode-step attention; pair-pruned head dims (88).
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *     memory; the library never allocates, frees or synchronises.
+ *   - Dense tensors are row-major and contiguous with the shapes given.
+ *     Element type of q / K / V follows kvsel_shape.dtype (bf16 = 16-bit
+ *     brain float words, fp32 = IEEE single); scores and outputs are fp32.
+ *   - Argument checks run on the host before anything is enqueued.  A failed
+ *     check returns KVSEL_EINVAL / KVSEL_EUNSUPPORTED / KVSEL_ENOSPC and
+ *     enqueues nothing.  A failed launch returns KVSEL_EHIP.  The message of
+ *     the last non-OK status of the calling thread is kvsel_last_error().
+ *   - Preconditions on device data (indices in range, segments not
+ *     overlapping, chunk ends increasing) are documented, not checked; the
+ *     kernels still never read or write outside the buffers described by the
+ *     host-side sizes.
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVSEL_OK = 0,
+  KVSEL_EINVAL = 1,       /* bad argument (null pointer, bad size or shape) */
+  KVSEL_EUNSUPPORTED = 2, /* head_dim / dtype / group size not built */
+  KVSEL_ENOSPC = 3,       /* workspace smaller than the matching *_workspace() */
+  KVSEL_EHIP = 4          /* a HIP runtime call or kernel launch failed */
+} kvsel_status;
+
+typedef enum { KVSEL_FP32 = 0, KVSEL_BF16 = 1 } kvsel_dtype;
+
+/* Shape of one layer's attention.
+ *   batch, hq, hkv : batch size, query heads, KV heads; hq % hkv == 0 and the
+ *                    group size G = hq / hkv is at most 8; query head h reads
+ *                    KV head h / G.
+ *   head_dim       : 64, 88 or 128 (88 = RAP pair-pruned layout).
+ *   n              : cached keys per (batch, KV head); for chunk scoring the
+ *                    number of chunk keys.  1 <= n < 2^31.
+ *   dtype          : kvsel_dtype of q / K / V.
+ *   scale          : softmax scale applied to q . k (usually 1/sqrt(head dim
+ *                    of the unpruned model)). */
+typedef struct {
+  int32_t batch, hq, hkv, head_dim;
+  int64_t n;
+  int32_t dtype;
+  float scale;
+} kvsel_shape;
+
+/* ---------------------------------------------------------------- score --
+ * ZigZagkv page, Eq. 7: the score of key j is the attention weight that the
+ * last w queries put on it, summed over those queries and (GQA) over the G
+ * query heads that share the KV head:
+ *   scores[b][kvh][j] = sum_{g<G} sum_{i<w} softmax_j'(scale q_{b,kvh*G+g,i} . k_{b,kvh,j'})[j]
+ * where window query i sees keys j' <= q_pos0 + i (causal); pass
+ * q_pos0 >= n - 1 for no mask.  The same call scores ChunkLLM chunk keys
+ * (w = 1, keys = compressed chunk keys, head_dim 64).
+ *   q_win   [batch][hq][w][head_dim]
+ *   k       [batch][hkv][n][head_dim]
+ *   scores  [batch][hkv][n] fp32 (out)
+ *   ws      workspace of at least kvsel_score_workspace(s, w) bytes
+ * Constraints: 1 <= w, G*w <= 256, q_pos0 >= 0.  Each row of scores sums to
+ * G*w up to rounding. */
+size_t kvsel_score_workspace(const kvsel_shape* s /*host*/, int32_t w);
+kvsel_status kvsel_score(const kvsel_shape* s /*host*/, int32_t w, int64_t q_pos0,
+                         const void* q_win, const void* k, float* scores,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------- select --
+ * Writes, per segment s, the kept token positions in ascending order to
+ * idx[seg_off[s] .. seg_off[s] + seg_len[s]) and their count to seg_len[s].
+ * Score order is (score descending, index ascending); NaN orders below every
+ * number and -0 equals +0.
+ *   TOPB   (ZigZagkv page, Eq. 7 + Eq. 6): keep the min(budget[s], n)
+ *          highest-score tokens.  scores [batch][hkv][n].
+ *   CHUNK  (ChunkLLM page, §2.2-§2.3): chunks are taken in score order until
+ *          their token count reaches keep_tokens; kept chunks are whole and
+ *          expanded to their token positions.  scores [batch][hkv][n_chunks];
+ *          chunk c of batch b covers [chunk_end[b][c-1], chunk_end[b][c]).
+ *   POLICY (FastGen page, core claim): per KV head kind: GLOBAL keeps all n,
+ *          LOCAL keeps the last min(local_window, n), SPECIAL keeps
+ *          special_pos[b][0 .. n_special).  scores unused (may be NULL).
+ * seg_off [batch*hkv] int64: first row of each segment in idx (and in the
+ *          compacted cache).  Precondition: seg_off[s] + kept_s does not reach
+ *          into another segment.  Rows at or beyond r_cap are never written
+ *          (seg_len still reports the full count).  */
+typedef enum { KVSEL_SEL_TOPB = 0, KVSEL_SEL_CHUNK = 1, KVSEL_SEL_POLICY = 2 } kvsel_sel_mode;
+typedef enum { KVSEL_HEAD_GLOBAL = 0, KVSEL_HEAD_LOCAL = 1, KVSEL_HEAD_SPECIAL = 2 } kvsel_head_kind;
+
+typedef struct {
+  int32_t mode;                 /* kvsel_sel_mode */
+  const int32_t* budget;        /* TOPB:   [batch*hkv] tokens per segment (clamped to [0, n]) */
+  int64_t n_chunks;             /* CHUNK:  chunks per sequence, >= 1 */
+  const int64_t* chunk_end;     /* CHUNK:  [batch][n_chunks], strictly increasing, last == n */
+  int64_t keep_tokens;          /* CHUNK:  token target per segment */
+  const int8_t* head_kind;      /* POLICY: [hkv] kvsel_head_kind */
+  int64_t local_window;         /* POLICY: tokens LOCAL heads keep, >= 0 */
+  const int32_t* special_pos;   /* POLICY: [batch][n_special], ascending, unique, in [0, n) */
+  int64_t n_special;            /* POLICY: entries per batch element, >= 0 */
+} kvsel_select_params;
+
+kvsel_status kvsel_select(const kvsel_shape* s /*host*/, const kvsel_select_params* p /*host*/,
+                          const float* scores, const int64_t* seg_off, int32_t* seg_len,
+                          int32_t* idx, int64_t r_cap, hipStream_t stream);
+
+/* -------------------------------------------------------------- compact --
+ * Packed variable-length cache: for every segment s and r < seg_len[s],
+ *   k_c[seg_off[s] + r] = k[b][kvh][idx[seg_off[s] + r]]   (bit-exact copy)
+ * and likewise v_c from v.  Rows of segments are clipped at r_cap; an index
+ * outside [0, n) yields a zero row.
+ *   k, v      [batch][hkv][n][head_dim]
+ *   k_c, v_c  [r_cap][head_dim] (out) */
+kvsel_status kvsel_compact(const kvsel_shape* s /*host*/, const void* k, const void* v,
+                           const int64_t* seg_off, const int32_t* seg_len, const int32_t* idx,
+                           void* k_c, void* v_c, int64_t r_cap, hipStream_t stream);
+
+/* --------------------------------------------------------------- decode --
+ * RAP page Fig. 2 / Eq. 2 decode step over the compacted cache:
+ *   out[b][h] = sum_{r < len} softmax_r(scale q[b][h] . k_c[off + r]) v_c[off + r]
+ * with off = seg_off[b*hkv + h/G], len = seg_len[...] (clipped at r_cap).
+ * Split-K: every segment is cut into row chunks processed in parallel; each
+ * chunk keeps (running max, sum of exponentials, weighted value sum) and a
+ * second pass merges them.  An empty segment gives a zero output row.
+ *   q    [batch][hq][head_dim]
+ *   k_c, v_c [r_cap][head_dim]
+ *   out  [batch][hq][head_dim] fp32 (out)
+ *   ws   at least kvsel_decode_workspace(s, r_cap) bytes */
+size_t kvsel_decode_workspace(const kvsel_shape* s /*host*/, int64_t r_cap);
+kvsel_status kvsel_decode_attn(const kvsel_shape* s /*host*/, const void* q, const void* k_c,
+                               const void* v_c, const int64_t* seg_off, const int32_t* seg_len,
+                               int64_t r_cap, float* out, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* --------------------------------------------------------------- budgets --
+ * ZigZagkv page, Eq. 4 and Eq. 6 (host only, no GPU work):
+ *   u_l = x_l / sum x;  beta_l = floor_budget + (avg_budget - floor_budget) * L * u_l
+ * Layers with beta_l > n are fixed at n and Eq. 6 is applied again to the
+ * rest with the remaining total.  Integer budgets: floor of beta, then the
+ * leftover units one each to the largest fractional parts (ties to the lower
+ * layer).  Result sums to L * avg_budget, each in [floor_budget, n].
+ *   profile (host) [L] finite, > 0;  out (host) [L]
+ * Errors: EINVAL unless 0 <= floor_budget <= avg_budget <= n and L >= 1. */
+kvsel_status kvsel_zigzag_budgets(const double* profile, int32_t L, int64_t n,
+                                  int64_t avg_budget, int64_t floor_budget, int32_t* out);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* kvsel_last_error(void);
+
+/* Library version string. */
+const char* kvsel_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVSEL_H */

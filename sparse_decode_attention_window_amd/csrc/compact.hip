@@ -1,0 +1,106 @@
+// Gather-compact: copy the kept K/V rows of every segment into one packed,
+// variable-length cache (only the selected tokens stay in the KV cache, as
+// on the ChunkLLM page, §2.3; per-head budgets as on the ZigZagkv page).
+//
+// The copy is flattened over (segment, row, 16-byte chunk) so the grid is
+// balanced however uneven the segment lengths are: consecutive lanes take
+// consecutive 16-byte chunks of the destination, so every store is fully
+// coalesced and every gathered source row is read as one contiguous run.
+#include "kvsel_internal.h"
+
+namespace kvsel {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // 16-byte vectors per thread in flight per tensor
+
+template <int CPR>  // 16-byte chunks per row
+__global__ __launch_bounds__(kThreads) void compact_kernel(
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+    const int64_t* __restrict__ seg_off, const int32_t* __restrict__ seg_len,
+    const int32_t* __restrict__ idx, u32x4* __restrict__ k_c, u32x4* __restrict__ v_c,
+    int S, int64_t n, int64_t r_cap) {
+  extern __shared__ int64_t lds[];  // segment table: pre[S + 1], off[S], len[S]
+  int64_t* pre = lds;
+  int64_t* off = lds + S + 1;
+  int32_t* len = reinterpret_cast<int32_t*>(off + S);
+  segment_table<kThreads>(seg_off, seg_len, S, r_cap, pre, off, len,
+                          [](int64_t l) { return l; });
+  const int64_t total = pre[S] * CPR;
+  const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll; base < total; base += step) {
+    u32x4 kv[kUnroll], vv[kUnroll];
+    int64_t dst[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t g = base + u * kThreads + threadIdx.x;
+      dst[u] = -1;
+      if (g < total) {
+        const int64_t flat = g / CPR;
+        const int c = (int)(g - flat * CPR);
+        const int s = find_segment(pre, S, flat);
+        const int64_t row = off[s] + (flat - pre[s]);
+        const int64_t src = idx[row];
+        dst[u] = row * CPR + c;
+        if (src >= 0 && src < n) {
+          const int64_t so = ((int64_t)s * n + src) * CPR + c;
+          kv[u] = __builtin_nontemporal_load(k + so);
+          vv[u] = __builtin_nontemporal_load(v + so);
+        } else {
+          kv[u] = u32x4{0, 0, 0, 0};
+          vv[u] = u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (dst[u] >= 0) {
+        k_c[dst[u]] = kv[u];
+        v_c[dst[u]] = vv[u];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compact(int dtype, int head_dim, const void* k, const void* v,
+                          const int64_t* seg_off, const int32_t* seg_len, const int32_t* idx,
+                          void* k_c, void* v_c, int S, int64_t n, int64_t r_cap,
+                          hipStream_t stream) {
+  const int es = dtype == 0 ? 4 : 2;
+  const int cpr = head_dim * es / 16;
+  const int64_t vecs = r_cap * cpr;
+  int64_t blocks = (vecs + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  const int64_t cap = (int64_t)device_info().cus * 8;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  const size_t lds = segment_table_bytes(S);
+  auto K = static_cast<const u32x4*>(k);
+  auto Vv = static_cast<const u32x4*>(v);
+  auto KC = static_cast<u32x4*>(k_c);
+  auto VC = static_cast<u32x4*>(v_c);
+  switch (cpr) {
+    case 8:
+      compact_kernel<8><<<grid, block, lds, stream>>>(K, Vv, seg_off, seg_len, idx, KC, VC, S, n, r_cap);
+      break;
+    case 11:
+      compact_kernel<11><<<grid, block, lds, stream>>>(K, Vv, seg_off, seg_len, idx, KC, VC, S, n, r_cap);
+      break;
+    case 16:
+      compact_kernel<16><<<grid, block, lds, stream>>>(K, Vv, seg_off, seg_len, idx, KC, VC, S, n, r_cap);
+      break;
+    case 22:
+      compact_kernel<22><<<grid, block, lds, stream>>>(K, Vv, seg_off, seg_len, idx, KC, VC, S, n, r_cap);
+      break;
+    case 32:
+      compact_kernel<32><<<grid, block, lds, stream>>>(K, Vv, seg_off, seg_len, idx, KC, VC, S, n, r_cap);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

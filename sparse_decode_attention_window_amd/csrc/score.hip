@@ -1,0 +1,306 @@
+// Window-mass token score (ZigZagkv page, Eq. 7): for every cached key j of
+// a KV head, the softmax attention weight that each of the last w queries of
+// each of the G query heads sharing that KV head puts on j, summed.
+//
+// A softmax weight needs its row's max and normaliser before it is final, so
+// the score runs in two passes over the keys (each reading K once):
+//   stats   per 512-key tile, per query row: running max and sum of 2^(x-max)
+//           (x = scale * log2(e) * q.k, the log2-domain logit)
+//   reduce  per query row: K_r = max + log2(sum) over all tiles
+//   final   per key: sum over rows of 2^(x - K_r)
+// Both heavy passes put Q K^T on the matrix cores (32x32 tiles): in the
+// stats pass keys are the M operand so a lane owns one query row (row
+// statistics stay in-lane); in the final pass queries are the M operand so a
+// lane owns one key (column sums stay in-lane).  Q of the segment is staged
+// once per workgroup in LDS; K fragments go straight from HBM to registers
+// and serve as A or B operand unchanged (both operands share one per-lane
+// layout).  Causal masking (query row i at position q_pos0 + i) is only
+// evaluated on tiles that reach past q_pos0.
+#include "kvsel_internal.h"
+
+namespace kvsel {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kIter = 2;                        // 64-key sub-tiles per wavefront
+constexpr int kTileKeys = kWaves * kIter * 64;  // 512 keys per workgroup
+constexpr int kMaxRows = 256;
+
+template <typename T, int D>
+struct SGeom {
+  static constexpr int ES = sizeof(T);
+  static constexpr int RB = D * ES;           // row bytes
+  static constexpr int NA = (RB + 31) / 32;   // 32-byte MFMA steps per row
+  static constexpr int PITCH = RB + 16;       // LDS row pitch (breaks bank aliasing)
+};
+
+// One 32-byte step of a 32x32 product: bf16 -> one 32x32x16 MFMA; fp32 -> four 32x32x2.
+__device__ __forceinline__ f32x16 mma_step(const u32x4& a, const u32x4& b, f32x16 acc, bf16_t) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma_step(const u32x4& a, const u32x4& b, f32x16 acc, float) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[t]), __uint_as_float(b[t]), acc,
+                                               0, 0, 0);
+  return acc;
+}
+
+// Row m of the 32x32 accumulator element j for this lane (the column is lane % 32).
+__device__ __forceinline__ int acc_row(int j, int lane) {
+  return (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
+}
+
+// Stage the R query rows of segment (b, kvh) into LDS (rows >= R zero-filled).
+template <typename T, int D>
+__device__ void stage_q(const char* __restrict__ qw, int b, int kvh, int hq, int G, int w, int R,
+                        int RP, char* sq) {
+  using Gm = SGeom<T, D>;
+  const char* src = qw + ((int64_t)b * hq + (int64_t)kvh * G) * w * Gm::RB;
+  constexpr int CH = Gm::RB / 16;
+  for (int i = threadIdx.x; i < RP * CH; i += kThreads) {
+    const int r = i / CH, c = i - r * CH;
+    const u32x4 v = r < R ? load16(src + (int64_t)r * Gm::RB + 16 * c) : u32x4{0, 0, 0, 0};
+    store16(sq + r * Gm::PITCH + 16 * c, v);
+  }
+  // zero the pad step beyond the row (NA * 32 may exceed RB)
+  for (int i = threadIdx.x; i < RP; i += kThreads)
+    if (Gm::NA * 32 > Gm::RB) store16(sq + i * Gm::PITCH + Gm::RB, u32x4{0, 0, 0, 0});
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_k(const char* __restrict__ kseg, int64_t key, int64_t n,
+                                       int half, u32x4* kf) {
+  using Gm = SGeom<T, D>;
+#pragma unroll
+  for (int a = 0; a < Gm::NA; ++a) {
+    const int o = 32 * a + 16 * half;
+    kf[a] = (key < n && o < Gm::RB) ? load16(kseg + key * Gm::RB + o) : u32x4{0, 0, 0, 0};
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void score_stats_kernel(
+    const char* __restrict__ qw, const char* __restrict__ k, int64_t n, int hq, int hkv, int G,
+    int w, int R, int64_t q_pos0, float c, float2* __restrict__ stats, int tiles) {
+  using Gm = SGeom<T, D>;
+  extern __shared__ char lds_raw[];
+  char* sq = lds_raw;                                   // RP * PITCH
+  __shared__ float2 sm[kWaves][kMaxRows];
+  __shared__ int lim[kMaxRows];
+
+  const int s = blockIdx.y, tile = blockIdx.x;
+  const int b = s / hkv, kvh = s % hkv;
+  const int RP = (R + 31) & ~31, RBLK = RP / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, half = lane >> 5;
+  stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq);
+  for (int r = tid; r < RP; r += kThreads) {
+    const int64_t p = q_pos0 + (r % w);
+    lim[r] = r < R ? (int)(p < n ? p : n) : -1;   // row r sees keys <= lim[r]
+  }
+  __syncthreads();
+
+  const char* kseg = k + (int64_t)s * n * Gm::RB;
+  const int64_t tile0 = (int64_t)tile * kTileKeys;
+  float Mr[kMaxRows / 32], Lr[kMaxRows / 32];
+#pragma unroll
+  for (int rb = 0; rb < kMaxRows / 32; ++rb) { Mr[rb] = -INFINITY; Lr[rb] = 0.f; }
+
+  for (int it = 0; it < kIter; ++it) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int64_t key0 = tile0 + (int64_t)((wid * kIter + it) * 2 + kb) * 32;
+      if (key0 >= n) break;
+      u32x4 kf[Gm::NA];
+      load_k<T, D>(kseg, key0 + (lane & 31), n, half, kf);
+      const bool need_mask = key0 + 31 >= n || key0 + 31 > q_pos0;
+#pragma unroll
+      for (int rb = 0; rb < kMaxRows / 32; ++rb) {
+        if (rb >= RBLK) break;
+        f32x16 acc = {};
+        const char* qrow = sq + (rb * 32 + (lane & 31)) * Gm::PITCH + 16 * half;
+#pragma unroll
+        for (int a = 0; a < Gm::NA; ++a)
+          acc = mma_step(kf[a], *reinterpret_cast<const u32x4*>(qrow + 32 * a), acc, T{});
+        // lane owns query row rb*32 + lane%32 and 16 keys key0 + acc_row(j)
+        float x[16];
+        const int lr = lim[rb * 32 + (lane & 31)];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          x[j] = acc[j] * c;
+          if (need_mask && key0 + acc_row(j, lane) > lr) x[j] = -INFINITY;
+        }
+        float tm = x[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) tm = fmaxf(tm, x[j]);
+        const float mn = fmaxf(Mr[rb], tm);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sum += exp2f(x[j] - ms);
+        Lr[rb] = Lr[rb] * exp2f(Mr[rb] - ms) + sum;
+        Mr[rb] = mn;
+      }
+    }
+  }
+  // merge the two half-waves (same row, other 16 keys) and write per-wave stats
+#pragma unroll
+  for (int rb = 0; rb < kMaxRows / 32; ++rb) {
+    if (rb >= RBLK) break;
+    const float mo = __shfl_xor(Mr[rb], 32), lo = __shfl_xor(Lr[rb], 32);
+    const float mn = fmaxf(Mr[rb], mo);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    const float L = Lr[rb] * exp2f(Mr[rb] - ms) + lo * exp2f(mo - ms);
+    if (half == 0) sm[wid][rb * 32 + lane] = make_float2(mn, L);
+  }
+  __syncthreads();
+  for (int r = tid; r < RP; r += kThreads) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, sm[w2][r].x);
+    const float ms = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) L += sm[w2][r].y * exp2f(sm[w2][r].x - ms);
+    stats[((int64_t)s * tiles + tile) * RP + r] = make_float2(M, L);
+  }
+}
+
+// rowc[s][r] = log2 of the row's normaliser in the log2 domain (max + log2(sum)); +inf for pad rows.
+__global__ __launch_bounds__(kMaxRows) void score_reduce_kernel(
+    const float2* __restrict__ stats, int tiles, int R, float* __restrict__ rowc) {
+  const int s = blockIdx.x, r = threadIdx.x;
+  const int RP = (R + 31) & ~31;
+  if (r >= RP) return;
+  float M = -INFINITY, L = 0.f;
+  for (int t = 0; t < tiles; ++t) {
+    const float2 v = stats[((int64_t)s * tiles + t) * RP + r];
+    const float mn = fmaxf(M, v.x);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    L = L * exp2f(M - ms) + v.y * exp2f(v.x - ms);
+    M = mn;
+  }
+  rowc[(int64_t)s * RP + r] = (r < R && L > 0.f) ? M + log2f(L) : INFINITY;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void score_final_kernel(
+    const char* __restrict__ qw, const char* __restrict__ k, int64_t n, int hq, int hkv, int G,
+    int w, int R, int64_t q_pos0, float c, const float* __restrict__ rowc,
+    float* __restrict__ scores) {
+  using Gm = SGeom<T, D>;
+  extern __shared__ char lds_raw[];
+  char* sq = lds_raw;
+  __shared__ float krow[kMaxRows];
+  __shared__ int lim[kMaxRows];
+
+  const int s = blockIdx.y, tile = blockIdx.x;
+  const int b = s / hkv, kvh = s % hkv;
+  const int RP = (R + 31) & ~31, RBLK = RP / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, half = lane >> 5;
+  stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq);
+  for (int r = tid; r < RP; r += kThreads) {
+    krow[r] = rowc[(int64_t)s * RP + r];
+    const int64_t p = q_pos0 + (r % w);
+    lim[r] = r < R ? (int)(p < n ? p : n) : -1;
+  }
+  __syncthreads();
+
+  const char* kseg = k + (int64_t)s * n * Gm::RB;
+  const int64_t tile0 = (int64_t)tile * kTileKeys;
+  for (int it = 0; it < kIter; ++it) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int64_t key0 = tile0 + (int64_t)((wid * kIter + it) * 2 + kb) * 32;
+      if (key0 >= n) break;
+      const int64_t key = key0 + (lane & 31);
+      u32x4 kf[Gm::NA];
+      load_k<T, D>(kseg, key, n, half, kf);
+      const bool need_mask = key0 + 31 >= n || key0 + 31 > q_pos0;
+      float ssum = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < kMaxRows / 32; ++rb) {
+        if (rb >= RBLK) break;
+        f32x16 acc = {};
+        const char* qrow = sq + (rb * 32 + (lane & 31)) * Gm::PITCH + 16 * half;
+#pragma unroll
+        for (int a = 0; a < Gm::NA; ++a)
+          acc = mma_step(*reinterpret_cast<const u32x4*>(qrow + 32 * a), kf[a], acc, T{});
+        // lane owns key `key` and the 16 query rows rb*32 + acc_row(j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int r0 = rb * 32 + g4 * 8 + half * 4;
+          const float4 kr = *reinterpret_cast<const float4*>(&krow[r0]);
+          const float kk[4] = {kr.x, kr.y, kr.z, kr.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float p = exp2f(acc[g4 * 4 + e] * c - kk[e]);
+            if (need_mask && key > lim[r0 + e]) p = 0.f;
+            ssum += p;
+          }
+        }
+      }
+      ssum += __shfl_xor(ssum, 32);
+      if (half == 0 && key < n) scores[(int64_t)s * n + key] = ssum;
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t run(int batch, int hq, int hkv, int w, int64_t n, int64_t q_pos0, float scale,
+               const void* q_win, const void* k, float* scores, void* ws, hipStream_t stream) {
+  using Gm = SGeom<T, D>;
+  const int S = batch * hkv, G = hq / hkv, R = G * w;
+  const int RP = (R + 31) & ~31;
+  const int tiles = (int)((n + kTileKeys - 1) / kTileKeys);
+  auto* stats = static_cast<float2*>(ws);
+  auto* rowc = reinterpret_cast<float*>(stats + (size_t)S * tiles * RP);
+  const float c = scale * kLog2e;
+  const size_t lds = (size_t)RP * Gm::PITCH;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)score_stats_kernel<T, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)score_final_kernel<T, D>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(tiles, S);
+  auto qp = static_cast<const char*>(q_win);
+  auto kp = static_cast<const char*>(k);
+  score_stats_kernel<T, D><<<grid, dim3(kThreads), lds, stream>>>(qp, kp, n, hq, hkv, G, w, R,
+                                                                  q_pos0, c, stats, tiles);
+  score_reduce_kernel<<<dim3(S), dim3(kMaxRows), 0, stream>>>(stats, tiles, R, rowc);
+  score_final_kernel<T, D><<<grid, dim3(kThreads), lds, stream>>>(qp, kp, n, hq, hkv, G, w, R,
+                                                                  q_pos0, c, rowc, scores);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t score_workspace_bytes(int S, int64_t n, int rows) {
+  const int RP = (rows + 31) & ~31;
+  const int64_t tiles = (n + kTileKeys - 1) / kTileKeys;
+  return (size_t)S * tiles * RP * sizeof(float2) + (size_t)S * RP * sizeof(float);
+}
+
+hipError_t launch_score(int dtype, int head_dim, int batch, int hq, int hkv, int w, int64_t n,
+                        int64_t q_pos0, float scale, const void* q_win, const void* k,
+                        float* scores, void* ws, hipStream_t stream) {
+#define KVSEL_SC(T, D) return run<T, D>(batch, hq, hkv, w, n, q_pos0, scale, q_win, k, scores, ws, stream)
+  if (dtype == 1) {
+    if (head_dim == 64) KVSEL_SC(bf16_t, 64);
+    if (head_dim == 88) KVSEL_SC(bf16_t, 88);
+    if (head_dim == 128) KVSEL_SC(bf16_t, 128);
+  } else {
+    if (head_dim == 64) KVSEL_SC(float, 64);
+    if (head_dim == 88) KVSEL_SC(float, 88);
+    if (head_dim == 128) KVSEL_SC(float, 128);
+  }
+#undef KVSEL_SC
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvsel

@@ -1,0 +1,172 @@
+"""One layer of the hot path through the C ABI: score -> select -> compact ->
+decode.  PyTorch only allocates the device buffers; every step runs in the
+HIP kernels behind libkvsel.so.
+
+Capacity layout of the packed cache (caller-chosen, as the C ABI requires):
+segment s = b * hkv + kvh gets rows [seg_off[s], seg_off[s] + cap[s]) with
+  TOPB    cap = min(budget, n)
+  CHUNK   cap = min(n, keep_tokens + longest chunk - 1)  (a chunk prefix that
+          first reaches keep_tokens overshoots by less than one chunk)
+  POLICY  cap = n (global), min(local_window, n) (local), n_special (special)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import _lib as K
+
+
+def device_tensor(arr: np.ndarray, device="cuda"):
+    """Upload a numpy array; uint16 arrays are bf16 words and become bfloat16."""
+    import torch
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def capacities(mode: int, batch: int, hkv: int, n: int, *, budget=None, keep_tokens=0,
+               max_chunk=0, head_kind=None, local_window=0, n_special=0) -> np.ndarray:
+    """Rows reserved per segment (int64 [batch*hkv])."""
+    S = batch * hkv
+    if mode == K.KVSEL_SEL_TOPB:
+        cap = np.minimum(np.maximum(np.asarray(budget, np.int64).reshape(S), 0), n)
+    elif mode == K.KVSEL_SEL_CHUNK:
+        rows = 0 if keep_tokens <= 0 else min(n, keep_tokens + max(0, max_chunk - 1))
+        cap = np.full(S, rows, np.int64)
+    else:
+        per_kind = {K.KVSEL_HEAD_GLOBAL: n, K.KVSEL_HEAD_LOCAL: min(local_window, n),
+                    K.KVSEL_HEAD_SPECIAL: n_special}
+        kinds = np.asarray(head_kind).reshape(hkv)
+        cap = np.array([per_kind.get(int(kinds[s % hkv]), n) for s in range(S)], np.int64)
+    return cap
+
+
+def offsets(cap: np.ndarray) -> tuple[np.ndarray, int]:
+    off = np.zeros(cap.size, np.int64)
+    off[1:] = np.cumsum(cap)[:-1]
+    return off, int(cap.sum())
+
+
+@dataclass
+class LayerRun:
+    """Device buffers of one layer and the calls that fill them."""
+    shape: K.Shape
+    k: object
+    v: object
+    q_dec: object
+    mode: int
+    r_cap: int
+    seg_off: object
+    w: int = 0
+    q_pos0: int = 0
+    q_win: object = None
+    score_shape: K.Shape | None = None     # chunk keys use their own shape
+    score_keys: object = None               # keys that kvsel_score reads
+    params: K.SelectParams | None = None
+    keep: list = field(default_factory=list)   # tensors the params point at
+    scores: object = None
+    seg_len: object = None
+    idx: object = None
+    k_c: object = None
+    v_c: object = None
+    out: object = None
+    ws_score: object = None
+    ws_dec: object = None
+
+    def allocate(self):
+        import torch
+        dev = self.k.device
+        S = self.shape.batch * self.shape.hkv
+        if self.q_win is not None:
+            ss = self.score_shape or self.shape
+            self.scores = torch.empty(ss.batch * ss.hkv * ss.n, dtype=torch.float32, device=dev)
+            nb = K.kvsel_score_workspace(ss, self.w)
+            self.ws_score = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        self.seg_len = torch.empty(S, dtype=torch.int32, device=dev)
+        self.idx = torch.empty(max(self.r_cap, 1), dtype=torch.int32, device=dev)
+        d = self.shape.head_dim
+        self.k_c = torch.empty((max(self.r_cap, 1), d), dtype=self.k.dtype, device=dev)
+        self.v_c = torch.empty((max(self.r_cap, 1), d), dtype=self.k.dtype, device=dev)
+        self.out = torch.empty((self.shape.batch, self.shape.hq, d), dtype=torch.float32,
+                               device=dev)
+        nb = K.kvsel_decode_workspace(self.shape, self.r_cap)
+        self.ws_dec = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        return self
+
+    def score(self, stream=None):
+        if self.q_win is not None:
+            K.kvsel_score(self.score_shape or self.shape, self.w, self.q_pos0, self.q_win,
+                          self.score_keys if self.score_keys is not None else self.k,
+                          self.scores, self.ws_score, stream)
+
+    def select(self, stream=None):
+        K.kvsel_select(self.shape, self.params, self.scores, self.seg_off, self.seg_len, self.idx,
+                       self.r_cap, stream)
+
+    def compact(self, stream=None):
+        K.kvsel_compact(self.shape, self.k, self.v, self.seg_off, self.seg_len, self.idx,
+                        self.k_c, self.v_c, self.r_cap, stream)
+
+    def decode(self, stream=None):
+        K.kvsel_decode_attn(self.shape, self.q_dec, self.k_c, self.v_c, self.seg_off,
+                            self.seg_len, self.r_cap, self.out, self.ws_dec, stream)
+
+    def run(self, stream=None):
+        self.score(stream)
+        self.select(stream)
+        self.compact(stream)
+        self.decode(stream)
+        return self
+
+
+def build_layer(cfg, inputs: dict, *, budget=None, device="cuda") -> LayerRun:
+    """LayerRun for one synthetic layer (cfg: a kvsynth Config, inputs: layer_inputs())."""
+    import torch
+    B, hq, hkv, d, n = cfg.batch, cfg.hq, cfg.hkv, cfg.d, cfg.n
+    shape = K.make_shape(B, hq, hkv, d, n, cfg.dtype, cfg.scale)
+    k = device_tensor(inputs["K"], device)
+    v = device_tensor(inputs["V"], device)
+    qd = device_tensor(inputs["q_dec"], device)
+    keep = []
+    if cfg.mode == "topb":
+        mode = K.KVSEL_SEL_TOPB
+        bud = np.full(B * hkv, cfg.budget, np.int32) if budget is None else \
+            np.broadcast_to(np.asarray(budget, np.int32), (B * hkv,)).copy()
+        cap = capacities(mode, B, hkv, n, budget=bud)
+        bt = device_tensor(bud, device)
+        keep.append(bt)
+        params = K.select_params(mode, budget=bt)
+        run = LayerRun(shape, k, v, qd, mode, 0, None, w=cfg.w, q_pos0=n - cfg.w,
+                       q_win=device_tensor(inputs["q_win"], device), params=params)
+    elif cfg.mode == "chunk":
+        mode = K.KVSEL_SEL_CHUNK
+        ends = np.asarray(inputs["chunk_end"], np.int64)
+        nc = ends.shape[1]
+        lens = np.diff(np.concatenate([[0], ends[0]]))
+        cap = capacities(mode, B, hkv, n, keep_tokens=cfg.keep_tokens, max_chunk=int(lens.max()))
+        et = device_tensor(ends, device)
+        keep.append(et)
+        params = K.select_params(mode, n_chunks=nc, chunk_end=et, keep_tokens=cfg.keep_tokens)
+        sshape = K.make_shape(B, hq, hkv, cfg.chunk_dim, nc, cfg.dtype, cfg.scale)
+        run = LayerRun(shape, k, v, qd, mode, 0, None, w=1, q_pos0=nc - 1,
+                       q_win=device_tensor(inputs["chunk_q"], device), score_shape=sshape,
+                       score_keys=device_tensor(inputs["chunk_keys"], device), params=params)
+    else:
+        mode = K.KVSEL_SEL_POLICY
+        kinds = np.asarray(inputs["head_kind"], np.int8)
+        sp = np.asarray(inputs["special_pos"], np.int32)
+        cap = capacities(mode, B, hkv, n, head_kind=kinds, local_window=cfg.local_window,
+                         n_special=sp.shape[1])
+        kt, st = device_tensor(kinds, device), device_tensor(sp, device)
+        keep += [kt, st]
+        params = K.select_params(mode, head_kind=kt, local_window=cfg.local_window,
+                                 special_pos=st, n_special=sp.shape[1])
+        run = LayerRun(shape, k, v, qd, mode, 0, None, params=params)
+    off, r_cap = offsets(cap)
+    run.seg_off = device_tensor(off, device)
+    run.r_cap = r_cap
+    run.keep = keep
+    return run.allocate()

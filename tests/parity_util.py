@@ -1,0 +1,89 @@
+"""Helpers for the GPU-vs-oracle parity tests (imported by tests only)."""
+from __future__ import annotations
+
+import numpy as np
+
+import kvsynth
+import oracle
+
+# Bars: scores relative (fp32 arithmetic against fp64), outputs max-abs per dtype.
+SCORE_RTOL = 1e-5
+TIE_BAND = 1e-5
+OUT_ATOL = {"fp32": 1e-5, "bf16": 1e-2}
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def zigzag_layer_budgets(cfg) -> np.ndarray:
+    return oracle.zigzag_budgets(kvsynth.zigzag_profile(cfg), cfg.n, cfg.avg_budget,
+                                 cfg.floor_budget)
+
+
+def check_scores(s_gpu: np.ndarray, s_ref: np.ndarray, rows: int, what: str) -> float:
+    """Elementwise relative check; returns the max relative error seen."""
+    s_gpu = s_gpu.astype(np.float64)
+    err = np.abs(s_gpu - s_ref)
+    tol = SCORE_RTOL * np.abs(s_ref) + 1e-30
+    bad = np.nonzero(err > tol)[0]
+    assert bad.size == 0, (f"{what}: {bad.size} scores off, first j={bad[0]} gpu={s_gpu[bad[0]]!r} "
+                           f"ref={s_ref[bad[0]]!r}")
+    assert abs(s_gpu.sum() - rows) < 1e-4 * rows, f"{what}: mass {s_gpu.sum()} != {rows}"
+    nz = s_ref > 0
+    return float(np.max(err[nz] / s_ref[nz])) if nz.any() else 0.0
+
+
+def check_topb_selection(idx_gpu: np.ndarray, s_gpu: np.ndarray, s_ref: np.ndarray, budget: int,
+                         what: str) -> None:
+    n = s_ref.size
+    B = max(0, min(budget, n))
+    assert idx_gpu.size == B, f"{what}: kept {idx_gpu.size}, want {B}"
+    assert np.all(np.diff(idx_gpu) > 0), f"{what}: kept indices not strictly ascending"
+    # exact: same fp32 scores give exactly one answer
+    want = oracle.select_topb(s_gpu.astype(np.float64), B)
+    assert np.array_equal(idx_gpu, want), f"{what}: select differs from the oracle on GPU scores"
+    # end to end: differences to the fp64 selection only inside the tie band
+    if B == 0 or B == n:
+        return
+    ref = oracle.select_topb(s_ref, B)
+    diff = np.setxor1d(ref, idx_gpu)
+    if diff.size:
+        sB = np.sort(s_ref)[::-1][B - 1]
+        out = diff[np.abs(s_ref[diff] - sB) > TIE_BAND * abs(sB)]
+        assert out.size == 0, f"{what}: {out.size} selections differ outside the tie band"
+
+
+def check_chunk_selection(idx_gpu, cs_gpu, cs_ref, ends, keep, what):
+    want = oracle.select_chunks(cs_gpu.astype(np.float64), ends, keep)
+    assert np.array_equal(idx_gpu, want), f"{what}: chunk select differs on GPU scores"
+    ref = oracle.select_chunks(cs_ref, ends, keep)
+    if np.array_equal(ref, idx_gpu):
+        return
+    chunk_of = lambda toks: set(np.searchsorted(ends, toks, side="right").tolist())
+    cg, cr = chunk_of(idx_gpu), chunk_of(ref)
+    last = max(cr, key=lambda c: (-cs_ref[c], c))
+    band = TIE_BAND * abs(cs_ref[last])
+    for c in cg ^ cr:
+        assert abs(cs_ref[c] - cs_ref[last]) <= band, f"{what}: chunk {c} differs outside band"
+
+
+def check_compact(kc_gpu, vc_gpu, K, V, idx, what):
+    kr, vr = oracle.compact(K, V, idx)
+    assert np.array_equal(kc_gpu, kr) and np.array_equal(vc_gpu, vr), f"{what}: compaction not exact"
+
+
+def check_decode(out_gpu, q_dec, K, V, idx, scale, dtype, what) -> float:
+    """out_gpu [G][d] against the oracle over the rows idx; returns max abs error."""
+    Kc, Vc = oracle.compact(oracle.to_f64(K), oracle.to_f64(V), idx)
+    qd = oracle.to_f64(q_dec)
+    err = 0.0
+    for g in range(qd.shape[0]):
+        ref = oracle.decode_attention(qd[g], Kc, Vc, scale)
+        err = max(err, float(np.max(np.abs(out_gpu[g].astype(np.float64) - ref))) if ref.size else 0)
+    assert err <= OUT_ATOL[dtype], f"{what}: decode max-abs error {err}"
+    return err

@@ -1,0 +1,140 @@
+"""The C ABI on the host: the library loads, exports every entry point
+include/kvsel.h declares, rejects bad arguments before launching anything,
+and its host-only budget helper matches the oracle exactly."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kvsynth
+import oracle
+import sparse_decode_attention_window_amd as kvsel
+from sparse_decode_attention_window_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kvsel.h")
+
+FAKE = 0x1000   # never dereferenced: every call below fails its host checks first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvsel_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert "kvsel_score" in names and "kvsel_decode_attn" in names
+    lib = kvsel.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_version():
+    assert "gfx950" in kvsel.kvsel_version()
+
+
+def shape(**kw):
+    base = dict(batch=1, hq=4, hkv=2, head_dim=64, n=512, dtype="fp32", scale=0.125)
+    base.update(kw)
+    return kvsel.make_shape(**base)
+
+
+def call_score(sh, w=8, q_pos0=0, q=FAKE, k=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return kvsel.lib().kvsel_score(ctypes.byref(sh), w, q_pos0, q, k, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), _lib.KVSEL_EINVAL), (dict(hq=3), _lib.KVSEL_EINVAL),
+    (dict(n=0), _lib.KVSEL_EINVAL), (dict(head_dim=96), _lib.KVSEL_EUNSUPPORTED),
+    (dict(dtype=7), _lib.KVSEL_EUNSUPPORTED), (dict(scale=float("inf")), _lib.KVSEL_EINVAL),
+    (dict(batch=2049, hkv=1, hq=1), _lib.KVSEL_EUNSUPPORTED)])
+def test_score_rejects_bad_shape(kw, code):
+    assert call_score(shape(**kw)) == code
+    assert kvsel.kvsel_last_error()
+
+
+def test_score_rejects_bad_args():
+    sh = shape()
+    assert call_score(sh, w=0) == _lib.KVSEL_EINVAL
+    assert call_score(sh, w=200) == _lib.KVSEL_EUNSUPPORTED      # G*w = 400 rows
+    assert call_score(sh, q_pos0=-1) == _lib.KVSEL_EINVAL
+    assert call_score(sh, q=None) == _lib.KVSEL_EINVAL
+    need = kvsel.kvsel_score_workspace(sh, 8)
+    assert need > 0
+    assert call_score(sh, ws_bytes=need - 1) == _lib.KVSEL_ENOSPC
+    assert "workspace" in kvsel.kvsel_last_error()
+
+
+def test_select_rejects_bad_args():
+    sh = shape()
+    lib = kvsel.lib()
+
+    def sel(p, scores=FAKE, off=FAKE, ln=FAKE, ix=FAKE, r_cap=10):
+        return lib.kvsel_select(ctypes.byref(sh), ctypes.byref(p), scores, off, ln, ix, r_cap, None)
+
+    topb = _lib.SelectParams(mode=0, budget=FAKE)
+    assert sel(_lib.SelectParams(mode=0, budget=None)) == _lib.KVSEL_EINVAL
+    assert sel(topb, scores=None) == _lib.KVSEL_EINVAL
+    assert sel(topb, r_cap=-1) == _lib.KVSEL_EINVAL
+    assert sel(topb, off=None) == _lib.KVSEL_EINVAL
+    assert sel(_lib.SelectParams(mode=1, chunk_end=FAKE, n_chunks=0)) == _lib.KVSEL_EINVAL
+    assert sel(_lib.SelectParams(mode=1, chunk_end=FAKE, n_chunks=513)) == _lib.KVSEL_EINVAL
+    assert sel(_lib.SelectParams(mode=2, head_kind=FAKE, local_window=-1)) == _lib.KVSEL_EINVAL
+    assert sel(_lib.SelectParams(mode=2, head_kind=FAKE, n_special=3)) == _lib.KVSEL_EINVAL
+    assert sel(_lib.SelectParams(mode=9)) == _lib.KVSEL_EINVAL
+
+
+def test_compact_and_decode_reject_bad_args():
+    sh = shape()
+    lib = kvsel.lib()
+    assert lib.kvsel_compact(ctypes.byref(sh), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4,
+                             None) == _lib.KVSEL_EINVAL
+    assert lib.kvsel_compact(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -4,
+                             None) == _lib.KVSEL_EINVAL
+    need = kvsel.kvsel_decode_workspace(sh, 100)
+    assert need > 0
+    assert lib.kvsel_decode_attn(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE,
+                                 need - 1, None) == _lib.KVSEL_ENOSPC
+    big_group = shape(hq=16, hkv=2)
+    assert lib.kvsel_decode_attn(ctypes.byref(big_group), FAKE, FAKE, FAKE, FAKE, FAKE, 100, FAKE,
+                                 FAKE, 1 << 30, None) == _lib.KVSEL_EUNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# host budget helper vs the oracle (ZigZagkv page, Eq. 4 + Eq. 6): exact
+# ---------------------------------------------------------------------------
+
+def test_budgets_c2_profile_exact():
+    cfg = kvsynth.get_config(2)
+    p = kvsynth.zigzag_profile(cfg)
+    got = kvsel.kvsel_zigzag_budgets(p, cfg.n, cfg.avg_budget, cfg.floor_budget)
+    want = oracle.zigzag_budgets(p, cfg.n, cfg.avg_budget, cfg.floor_budget)
+    assert got == want.tolist()
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_budgets_random_exact(seed):
+    r = np.random.default_rng(1000 + seed)
+    L = int(r.integers(1, 64))
+    n = int(r.integers(1, 200000))
+    B = int(r.integers(0, n + 1))
+    F = int(r.integers(0, B + 1))
+    p = r.lognormal(0, float(r.uniform(0.05, 3.0)), size=L)
+    if seed % 7 == 0:
+        p = np.round(p, 1) + 0.1          # ties in the profile
+    got = kvsel.kvsel_zigzag_budgets(p, n, B, F)
+    want = oracle.zigzag_budgets(p, n, B, F)
+    assert got == want.tolist()
+
+
+def test_budgets_reject():
+    with pytest.raises(kvsel.KvselError):
+        kvsel.kvsel_zigzag_budgets([1.0, 2.0], 100, 10, 11)
+    with pytest.raises(kvsel.KvselError):
+        kvsel.kvsel_zigzag_budgets([1.0, -2.0], 100, 10, 1)
+    with pytest.raises(kvsel.KvselError):
+        kvsel.kvsel_zigzag_budgets([], 100, 10, 1)

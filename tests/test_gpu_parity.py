@@ -1,0 +1,356 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Every case prints its name before touching the GPU.  Sizes: the small
+configurations in full; reduced variants (ragged n, several tiles); and
+full-size layers in the launch configuration the benchmark times, checked on
+sampled segments the oracle recomputes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import kvsynth
+import oracle
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def kv():
+    import torch
+    import sparse_decode_attention_window_amd as kvsel
+    from sparse_decode_attention_window_amd import pipeline
+    assert torch.cuda.is_available()
+    kvsel.lib()  # raises if the library is missing: no silent fallback
+    return kvsel, pipeline, torch
+
+
+def _run(kv, cfg, layer=0, budget=None):
+    kvsel, pipeline, torch = kv
+    inputs = kvsynth.layer_inputs(cfg, layer)
+    run = pipeline.build_layer(cfg, inputs, budget=budget)
+    run.run()
+    torch.cuda.synchronize()
+    return inputs, run
+
+
+def _host(run):
+    h = {
+        "seg_off": pu.to_host(run.seg_off), "seg_len": pu.to_host(run.seg_len),
+        "idx": pu.to_host(run.idx), "k_c": pu.to_host(run.k_c), "v_c": pu.to_host(run.v_c),
+        "out": pu.to_host(run.out),
+    }
+    h["scores"] = pu.to_host(run.scores) if run.scores is not None else None
+    return h
+
+
+def _check_segments(cfg, inputs, run, segs, budgets=None, layer=0):
+    h = _host(run)
+    G, w, d = cfg.G, cfg.w, cfg.d
+    stats = {"score_rel": 0.0, "out_abs": 0.0}
+    for s in segs:
+        b, kvh = divmod(s, cfg.hkv)
+        what = f"{cfg.name} layer {layer} seg {s}"
+        K, V = inputs["K"][b, kvh], inputs["V"][b, kvh]
+        off, ln = int(h["seg_off"][s]), int(h["seg_len"][s])
+        idx = h["idx"][off:off + ln].astype(np.int64)
+        if cfg.mode == "topb":
+            n = cfg.n
+            s_gpu = h["scores"][s * n:(s + 1) * n]
+            s_ref = oracle.window_scores(oracle.to_f64(inputs["q_win"][b, kvh * G:(kvh + 1) * G]),
+                                         oracle.to_f64(K), cfg.scale, n - w)
+            stats["score_rel"] = max(stats["score_rel"],
+                                     pu.check_scores(s_gpu, s_ref, G * w, what))
+            B = int(budgets[s]) if budgets is not None else cfg.budget
+            pu.check_topb_selection(idx, s_gpu, s_ref, B, what)
+        elif cfg.mode == "chunk":
+            ends = inputs["chunk_end"][b]
+            nc = ends.size
+            cs_gpu = h["scores"][s * nc:(s + 1) * nc]
+            cs_ref = oracle.window_scores(oracle.to_f64(inputs["chunk_q"][b, kvh * G:(kvh + 1) * G]),
+                                          oracle.to_f64(inputs["chunk_keys"][b, kvh]), cfg.scale,
+                                          nc - 1)
+            stats["score_rel"] = max(stats["score_rel"], pu.check_scores(cs_gpu, cs_ref, G, what))
+            pu.check_chunk_selection(idx, cs_gpu, cs_ref, ends, cfg.keep_tokens, what)
+        else:
+            want = oracle.select_policy(int(inputs["head_kind"][kvh]), cfg.n, cfg.local_window,
+                                        inputs["special_pos"][b])
+            assert np.array_equal(idx, want), f"{what}: policy selection differs"
+        pu.check_compact(h["k_c"][off:off + ln], h["v_c"][off:off + ln], K, V, idx, what)
+        out = h["out"][b, kvh * G:(kvh + 1) * G]
+        stats["out_abs"] = max(stats["out_abs"],
+                               pu.check_decode(out, inputs["q_dec"][b, kvh * G:(kvh + 1) * G], K, V,
+                                               idx, cfg.scale, cfg.dtype, what))
+    print(f"  {cfg.name}: max score rel err {stats['score_rel']:.2e}, "
+          f"max decode abs err {stats['out_abs']:.2e}", flush=True)
+    return h
+
+
+# ---------------------------------------------------------------------------
+# whole configurations
+# ---------------------------------------------------------------------------
+
+def test_c0_tiny_fp32_full(kv):
+    cfg = kvsynth.get_config(0)
+    _say(cfg.name)
+    inputs, run = _run(kv, cfg)
+    _check_segments(cfg, inputs, run, range(cfg.batch * cfg.hkv))
+
+
+def test_c1_llama_layer_full(kv):
+    cfg = kvsynth.get_config(1)
+    _say(cfg.name)
+    inputs, run = _run(kv, cfg)
+    _check_segments(cfg, inputs, run, range(cfg.batch * cfg.hkv))
+
+
+@pytest.mark.parametrize("layer", [0, 9])
+def test_c2_reduced_ragged(kv, layer):
+    cfg = kvsynth.get_config(2, batch=2, n=5000 + 77)
+    _say(cfg.name, "reduced n", cfg.n, "layer", layer)
+    bl = pu.zigzag_layer_budgets(cfg)[layer]
+    inputs, run = _run(kv, cfg, layer, budget=bl)
+    _check_segments(cfg, inputs, run, range(cfg.batch * cfg.hkv),
+                    budgets=np.full(cfg.batch * cfg.hkv, bl), layer=layer)
+
+
+def test_c2_full_layer_sampled(kv):
+    cfg = kvsynth.get_config(2)
+    layer = 3
+    _say(cfg.name, "full layer", layer)
+    bl = pu.zigzag_layer_budgets(cfg)[layer]
+    inputs, run = _run(kv, cfg, layer, budget=bl)
+    h = _check_segments(cfg, inputs, run, [0, 13, 31], budgets=np.full(32, bl), layer=layer)
+    # every segment: exact budget, mass G*w
+    assert np.all(h["seg_len"] == bl)
+    sc = h["scores"].reshape(32, cfg.n).astype(np.float64)
+    assert np.all(np.abs(sc.sum(1) - cfg.G * cfg.w) < 1e-3)
+
+
+def test_c3_reduced(kv):
+    cfg = kvsynth.get_config(3, batch=2, n=3000 + 5)
+    _say(cfg.name, "reduced n", cfg.n)
+    inputs, run = _run(kv, cfg)
+    _check_segments(cfg, inputs, run, range(cfg.batch * cfg.hkv))
+
+
+def test_c3_full_sampled(kv):
+    cfg = kvsynth.get_config(3)
+    _say(cfg.name, "full")
+    inputs, run = _run(kv, cfg)
+    kinds = inputs["head_kind"]
+    segs = [7 * cfg.hkv + int(np.nonzero(kinds == k)[0][0]) for k in (0, 1, 2)]
+    h = _check_segments(cfg, inputs, run, segs)
+    assert int(h["seg_len"].sum()) == 8 * 73648
+
+
+def test_c4_reduced(kv):
+    cfg = kvsynth.get_config(4, n=20000 + 3)
+    _say(cfg.name, "reduced n", cfg.n)
+    inputs, run = _run(kv, cfg)
+    _check_segments(cfg, inputs, run, range(cfg.batch * cfg.hkv))
+
+
+def test_c4_full_sampled(kv):
+    cfg = kvsynth.get_config(4)
+    _say(cfg.name, "full")
+    inputs, run = _run(kv, cfg)
+    h = _check_segments(cfg, inputs, run, [0, 5])
+    assert np.all(h["seg_len"] >= cfg.keep_tokens)
+
+
+def test_determinism_c1(kv):
+    cfg = kvsynth.get_config(1, n=3001)
+    _say(cfg.name, "determinism")
+    inputs, run = _run(kv, cfg)
+    a = _host(run)
+    run.run()
+    kv[2].cuda.synchronize()
+    b = _host(run)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------------------
+# single kernels on crafted inputs
+# ---------------------------------------------------------------------------
+
+def _select_topb(kv, scores: np.ndarray, budgets, hkv=1):
+    kvsel, pipeline, torch = kv
+    S, n = scores.shape
+    shape = kvsel.make_shape(S // hkv, hkv, hkv, 64, n, "bf16", 1.0)
+    bud = np.asarray(budgets, np.int32)
+    cap = pipeline.capacities(kvsel.KVSEL_SEL_TOPB, S // hkv, hkv, n, budget=bud)
+    off, r_cap = pipeline.offsets(cap)
+    bt = pipeline.device_tensor(bud)
+    st = pipeline.device_tensor(scores.astype(np.float32).ravel())
+    ot = pipeline.device_tensor(off)
+    lt = torch.empty(S, dtype=torch.int32, device="cuda")
+    it = torch.full((max(r_cap, 1),), -7, dtype=torch.int32, device="cuda")
+    kvsel.kvsel_select(shape, kvsel.select_params(kvsel.KVSEL_SEL_TOPB, budget=bt), st, ot, lt, it,
+                       r_cap)
+    torch.cuda.synchronize()
+    lens, idx = pu.to_host(lt), pu.to_host(it)
+    return [idx[off[s]:off[s] + lens[s]] for s in range(S)], lens
+
+
+@pytest.mark.parametrize("n", [1, 37, 1000, 32768, 45000])
+def test_select_topb_exact_with_ties(kv, n):
+    _say("select topb n", n)
+    r = np.random.default_rng(n)
+    rows = [
+        r.random(n).astype(np.float32),                         # distinct
+        r.integers(0, 5, n).astype(np.float32),                 # heavy ties
+        np.full(n, 0.25, np.float32),                           # all equal
+        np.where(r.random(n) < 0.1, np.nan, r.random(n)).astype(np.float32),   # NaN
+        np.where(r.random(n) < 0.5, -0.0, 0.0).astype(np.float32),             # +-0
+        (r.standard_normal(n) * 1e-30).astype(np.float32),     # tiny, signed
+    ]
+    scores = np.stack(rows)
+    budgets = [max(0, n // 5), n // 3, min(n, 7), n - 1 if n > 1 else 1, n + 5, 0]
+    got, lens = _select_topb(kv, scores, budgets)
+    for s in range(len(rows)):
+        want = oracle.select_topb(scores[s].astype(np.float64), budgets[s])
+        assert lens[s] == want.size, (s, lens[s], want.size)
+        assert np.array_equal(got[s], want), f"row {s}"
+
+
+def test_select_chunk_exact(kv):
+    kvsel, pipeline, torch = kv
+    _say("select chunk crafted")
+    r = np.random.default_rng(7)
+    n = 5000
+    lens_c = r.geometric(1 / 20, size=600)
+    ends = np.minimum(np.cumsum(lens_c), n)
+    ends = np.unique(ends)
+    if ends[-1] != n:
+        ends = np.append(ends, n)
+    nc = ends.size
+    hkv = 3
+    cs = np.stack([r.random(nc), r.integers(0, 3, nc), np.full(nc, 1.0)]).astype(np.float32)
+    for keep in [1, 777, 2400, n, n + 10, 0]:
+        shape = kvsel.make_shape(1, hkv, hkv, 64, n, "bf16", 1.0)
+        maxc = int(np.diff(np.concatenate([[0], ends])).max())
+        cap = pipeline.capacities(kvsel.KVSEL_SEL_CHUNK, 1, hkv, n, keep_tokens=keep, max_chunk=maxc)
+        off, r_cap = pipeline.offsets(cap)
+        et = pipeline.device_tensor(ends[None, :].astype(np.int64))
+        st = pipeline.device_tensor(cs.ravel())
+        ot = pipeline.device_tensor(off)
+        lt = torch.empty(hkv, dtype=torch.int32, device="cuda")
+        it = torch.full((max(r_cap, 1),), -7, dtype=torch.int32, device="cuda")
+        p = kvsel.select_params(kvsel.KVSEL_SEL_CHUNK, n_chunks=nc, chunk_end=et, keep_tokens=keep)
+        kvsel.kvsel_select(shape, p, st, ot, lt, it, r_cap)
+        torch.cuda.synchronize()
+        ln, ix = pu.to_host(lt), pu.to_host(it)
+        for s in range(hkv):
+            want = oracle.select_chunks(cs[s].astype(np.float64), ends, keep)
+            assert ln[s] == want.size, (keep, s)
+            assert np.array_equal(ix[off[s]:off[s] + ln[s]], want), (keep, s)
+
+
+def test_compact_gaps_empty_and_bad_indices(kv):
+    kvsel, pipeline, torch = kv
+    _say("compact crafted")
+    r = np.random.default_rng(11)
+    B, hkv, n, d = 2, 3, 700, 88
+    K = r.integers(0, 65535, size=(B, hkv, n, d), dtype=np.uint16)
+    V = r.integers(0, 65535, size=(B, hkv, n, d), dtype=np.uint16)
+    lens = np.array([0, 5, 700, 1, 33, 0], np.int32)
+    off = np.array([0, 3, 20, 730, 740, 800], np.int64)    # gaps between segments
+    r_cap = 790                                            # clips segment 4 (740 + 33 > 790? no)
+    idx = np.full(r_cap, -1, np.int32)
+    for s in range(6):
+        m = min(lens[s], r_cap - off[s]) if off[s] < r_cap else 0
+        idx[off[s]:off[s] + m] = np.sort(r.choice(n, size=m, replace=False))
+    idx[25] = n + 3          # out of range -> zero row
+    idx[26] = -5
+    shape = kvsel.make_shape(B, hkv, hkv, d, n, "bf16", 1.0)
+    kc = torch.full((r_cap, d), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vc = torch.full((r_cap, d), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    kt, vt = pipeline.device_tensor(K), pipeline.device_tensor(V)
+    kvsel.kvsel_compact(shape, kt, vt, pipeline.device_tensor(off), pipeline.device_tensor(lens),
+                        pipeline.device_tensor(idx), kc, vc, r_cap)
+    torch.cuda.synchronize()
+    kch, vch = pu.to_host(kc), pu.to_host(vc)
+    for s in range(6):
+        b, h = divmod(s, hkv)
+        m = max(0, min(lens[s], r_cap - off[s]))
+        for rr in range(m):
+            row = off[s] + rr
+            j = idx[row]
+            if 0 <= j < n:
+                assert np.array_equal(kch[row], K[b, h, j]) and np.array_equal(vch[row], V[b, h, j])
+            else:
+                assert not kch[row].any() and not vch[row].any()
+    # rows outside every segment are untouched
+    assert np.all(kch[0:3] == 7) and np.all(kch[733:740] == 7)
+
+
+@pytest.mark.parametrize("dtype,d,G", [("bf16", 128, 4), ("bf16", 88, 4), ("bf16", 64, 2),
+                                       ("fp32", 64, 2), ("fp32", 128, 3), ("bf16", 128, 1),
+                                       ("fp32", 88, 4)])
+def test_decode_ragged_segments(kv, dtype, d, G):
+    kvsel, pipeline, torch = kv
+    _say("decode", dtype, d, G)
+    r = np.random.default_rng(d * 10 + G)
+    B, hkv = 2, 2
+    S = B * hkv
+    lens = np.array([0, 1, 257, 1000], np.int32)[:S]
+    off, r_cap = pipeline.offsets(lens.astype(np.int64) + 3)   # 3 spare rows per segment
+    Kc = r.standard_normal((r_cap, d)).astype(np.float32)
+    Vc = r.standard_normal((r_cap, d)).astype(np.float32)
+    q = (2 * r.standard_normal((B, hkv * G, d))).astype(np.float32)
+    store = (lambda x: kvsynth.f32_to_bf16_bits(x)) if dtype == "bf16" else (lambda x: x)
+    Kc, Vc, q = store(Kc), store(Vc), store(q)
+    shape = kvsel.make_shape(B, hkv * G, hkv, d, 1000, dtype, 1 / math.sqrt(d))
+    out = torch.empty((B, hkv * G, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvsel.kvsel_decode_workspace(shape, r_cap), dtype=torch.uint8, device="cuda")
+    kvsel.kvsel_decode_attn(shape, pipeline.device_tensor(q), pipeline.device_tensor(Kc),
+                            pipeline.device_tensor(Vc), pipeline.device_tensor(off),
+                            pipeline.device_tensor(lens), r_cap, out, ws)
+    torch.cuda.synchronize()
+    o = pu.to_host(out)
+    for s in range(S):
+        b, h = divmod(s, hkv)
+        rows = np.arange(off[s], off[s] + lens[s])
+        for g in range(G):
+            ref = oracle.decode_attention(oracle.to_f64(q[b, h * G + g]), oracle.to_f64(Kc[rows]),
+                                          oracle.to_f64(Vc[rows]), 1 / math.sqrt(d))
+            err = np.max(np.abs(o[b, h * G + g] - ref))
+            assert err <= pu.OUT_ATOL[dtype], (s, g, err)
+            if lens[s] == 0:
+                assert not o[b, h * G + g].any()
+
+
+@pytest.mark.parametrize("dtype,d,G,w,n,q_pos0", [
+    ("bf16", 128, 4, 32, 1500, 1468), ("bf16", 128, 4, 32, 700, 10**9),
+    ("fp32", 64, 2, 8, 513, 505), ("bf16", 64, 4, 1, 999, 998), ("bf16", 88, 4, 5, 2049, 100),
+    ("fp32", 128, 1, 3, 90, 87), ("bf16", 128, 8, 32, 600, 568)])
+def test_score_shapes(kv, dtype, d, G, w, n, q_pos0):
+    kvsel, pipeline, torch = kv
+    _say("score", dtype, d, G, w, n, q_pos0)
+    r = np.random.default_rng(n + d)
+    B, hkv = 1, 2
+    q = (r.standard_normal((B, hkv * G, w, d)) * 1.5).astype(np.float32)
+    Kf = r.standard_normal((B, hkv, n, d)).astype(np.float32)
+    store = (lambda x: kvsynth.f32_to_bf16_bits(x)) if dtype == "bf16" else (lambda x: x)
+    q, Kf = store(q), store(Kf)
+    shape = kvsel.make_shape(B, hkv * G, hkv, d, n, dtype, 1 / math.sqrt(d))
+    sc = torch.empty(B * hkv * n, dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvsel.kvsel_score_workspace(shape, w), dtype=torch.uint8, device="cuda")
+    kvsel.kvsel_score(shape, w, q_pos0, pipeline.device_tensor(q), pipeline.device_tensor(Kf), sc, ws)
+    torch.cuda.synchronize()
+    s_gpu = pu.to_host(sc).reshape(B * hkv, n)
+    for s in range(B * hkv):
+        b, h = divmod(s, hkv)
+        ref = oracle.window_scores(oracle.to_f64(q[b, h * G:(h + 1) * G]), oracle.to_f64(Kf[b, h]),
+                                   1 / math.sqrt(d), q_pos0)
+        pu.check_scores(s_gpu[s], ref, G * w, f"score seg {s}")
