@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(
   stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq);
   for (int r = tid; r < RP; r += kThreads) {
     const int64_t p = q_pos0 + (r % w);
-    lim[r] = r < R ? (int)(p < n ? p : n) : -1;   // row r sees keys <= lim[r]
+    lim[r] = r < R ? (int)(p < n - 1 ? p : n - 1) : -1;   // row r sees keys <= lim[r]
   }
   __syncthreads();
 
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
   for (int r = tid; r < RP; r += kThreads) {
     krow[r] = rowc[(int64_t)s * RP + r];
     const int64_t p = q_pos0 + (r % w);
-    lim[r] = r < R ? (int)(p < n ? p : n) : -1;
+    lim[r] = r < R ? (int)(p < n - 1 ? p : n - 1) : -1;
   }
   __syncthreads();
 
