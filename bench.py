@@ -2,13 +2,15 @@
 """Benchmark: one step = the whole hot path over the 32-layer, 32K-context,
 batch-4 Llama-3-8B-shaped workload with per-layer bounded budgets:
 
-  per layer   window score -> top-B select -> gather-compact
-  then        one decode step through all 32 layers over the compacted caches
-  (plus the host-side per-layer budget computation)
+  window score (all layers) -> top-B select (all layers) -> gather-compact
+  (all layers) -> one decode step through all 32 layers over the compacted
+  caches, plus the host-side per-layer budget computation.
 
-Inputs are synthetic (seeded generator), resident in HBM before timing.  HIP
-events around every entry point give per-stage times; the reported value is
-the decode attention's algorithmic HBM bandwidth.  Prints ONE JSON line.
+Inputs are synthetic (seeded generator), resident in HBM before timing.  Each
+phase is captured once as a HIP graph of the library's launches and replayed
+between two HIP events, so per-layer stage times carry no host launch gaps;
+the reported value is the decode attention's algorithmic HBM bandwidth.
+Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -139,24 +141,35 @@ def main() -> int:
             log(f"[bench] layer {l + 1}/{L} resident ({time.perf_counter() - t0:.1f} s)")
     torch.cuda.synchronize()
 
+    # One step = four phases over all layers, each captured once as a HIP graph
+    # (the kernels are the eager ones; the graph only removes host launch gaps).
+    phases = {
+        "score": lambda: [run.score() for run in layers],
+        "select": lambda: [run.select() for run in layers],
+        "compact": lambda: [run.compact() for run in layers],
+        "decode": lambda: [run.decode() for run in layers],
+    }
+    for fn in phases.values():   # eager warm-up before capture
+        fn()
+    torch.cuda.synchronize()
+    graphs = {}
+    for name, fn in phases.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs[name] = g
+    torch.cuda.synchronize()
+
     def step(ev):
         bud = kvsel.kvsel_zigzag_budgets(profile, cfg.n, cfg.avg_budget, cfg.floor_budget)
         assert bud == budgets
-        for l, run in enumerate(layers):
-            ev[l][0].record()
-            run.score()
-            ev[l][1].record()
-            run.select()
-            ev[l][2].record()
-            run.compact()
-            ev[l][3].record()
-        for l, run in enumerate(layers):
-            ev[l][4].record()
-            run.decode()
-            ev[l][5].record()
+        ev[0].record()
+        for i, name in enumerate(phases):
+            graphs[name].replay()
+            ev[i + 1].record()
 
     def events():
-        return [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
+        return [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
 
     for i in range(args.warmup):
         step(events())
@@ -172,16 +185,13 @@ def main() -> int:
     wall = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {wall:.3f} s")
 
-    # per-stage GPU times (ms), summed over layers, averaged over steps
-    st = {"score": 0.0, "select": 0.0, "compact": 0.0, "decode": 0.0}
+    # per-phase GPU time (ms) averaged over steps, then per layer
+    st = {name: 0.0 for name in phases}
     for ev in evs:
-        for l in range(L):
-            st["score"] += ev[l][0].elapsed_time(ev[l][1])
-            st["select"] += ev[l][1].elapsed_time(ev[l][2])
-            st["compact"] += ev[l][2].elapsed_time(ev[l][3])
-            st["decode"] += ev[l][4].elapsed_time(ev[l][5])
+        for i, name in enumerate(phases):
+            st[name] += ev[i].elapsed_time(ev[i + 1])
     launches = args.steps * L
-    us = {k: v / launches * 1e3 for k, v in st.items()}       # µs per layer launch
+    us = {k: v / launches * 1e3 for k, v in st.items()}       # µs per layer
 
     es, d, B, hq, hkv, n = cfg.es, cfg.d, cfg.batch, cfg.hq, cfg.hkv, cfg.n
     rows = [int(layers[l].seg_len.sum().item()) for l in range(L)]
@@ -224,7 +234,7 @@ def main() -> int:
         "select_and_compact_us_per_layer": round(us["select"] + us["compact"], 2),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel": "kvsel_decode_attn (split + combine)",
+                     "traffic": traffic, "kernel": "kvsel_decode_attn (decode_split_kernel)",
                      "algorithmic_bytes_per_launch": int(dec_bytes),
                      "avg_launch_us": round(us["decode"], 3)},
         "stages_us_per_layer": {k: round(v, 3) for k, v in us.items()},

@@ -39,14 +39,16 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD,
+          defines: tuple = ()) -> str:
+    """Compile every source and link `out`; `defines` are extra -D flags."""
+    os.makedirs(build_dir, exist_ok=True)
     jobs = []
     for f in sorted(os.listdir(CSRC)):
         src = os.path.join(CSRC, f)
-        obj = os.path.join(BUILD, f + ".o")
+        obj = os.path.join(build_dir, f + ".o")
         if f.endswith(".hip"):
-            jobs.append([HIPCC, *HIP_FLAGS, "-c", src, "-o", obj])
+            jobs.append([HIPCC, *HIP_FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj])
         elif f.endswith(".cpp"):
             jobs.append(["g++", *CXX_FLAGS, "-c", src, "-o", obj])
     with ThreadPoolExecutor(min(8, len(jobs))) as ex:
@@ -56,10 +58,10 @@ def build(verbose: bool = False) -> str:
             if o.strip():
                 print(o)
     objs = [j[-1] for j in jobs]
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

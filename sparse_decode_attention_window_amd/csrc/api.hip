@@ -116,7 +116,8 @@ kvsel_status kvsel_score(const kvsel_shape* s, int32_t w, int64_t q_pos0, const 
   if (q_pos0 < 0) return fail(KVSEL_EINVAL, "q_pos0 must be >= 0");
   if (!q_win || !k || !scores) return fail(KVSEL_EINVAL, "q_win, k and scores must be non-NULL");
   if (S > 65535) return fail(KVSEL_EUNSUPPORTED, "too many segments for the score grid");
-  const int RP = (G * w + 31) & ~31;
+  int RP = 32;
+  while (RP < G * w) RP *= 2;   // query rows padded to a power-of-two count of 32-row blocks
   const size_t lds = (size_t)RP * (s->head_dim * elem_size(s) + 16);
   if (lds + 8192 > (size_t)device_info().max_lds)
     return fail(KVSEL_EUNSUPPORTED, "query block of %zu bytes does not fit in LDS", lds);

@@ -12,7 +12,7 @@ namespace kvsel {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;  // 16-byte vectors per thread in flight per tensor
+constexpr int kUnroll = 8;  // 16-byte vectors per thread in flight per tensor
 
 template <int CPR>  // 16-byte chunks per row
 __global__ __launch_bounds__(kThreads) void compact_kernel(
@@ -28,35 +28,40 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
                           [](int64_t l) { return l; });
   const int64_t total = pre[S] * CPR;
   const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
+  const u32x4 zero = {0, 0, 0, 0};
   for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll; base < total; base += step) {
-    u32x4 kv[kUnroll], vv[kUnroll];
-    int64_t dst[kUnroll];
+    // phase 1: locate every vector and fetch its source index (all loads independent)
+    int64_t row[kUnroll];
+    int seg[kUnroll], col[kUnroll];
+    int32_t src[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t g = base + u * kThreads + threadIdx.x;
-      dst[u] = -1;
-      if (g < total) {
-        const int64_t flat = g / CPR;
-        const int c = (int)(g - flat * CPR);
-        const int s = find_segment(pre, S, flat);
-        const int64_t row = off[s] + (flat - pre[s]);
-        const int64_t src = idx[row];
-        dst[u] = row * CPR + c;
-        if (src >= 0 && src < n) {
-          const int64_t so = ((int64_t)s * n + src) * CPR + c;
-          kv[u] = __builtin_nontemporal_load(k + so);
-          vv[u] = __builtin_nontemporal_load(v + so);
-        } else {
-          kv[u] = u32x4{0, 0, 0, 0};
-          vv[u] = u32x4{0, 0, 0, 0};
-        }
-      }
+      const int64_t g0 = base + u * kThreads + threadIdx.x;
+      const int64_t g = g0 < total ? g0 : total - 1;   // clamped: always a real vector
+      const int64_t flat = g / CPR;
+      col[u] = (int)(g - flat * CPR);
+      seg[u] = find_segment(pre, S, flat);
+      row[u] = off[seg[u]] + (flat - pre[seg[u]]);
     }
 #pragma unroll
+    for (int u = 0; u < kUnroll; ++u) src[u] = idx[row[u]];
+    // phase 2: gather the rows (invalid indices read row 0 and store zeros)
+    u32x4 kv[kUnroll], vv[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (dst[u] >= 0) {
-        k_c[dst[u]] = kv[u];
-        v_c[dst[u]] = vv[u];
+      ok[u] = src[u] >= 0 && src[u] < n;
+      const int64_t so = ok[u] ? ((int64_t)seg[u] * n + src[u]) * CPR + col[u] : 0;
+      kv[u] = __builtin_nontemporal_load(k + so);
+      vv[u] = __builtin_nontemporal_load(v + so);
+    }
+    // phase 3: coalesced stores
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (base + u * kThreads + threadIdx.x < total) {
+        const int64_t d = row[u] * CPR + col[u];
+        k_c[d] = ok[u] ? kv[u] : zero;
+        v_c[d] = ok[u] ? vv[u] : zero;
       }
     }
   }

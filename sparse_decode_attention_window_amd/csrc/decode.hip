@@ -2,20 +2,26 @@
 // cache: the decode-step attention of the RAP page (Fig. 2 / Eq. 2) run over
 // only the kept tokens (ChunkLLM page §2.3; ZigZagkv page Eq. 6 budgets).
 //
-// Work items are (segment, 256-row chunk) pairs flattened over all segments,
-// so segments of very different lengths (FastGen local / special / global
-// heads) load the chip evenly.  A workgroup of four wavefronts owns one item;
-// each wavefront streams 64 rows in tiles of 16:
+// Work items are (segment, chunk of 64*tpw rows) pairs flattened over all
+// segments, so segments of very different lengths (FastGen local / special /
+// global heads) load the chip evenly; tpw (16-row tiles per wavefront) is
+// picked from the cache size so a launch holds about a thousand workgroups.
+// A workgroup of four wavefronts owns one item; each wavefront streams its
+// rows in 16-row tiles with the next tile's loads in flight while the current
+// one is computed:
 //   QK^T  on the matrix cores: A = the G query heads of the KV head
 //         replicated over 16 rows, B = 16 keys; every lane ends up with the
-//         logits of one key for all heads.
+//         logits of one key for all heads.  The tile max is a DPP row
+//         reduction; probabilities reach the value lanes through LDS.
 //   PV    on the vector ALUs in fp32: lane (slot g, chunk c) owns 16 bytes
-//         of a value row, takes its keys' probabilities by lane permute and
-//         accumulates heads x elements.
-// Each item keeps (running max, sum of exponentials, unnormalised output);
-// the combine kernel merges the items of a segment (the usual split-softmax
-// identity) and normalises.  Softmax runs in the log2 domain with the scale
-// folded into one multiply.
+//         of value row 4t+g and accumulates heads x elements.
+// Each item keeps (running max, sum of exponentials, unnormalised output) in
+// the workspace; a second kernel (one wavefront per segment and query head)
+// merges a segment's items (the split-softmax identity) and normalises.  The
+// merge is a separate launch on purpose: handing partials between workgroups
+// inside one kernel needs device-scope fences, which on this multi-XCD part
+// write back and invalidate the L2 of the issuing XCD.  Softmax runs in the
+// log2 domain with the scale folded into one multiply.
 #include "kvsel_internal.h"
 
 namespace kvsel {
@@ -23,8 +29,15 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kRowsPerWave = kDecodeRowsPerItem / kWaves;  // 64
 constexpr int kTile = 16;
+#ifndef KVSEL_DECODE_TARGET_ITEMS
+#define KVSEL_DECODE_TARGET_ITEMS 1024
+#endif
+#ifndef KVSEL_DECODE_MAX_TPW
+#define KVSEL_DECODE_MAX_TPW 32
+#endif
+constexpr int kTargetItems = KVSEL_DECODE_TARGET_ITEMS;  // workgroups a launch aims for
+constexpr int kMaxTpw = KVSEL_DECODE_MAX_TPW;
 
 template <typename T, int D>
 struct Geom {
@@ -49,36 +62,152 @@ __device__ __forceinline__ f32x4 qk_step(const u32x4& a, const u32x4& b, f32x4 a
   return acc;
 }
 
+// rows per work item for a packed cache of r_cap rows (host and device agree)
+__host__ __device__ inline int tiles_per_wave(int64_t r_cap) {
+  int64_t t = (r_cap + (int64_t)kWaves * kTile * kTargetItems - 1) /
+              ((int64_t)kWaves * kTile * kTargetItems);
+  return (int)(t < 1 ? 1 : (t > kMaxTpw ? kMaxTpw : t));
+}
+
+template <typename T, int D>
+struct TileRegs {
+  u32x4 k[Geom<T, D>::NA];
+  u32x4 v[4][Geom<T, D>::CPL];
+};
+
+// Branch-free tile loads from a wave-uniform tile base: rows past the wave's
+// range are clamped to its last row (cache hits; their keys are masked in
+// compute_tile, so their values only ever meet a zero probability), which
+// lets the compiler keep the next tile's loads in flight with a partial vmcnt
+// wait.  lim = last valid row of the tile (0..15).
+template <typename T, int D>
+__device__ __forceinline__ void load_tile(TileRegs<T, D>& r, const char* kt, const char* vt,
+                                          int lim, int grp, int l16) {
+  using Gm = Geom<T, D>;
+  const u32x4 zero = {0, 0, 0, 0};
+  const int kr = min(l16, lim) * Gm::RB;
+#pragma unroll
+  for (int a = 0; a < Gm::NA; ++a) {
+    const int o = 64 * a + 16 * grp;
+    if (64 * (a + 1) <= Gm::RB) {
+      r.k[a] = load16(kt + kr + o);
+    } else {  // last, partial step (head_dim 88): lanes past the row read zeros
+      const u32x4 x = load16(kt + kr + min(o, Gm::RB - 16));
+      r.k[a] = o < Gm::RB ? x : zero;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int vr = min(4 * t + grp, lim) * Gm::RB;
+#pragma unroll
+    for (int x = 0; x < Gm::CPL; ++x) {
+      // lanes past the row's last chunk reread it; their sums are never stored
+      const int ch = min(l16 + 16 * x, Gm::NCH - 1);
+      r.v[t][x] = load16(vt + vr + 16 * ch);
+    }
+  }
+}
+
 template <typename T, int D, int HG>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+struct WaveState {
+  float m[HG], l[HG];
+  float acc[HG][Geom<T, D>::CPL][Geom<T, D>::EPV];
+};
+
+template <typename T, int D, int HG>
+__device__ __forceinline__ void compute_tile(WaveState<T, D, HG>& st, const TileRegs<T, D>& r,
+                                             const u32x4* qf, float c, bool kok, float4* sp,
+                                             int grp, int l16) {
+  using Gm = Geom<T, D>;
+  // logits: this lane's key (t0 + l16) for heads j % HG (A rows replicate the heads)
+  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int a = 0; a < Gm::NA; ++a) sacc = qk_step(qf[a], r.k[a], sacc, T{});
+
+  float p[4] = {0.f, 0.f, 0.f, 0.f}, alpha[HG];
+  bool rescale = false;
+#pragma unroll
+  for (int h = 0; h < HG; ++h) {
+    const float x = kok ? sacc[h] * c : -INFINITY;
+    const float mn = fmaxf(st.m[h], row_max16(x));
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    alpha[h] = __builtin_amdgcn_exp2f(st.m[h] - ms);
+    rescale |= mn != st.m[h];
+    p[h] = __builtin_amdgcn_exp2f(x - ms);
+    st.m[h] = mn;
+  }
+  // probabilities of the tile's 16 keys to every lane through LDS (4 heads per key)
+  if (grp == 0) sp[l16] = make_float4(p[0], p[1], p[2], p[3]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  if (rescale) {  // wave-uniform: the running max is the same in every lane
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+      st.l[h] *= alpha[h];
+#pragma unroll
+      for (int x = 0; x < Gm::CPL; ++x)
+#pragma unroll
+        for (int e = 0; e < Gm::EPV; ++e) st.acc[h][x][e] *= alpha[h];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float4 pv = sp[4 * t + grp];
+    const float pk[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+    for (int h = 0; h < HG; ++h) st.l[h] += pk[h];
+#pragma unroll
+    for (int x = 0; x < Gm::CPL; ++x) {
+      float v[Gm::EPV];
+      Vec16<T>::unpack(r.v[t][x], v);
+#pragma unroll
+      for (int h = 0; h < HG; ++h)
+#pragma unroll
+        for (int e = 0; e < Gm::EPV; ++e) st.acc[h][x][e] += pk[h] * v[e];
+    }
+  }
+  // the next tile's write must not pass this tile's reads
+  __builtin_amdgcn_wave_barrier();
+}
+
+#ifndef KVSEL_DECODE_MIN_BLOCKS
+#define KVSEL_DECODE_MIN_BLOCKS 1
+#endif
+#ifndef KVSEL_DECODE_PREFETCH
+#define KVSEL_DECODE_PREFETCH 1
+#endif
+
+template <typename T, int D, int HG>
+__global__ __launch_bounds__(kThreads, KVSEL_DECODE_MIN_BLOCKS) void decode_split_kernel(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
     const int64_t* __restrict__ seg_off, const int32_t* __restrict__ seg_len, int64_t r_cap,
-    int S, int hq, int hkv, int G, float c, float2* __restrict__ part_ml,
+    int S, int hq, int hkv, int G, float c, int tpw, float2* __restrict__ part_ml,
     float* __restrict__ part_o) {
   using Gm = Geom<T, D>;
-  extern __shared__ int64_t lds[];
-  int64_t* pre = lds;
-  int64_t* off = lds + S + 1;
-  int32_t* len = reinterpret_cast<int32_t*>(off + S);
+  __shared__ float4 sp_all[kWaves][kTile];
   __shared__ float sm_o[kWaves][HG][D];
   __shared__ float sm_m[kWaves][HG], sm_l[kWaves][HG];
 
-  segment_table<kThreads>(seg_off, seg_len, S, r_cap, pre, off, len, [](int64_t l) {
-    return (l + kDecodeRowsPerItem - 1) / kDecodeRowsPerItem;
-  });
   const int64_t item = blockIdx.x;
-  if (item >= pre[S]) return;  // uniform over the block
-  const int s = find_segment(pre, S, item);
+  const int64_t rows_per_item = (int64_t)kWaves * kTile * tpw;
+  const uint32_t rpi = (uint32_t)rows_per_item;
+  const SegLoc loc = wave_locate(seg_off, seg_len, S, r_cap, item, true,
+                                 [=](uint32_t l) { return (l + rpi - 1) / rpi; });
+  if (loc.s < 0) return;  // same answer in every wave of the block
+  const int s = loc.s;
   const int b = s / hkv, kvh = s % hkv;
-  const int64_t row0 = (item - pre[s]) * kDecodeRowsPerItem;
-  const int64_t row_end = min((int64_t)len[s], row0 + kDecodeRowsPerItem);
+  const int64_t row0 = (item - loc.first) * rows_per_item;
+  const int64_t row_end = min(loc.len, row0 + rows_per_item);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int grp = lane >> 4, l16 = lane & 15;
-  const int64_t wr0 = row0 + wid * kRowsPerWave;
-  const int64_t wr1 = min(row_end, wr0 + kRowsPerWave);
-  const char* kseg = kc + off[s] * Gm::RB;
-  const char* vseg = vc + off[s] * Gm::RB;
+  const int64_t wr0 = row0 + (int64_t)wid * kTile * tpw;
+  const int64_t wr1 = min(row_end, wr0 + (int64_t)kTile * tpw);
+  const char* kseg = kc + loc.off * Gm::RB;
+  const char* vseg = vc + loc.off * Gm::RB;
+  float4* sp = sp_all[wid];
 
   // A operand: query head (l16 % HG) of this KV head, 16 bytes per 64-byte step
   u32x4 qf[Gm::NA];
@@ -92,100 +221,61 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     }
   }
 
-  float m[HG], l[HG], acc[HG][Gm::CPL][Gm::EPV];
+  WaveState<T, D, HG> st;
 #pragma unroll
   for (int h = 0; h < HG; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
+    st.m[h] = -INFINITY;
+    st.l[h] = 0.f;
 #pragma unroll
     for (int x = 0; x < Gm::CPL; ++x)
 #pragma unroll
-      for (int e = 0; e < Gm::EPV; ++e) acc[h][x][e] = 0.f;
+      for (int e = 0; e < Gm::EPV; ++e) st.acc[h][x][e] = 0.f;
   }
 
-  for (int64_t t0 = wr0; t0 < wr1; t0 += kTile) {
-    // loads: K (QK layout) and V (PV layout) for 16 rows
-    const int64_t krow = t0 + l16;
-    const bool kok = krow < wr1;
-    u32x4 kf[Gm::NA];
-#pragma unroll
-    for (int a = 0; a < Gm::NA; ++a) {
-      const int o = 64 * a + 16 * grp;
-      kf[a] = (kok && o < Gm::RB) ? load16(kseg + krow * Gm::RB + o) : u32x4{0, 0, 0, 0};
+  // two register sets: the next tile's loads are in flight during compute
+  const int ntiles = (int)((wr1 - wr0 + kTile - 1) / kTile);
+  if (ntiles > 0) {
+    TileRegs<T, D> ra, rb;
+    auto tile_lim = [&](int64_t t0) { return (int)min((int64_t)kTile - 1, wr1 - 1 - t0); };
+#if KVSEL_DECODE_PREFETCH
+    // sched_barrier pins the issue order (vmcnt waits count in issue order)
+    load_tile(ra, kseg + wr0 * Gm::RB, vseg + wr0 * Gm::RB, tile_lim(wr0), grp, l16);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < ntiles; i += 2) {
+      const int64_t t0 = wr0 + (int64_t)i * kTile, t1 = t0 + kTile;
+      const int64_t t1c = min(t1, wr1 - 1);
+      load_tile(rb, kseg + t1c * Gm::RB, vseg + t1c * Gm::RB, tile_lim(t1c), grp, l16);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile(st, ra, qf, c, l16 <= tile_lim(t0), sp, grp, l16);
+      if (i + 1 >= ntiles) break;
+      const int64_t t2c = min(t1 + kTile, wr1 - 1);
+      load_tile(ra, kseg + t2c * Gm::RB, vseg + t2c * Gm::RB, tile_lim(t2c), grp, l16);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile(st, rb, qf, c, l16 <= tile_lim(t1), sp, grp, l16);
     }
-    u32x4 vf[4][Gm::CPL];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t vrow = t0 + 4 * t + grp;
-#pragma unroll
-      for (int x = 0; x < Gm::CPL; ++x) {
-        const int ch = l16 + 16 * x;
-        vf[t][x] = (vrow < wr1 && ch < Gm::NCH) ? load16(vseg + vrow * Gm::RB + 16 * ch)
-                                                : u32x4{0, 0, 0, 0};
-      }
+#else
+    (void)rb;
+    for (int i = 0; i < ntiles; ++i) {
+      const int64_t t0 = wr0 + (int64_t)i * kTile;
+      load_tile(ra, kseg + t0 * Gm::RB, vseg + t0 * Gm::RB, tile_lim(t0), grp, l16);
+      compute_tile(st, ra, qf, c, l16 <= tile_lim(t0), sp, grp, l16);
     }
-
-    // logits: lane holds key krow for heads j % HG (rows replicate the heads)
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int a = 0; a < Gm::NA; ++a) sacc = qk_step(qf[a], kf[a], sacc, T{});
-
-    float p[HG], alpha[HG];
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      const float x = kok ? sacc[h] * c : -INFINITY;
-      float tm = x;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) tm = fmaxf(tm, __shfl_xor(tm, o));
-      const float mn = fmaxf(m[h], tm);
-      const float ms = mn == -INFINITY ? 0.f : mn;
-      alpha[h] = exp2f(m[h] - ms);
-      p[h] = exp2f(x - ms);
-      m[h] = mn;
-    }
-
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      l[h] *= alpha[h];
-#pragma unroll
-      for (int x = 0; x < Gm::CPL; ++x)
-#pragma unroll
-        for (int e = 0; e < Gm::EPV; ++e) acc[h][x][e] *= alpha[h];
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int src = (lane & 48) | (4 * t + grp);
-      float pk[HG];
-#pragma unroll
-      for (int h = 0; h < HG; ++h) {
-        pk[h] = __shfl(p[h], src);
-        l[h] += pk[h];
-      }
-#pragma unroll
-      for (int x = 0; x < Gm::CPL; ++x) {
-        float v[Gm::EPV];
-        Vec16<T>::unpack(vf[t][x], v);
-#pragma unroll
-        for (int h = 0; h < HG; ++h)
-#pragma unroll
-          for (int e = 0; e < Gm::EPV; ++e) acc[h][x][e] += pk[h] * v[e];
-      }
-    }
+#endif
   }
 
   // fold the four key slots (lane groups) together
 #pragma unroll
   for (int h = 0; h < HG; ++h) {
-    l[h] += __shfl_xor(l[h], 16);
-    l[h] += __shfl_xor(l[h], 32);
+    st.l[h] += __shfl_xor(st.l[h], 16);
+    st.l[h] += __shfl_xor(st.l[h], 32);
 #pragma unroll
     for (int x = 0; x < Gm::CPL; ++x)
 #pragma unroll
       for (int e = 0; e < Gm::EPV; ++e) {
-        float v = acc[h][x][e];
+        float v = st.acc[h][x][e];
         v += __shfl_xor(v, 16);
         v += __shfl_xor(v, 32);
-        acc[h][x][e] = v;
+        st.acc[h][x][e] = v;
       }
   }
   if (grp == 0) {
@@ -196,14 +286,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
         for (int h = 0; h < HG; ++h)
 #pragma unroll
-          for (int e = 0; e < Gm::EPV; ++e) sm_o[wid][h][ch * Gm::EPV + e] = acc[h][x][e];
+          for (int e = 0; e < Gm::EPV; ++e) sm_o[wid][h][ch * Gm::EPV + e] = st.acc[h][x][e];
     }
   }
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < HG; ++h) {
-      sm_m[wid][h] = m[h];
-      sm_l[wid][h] = l[h];
+      sm_m[wid][h] = st.m[h];
+      sm_l[wid][h] = st.l[h];
     }
   }
   __syncthreads();
@@ -218,69 +308,104 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     float o = 0.f, L = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = exp2f(sm_m[w][h] - Ms);
+      const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - Ms);
       o += f * sm_o[w][h][d];
       L += f * sm_l[w][h];
     }
     part_o[(item * HG + h) * D + d] = o;
     if (d == 0) part_ml[item * HG + h] = make_float2(M, L);
   }
-}
 
-template <int HG>
-__global__ __launch_bounds__(128) void decode_combine_kernel(
-    const float2* __restrict__ part_ml, const float* __restrict__ part_o,
-    const int64_t* __restrict__ seg_off, const int32_t* __restrict__ seg_len, int64_t r_cap,
-    int S, int hq, int hkv, int G, int D, int64_t items_max, float* __restrict__ out) {
-  extern __shared__ int64_t lds[];
-  int64_t* pre = lds;
-  int64_t* off = lds + S + 1;
-  int32_t* len = reinterpret_cast<int32_t*>(off + S);
-  segment_table<128>(seg_off, seg_len, S, r_cap, pre, off, len, [](int64_t l) {
-    return (l + kDecodeRowsPerItem - 1) / kDecodeRowsPerItem;
-  });
-  const int s = blockIdx.x / G, g = blockIdx.x % G;
-  const int b = s / hkv, kvh = s % hkv;
-  // overlapping segments (a violated precondition) can ask for more items than
-  // the workspace holds; those were never computed, so clip the range
-  const int64_t first = min(pre[s], items_max);
-  const int64_t cnt = min(pre[s + 1], items_max) - first;
-  float* o = out + ((int64_t)b * hq + (int64_t)kvh * G + g) * D;
-  float M = -INFINITY;
-  for (int64_t it = 0; it < cnt; ++it) M = fmaxf(M, part_ml[(first + it) * HG + g].x);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    if (cnt == 0 || M == -INFINITY) {
-      o[d] = 0.f;
-      continue;
-    }
-    float num = 0.f, den = 0.f;
-    for (int64_t it = 0; it < cnt; ++it) {
-      const float2 ml = part_ml[(first + it) * HG + g];
-      const float f = exp2f(ml.x - M);
-      num += f * part_o[((first + it) * HG + g) * D + d];
-      den += f * ml.y;
-    }
-    o[d] = num / den;
-  }
 }
 
 int hg_for(int G) { return G <= 1 ? 1 : (G <= 2 ? 2 : 4); }
+
+int64_t items_for(int64_t r_cap, int S) {
+  const int64_t rows = (int64_t)kWaves * kTile * tiles_per_wave(r_cap);
+  return (r_cap + rows - 1) / rows + S;
+}
+
+// One wavefront per (segment, query head): merge that head's items.
+template <int HG>
+__global__ __launch_bounds__(64) void decode_combine_kernel(
+    const float2* __restrict__ part_ml, const float* __restrict__ part_o,
+    const int64_t* __restrict__ seg_off, const int32_t* __restrict__ seg_len, int64_t r_cap,
+    int hq, int hkv, int G, int D, int S, int tpw, int64_t items_max, float* __restrict__ out) {
+  const int s = blockIdx.x / G, g = blockIdx.x % G;
+  const int b = s / hkv, kvh = s % hkv;
+  const int lane = threadIdx.x;
+  const uint32_t rpi = (uint32_t)((int64_t)kWaves * kTile * tpw);
+  const SegLoc loc = wave_locate(seg_off, seg_len, S, r_cap, s, false,
+                                 [=](uint32_t l) { return (l + rpi - 1) / rpi; });
+  // overlapping segments (a violated precondition) can ask for more items than
+  // the workspace holds; those were never computed, so clip the range
+  const int64_t first = min(loc.first, items_max);
+  const int cnt = (int)(min(loc.first + loc.units, items_max) - first);
+  float* o = out + ((int64_t)b * hq + (int64_t)kvh * G + g) * D;
+  constexpr int kX = 2;  // output elements per lane (head_dim <= 128)
+
+  // per-lane running merge over items lane, lane + 64, ...; then across lanes
+  float M = -INFINITY, L = 0.f;
+  for (int it = lane; it < cnt; it += 64) {
+    const float2 ml = part_ml[(first + it) * HG + g];
+    const float mn = fmaxf(M, ml.x);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    L = L * __builtin_amdgcn_exp2f(M - ms) + ml.y * __builtin_amdgcn_exp2f(ml.x - ms);
+    M = mn;
+  }
+  float Mw = M;
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) Mw = fmaxf(Mw, __shfl_xor(Mw, x));
+  const float Ms = Mw == -INFINITY ? 0.f : Mw;
+  float Lw = L * __builtin_amdgcn_exp2f(M - Ms);
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) Lw += __shfl_xor(Lw, x);
+  const float inv = (Mw == -INFINITY || !(Lw > 0.f)) ? 0.f : 1.f / Lw;
+
+  float acc[kX] = {0.f, 0.f};
+  for (int c0 = 0; c0 < cnt; c0 += 64) {
+    const int nn = min(64, cnt - c0);
+    const float wl = lane < nn
+        ? __builtin_amdgcn_exp2f(part_ml[(first + c0 + lane) * HG + g].x - Ms) * inv : 0.f;
+    const float* po = part_o + ((first + c0) * HG + g) * D;
+    // batches of 8 items: 8 independent loads per element in flight
+    for (int j0 = 0; j0 < nn; j0 += 8) {
+      float v[8][kX], w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(j0 + u, nn - 1);           // tail rereads the last item, weight 0
+        w[u] = __shfl(wl, j0 + u < nn ? j0 + u : 63);
+#pragma unroll
+        for (int x = 0; x < kX; ++x) v[u][x] = po[(int64_t)j * HG * D + min(lane + 64 * x, D - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int x = 0; x < kX; ++x) acc[x] += (j0 + u < nn ? w[u] : 0.f) * v[u][x];
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < kX; ++x) {
+    const int d = lane + 64 * x;
+    if (d < D) o[d] = acc[x];
+  }
+}
 
 template <typename T, int D, int HG>
 hipError_t run(int batch, int hq, int hkv, float scale, const void* q, const void* k_c,
                const void* v_c, const int64_t* seg_off, const int32_t* seg_len, int64_t r_cap,
                float* out, void* ws, hipStream_t stream) {
   const int S = batch * hkv, G = hq / hkv;
-  const int64_t items = (r_cap + kDecodeRowsPerItem - 1) / kDecodeRowsPerItem + S;
+  const int tpw = tiles_per_wave(r_cap);
+  const int64_t items = items_for(r_cap, S);
   auto* ml = static_cast<float2*>(ws);
   auto* po = reinterpret_cast<float*>(ml + items * HG);
   const float c = scale * kLog2e;
-  const size_t lds = segment_table_bytes(S);
-  decode_split_kernel<T, D, HG><<<dim3((unsigned)items), dim3(kThreads), lds, stream>>>(
+  decode_split_kernel<T, D, HG><<<dim3((unsigned)items), dim3(kThreads), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(k_c),
-      static_cast<const char*>(v_c), seg_off, seg_len, r_cap, S, hq, hkv, G, c, ml, po);
-  decode_combine_kernel<HG><<<dim3(S * G), dim3(128), lds, stream>>>(
-      ml, po, seg_off, seg_len, r_cap, S, hq, hkv, G, D, items, out);
+      static_cast<const char*>(v_c), seg_off, seg_len, r_cap, S, hq, hkv, G, c, tpw, ml, po);
+  decode_combine_kernel<HG><<<dim3(S * G), dim3(64), 0, stream>>>(
+      ml, po, seg_off, seg_len, r_cap, hq, hkv, G, D, S, tpw, items, out);
   return hipGetLastError();
 }
 
@@ -298,9 +423,8 @@ hipError_t run_d(int batch, int hq, int hkv, float scale, const void* q, const v
 }  // namespace
 
 size_t decode_workspace_bytes(int S, int head_dim, int G, int64_t r_cap) {
-  const int64_t items = (r_cap + kDecodeRowsPerItem - 1) / kDecodeRowsPerItem + S;
   const int HG = hg_for(G);
-  return (size_t)items * HG * (sizeof(float2) + sizeof(float) * head_dim);
+  return (size_t)items_for(r_cap, S) * HG * (sizeof(float2) + sizeof(float) * head_dim);
 }
 
 hipError_t launch_decode(int dtype, int head_dim, int batch, int hq, int hkv, float scale,

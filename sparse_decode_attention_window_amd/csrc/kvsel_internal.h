@@ -20,7 +20,6 @@ struct bf16_t {  // storage-only 16-bit brain float
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSegments = 2048;    // batch * hkv handled by one call
-constexpr int kDecodeRowsPerItem = 256;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -109,6 +108,107 @@ __device__ __forceinline__ int find_segment(const int64_t* pre, int S, int64_t x
     if (pre[mid] <= x) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// ---------------------------------------------------------------------------
+// wave-level helpers (no LDS, no barrier)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+// max over the 16 lanes of a DPP row; every lane of the row gets the result
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_mov<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_mov<0x140>(v));  // row_mirror
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront, DPP only (no LDS).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return (uint32_t)x;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_u32(v), 63);
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int64_t readlane_i64(int64_t v, int lane) {
+  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)(uint64_t)v, lane);
+  const int hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), lane);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Segment s, clipped to the packed buffer: [off, off + len) inside [0, r_cap).
+__device__ __forceinline__ void clip_segment(const int64_t* seg_off, const int32_t* seg_len,
+                                             int s, int64_t r_cap, int64_t& off, int64_t& len) {
+  off = seg_off[s];
+  len = seg_len[s];
+  if (off < 0 || off > r_cap) off = r_cap;
+  len = len < 0 ? 0 : len;
+  len = len > r_cap - off ? r_cap - off : len;
+}
+
+struct SegLoc {
+  int s;            // segment, -1 when not found
+  int64_t first;    // index of the segment's first work unit
+  int64_t units;    // work units of the segment
+  int64_t off, len; // clipped row range
+};
+
+// Wave-uniform lookup over segments whose work-unit counts are units(len)
+// (units < 2^25 per segment, so 64 of them sum without overflow in 32 bits).
+// by_unit: find the segment owning unit `key`; otherwise describe segment `key`.
+template <typename Units>
+__device__ SegLoc wave_locate(const int64_t* __restrict__ seg_off,
+                              const int32_t* __restrict__ seg_len, int S, int64_t r_cap,
+                              int64_t key, bool by_unit, Units units) {
+  const int lane = threadIdx.x & 63;
+  SegLoc r{-1, 0, 0, 0, 0};
+  int64_t carry = 0;
+  for (int base = 0; base < S; base += 64) {
+    const int s = base + lane;
+    int64_t off = 0, len = 0;
+    uint32_t u = 0;
+    if (s < S) {
+      clip_segment(seg_off, seg_len, s, r_cap, off, len);
+      u = units((uint32_t)len);
+    }
+    const uint32_t incl = wave_incl_scan_u32(u);
+    const int64_t inc = carry + (int64_t)incl;
+    const uint64_t hit = by_unit ? __ballot(s < S && u > 0 && inc > key && inc - u <= key)
+                                 : __ballot(s == key);
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      r.s = base + f;
+      r.units = (uint32_t)__builtin_amdgcn_readlane((int)u, f);
+      r.first = carry + (uint32_t)__builtin_amdgcn_readlane((int)incl, f) - r.units;
+      r.off = readlane_i64(off, f);
+      r.len = readlane_i64(len, f);
+      return r;
+    }
+    carry += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  }
+  return r;
 }
 
 // LDS bytes a segment_table needs (pre, off, len).

@@ -35,6 +35,13 @@ struct SGeom {
   static constexpr int PITCH = RB + 16;       // LDS row pitch (breaks bank aliasing)
 };
 
+// Query rows padded to a power-of-two count of 32-row blocks (1, 2, 4 or 8).
+__host__ __device__ inline int padded_rows(int R) {
+  int b = 1;
+  while (b * 32 < R) b *= 2;
+  return b * 32;
+}
+
 // One 32-byte step of a 32x32 product: bf16 -> one 32x32x16 MFMA; fp32 -> four 32x32x2.
 __device__ __forceinline__ f32x16 mma_step(const u32x4& a, const u32x4& b, f32x16 acc, bf16_t) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -70,18 +77,56 @@ __device__ void stage_q(const char* __restrict__ qw, int b, int kvh, int hq, int
     if (Gm::NA * 32 > Gm::RB) store16(sq + i * Gm::PITCH + Gm::RB, u32x4{0, 0, 0, 0});
 }
 
+// Branch-free K fragment load of one key row (the caller clamps `key` into
+// [0, n)): a partial last 32-byte step (head_dim 88) reads zeros past the row.
 template <typename T, int D>
-__device__ __forceinline__ void load_k(const char* __restrict__ kseg, int64_t key, int64_t n,
-                                       int half, u32x4* kf) {
+__device__ __forceinline__ void load_k(const char* __restrict__ kseg, int64_t key, int half,
+                                       u32x4* kf) {
   using Gm = SGeom<T, D>;
+  const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
   for (int a = 0; a < Gm::NA; ++a) {
     const int o = 32 * a + 16 * half;
-    kf[a] = (key < n && o < Gm::RB) ? load16(kseg + key * Gm::RB + o) : u32x4{0, 0, 0, 0};
+    if (32 * (a + 1) <= Gm::RB) {
+      kf[a] = load16(kseg + key * Gm::RB + o);
+    } else {
+      const u32x4 x = load16(kseg + key * Gm::RB + min(o, Gm::RB - 16));
+      kf[a] = o < Gm::RB ? x : zero;
+    }
   }
 }
 
-template <typename T, int D>
+// Stream this wavefront's 32-key blocks of the tile with the next block's K
+// fragments in flight while the current one is processed.
+template <typename T, int D, typename F>
+__device__ __forceinline__ void for_each_key_block(const char* __restrict__ kseg, int64_t tile0,
+                                                   int wid, int64_t n, int lane, F&& process) {
+  using Gm = SGeom<T, D>;
+  constexpr int kBlocks = kIter * 2;
+  const int half = lane >> 5;
+  auto key0_of = [&](int i) { return tile0 + (int64_t)(wid * kBlocks + i) * 32; };
+  auto row_of = [&](int64_t key0) { return min(key0 + (lane & 31), n - 1); };
+  if (key0_of(0) >= n) return;
+  u32x4 ka[Gm::NA], kb[Gm::NA];
+  // sched_barrier keeps the scheduler from hoisting the prefetch above the
+  // loads of the block being processed (vmcnt waits are in issue order)
+  load_k<T, D>(kseg, row_of(key0_of(0)), half, ka);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kBlocks; i += 2) {
+    const int64_t k0 = key0_of(i), k1 = key0_of(i + 1);
+    load_k<T, D>(kseg, row_of(min(k1, n - 1)), half, kb);
+    __builtin_amdgcn_sched_barrier(0);
+    process(ka, k0);
+    if (i + 1 >= kBlocks || k1 >= n) break;
+    if (i + 2 < kBlocks) load_k<T, D>(kseg, row_of(min(key0_of(i + 2), n - 1)), half, ka);
+    __builtin_amdgcn_sched_barrier(0);
+    process(kb, k1);
+    if (i + 2 >= kBlocks || key0_of(i + 2) >= n) break;
+  }
+}
+
+template <typename T, int D, int RBN>
 __global__ __launch_bounds__(kThreads) void score_stats_kernel(
     const char* __restrict__ qw, const char* __restrict__ k, int64_t n, int hq, int hkv, int G,
     int w, int R, int64_t q_pos0, float c, float2* __restrict__ stats, int tiles) {
@@ -93,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(
 
   const int s = blockIdx.y, tile = blockIdx.x;
   const int b = s / hkv, kvh = s % hkv;
-  const int RP = (R + 31) & ~31, RBLK = RP / 32;
+  constexpr int RP = RBN * 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, half = lane >> 5;
   stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq);
   for (int r = tid; r < RP; r += kThreads) {
@@ -104,21 +149,14 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(
 
   const char* kseg = k + (int64_t)s * n * Gm::RB;
   const int64_t tile0 = (int64_t)tile * kTileKeys;
-  float Mr[kMaxRows / 32], Lr[kMaxRows / 32];
+  float Mr[RBN], Lr[RBN];
 #pragma unroll
-  for (int rb = 0; rb < kMaxRows / 32; ++rb) { Mr[rb] = -INFINITY; Lr[rb] = 0.f; }
+  for (int rb = 0; rb < RBN; ++rb) { Mr[rb] = -INFINITY; Lr[rb] = 0.f; }
 
-  for (int it = 0; it < kIter; ++it) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int64_t key0 = tile0 + (int64_t)((wid * kIter + it) * 2 + kb) * 32;
-      if (key0 >= n) break;
-      u32x4 kf[Gm::NA];
-      load_k<T, D>(kseg, key0 + (lane & 31), n, half, kf);
+  for_each_key_block<T, D>(kseg, tile0, wid, n, lane, [&](const u32x4* kf, int64_t key0) {
       const bool need_mask = key0 + 31 >= n || key0 + 31 > q_pos0;
 #pragma unroll
-      for (int rb = 0; rb < kMaxRows / 32; ++rb) {
-        if (rb >= RBLK) break;
+      for (int rb = 0; rb < RBN; ++rb) {
         f32x16 acc = {};
         const char* qrow = sq + (rb * 32 + (lane & 31)) * Gm::PITCH + 16 * half;
 #pragma unroll
@@ -127,10 +165,11 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(
         // lane owns query row rb*32 + lane%32 and 16 keys key0 + acc_row(j)
         float x[16];
         const int lr = lim[rb * 32 + (lane & 31)];
+        const int kb0 = (int)key0;   // keys < n < 2^31
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           x[j] = acc[j] * c;
-          if (need_mask && key0 + acc_row(j, lane) > lr) x[j] = -INFINITY;
+          if (need_mask && kb0 + acc_row(j, lane) > lr) x[j] = -INFINITY;
         }
         float tm = x[0];
 #pragma unroll
@@ -139,21 +178,19 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(
         const float ms = mn == -INFINITY ? 0.f : mn;
         float sum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sum += exp2f(x[j] - ms);
-        Lr[rb] = Lr[rb] * exp2f(Mr[rb] - ms) + sum;
+        for (int j = 0; j < 16; ++j) sum += __builtin_amdgcn_exp2f(x[j] - ms);
+        Lr[rb] = Lr[rb] * __builtin_amdgcn_exp2f(Mr[rb] - ms) + sum;
         Mr[rb] = mn;
       }
-    }
-  }
+  });
   // merge the two half-waves (same row, other 16 keys) and write per-wave stats
 #pragma unroll
-  for (int rb = 0; rb < kMaxRows / 32; ++rb) {
-    if (rb >= RBLK) break;
+  for (int rb = 0; rb < RBN; ++rb) {
     const float mo = __shfl_xor(Mr[rb], 32), lo = __shfl_xor(Lr[rb], 32);
     const float mn = fmaxf(Mr[rb], mo);
     const float ms = mn == -INFINITY ? 0.f : mn;
     const float L = Lr[rb] * exp2f(Mr[rb] - ms) + lo * exp2f(mo - ms);
-    if (half == 0) sm[wid][rb * 32 + lane] = make_float2(mn, L);
+    if (half == 0 && rb * 32 < RP) sm[wid][rb * 32 + lane] = make_float2(mn, L);
   }
   __syncthreads();
   for (int r = tid; r < RP; r += kThreads) {
@@ -168,24 +205,42 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(
   }
 }
 
-// rowc[s][r] = log2 of the row's normaliser in the log2 domain (max + log2(sum)); +inf for pad rows.
-__global__ __launch_bounds__(kMaxRows) void score_reduce_kernel(
-    const float2* __restrict__ stats, int tiles, int R, float* __restrict__ rowc) {
-  const int s = blockIdx.x, r = threadIdx.x;
-  const int RP = (R + 31) & ~31;
-  if (r >= RP) return;
-  float M = -INFINITY, L = 0.f;
-  for (int t = 0; t < tiles; ++t) {
-    const float2 v = stats[((int64_t)s * tiles + t) * RP + r];
-    const float mn = fmaxf(M, v.x);
-    const float ms = mn == -INFINITY ? 0.f : mn;
-    L = L * exp2f(M - ms) + v.y * exp2f(v.x - ms);
-    M = mn;
-  }
-  rowc[(int64_t)s * RP + r] = (r < R && L > 0.f) ? M + log2f(L) : INFINITY;
+// rowc[s][r] = log2 of the row's normaliser in the log2 domain (max + log2(sum));
+// +inf for pad rows.  1024 threads per segment: each row's tiles are split over
+// 1024 / RP threads, merged in LDS.
+constexpr int kReduceThreads = 1024;
+
+__device__ __forceinline__ void merge_ml(float& M, float& L, float m2, float l2) {
+  const float mn = fmaxf(M, m2);
+  const float ms = mn == -INFINITY ? 0.f : mn;
+  L = L * exp2f(M - ms) + l2 * exp2f(m2 - ms);
+  M = mn;
 }
 
-template <typename T, int D>
+__global__ __launch_bounds__(kReduceThreads) void score_reduce_kernel(
+    const float2* __restrict__ stats, int tiles, int R, float* __restrict__ rowc) {
+  __shared__ float2 part[kReduceThreads];
+  const int s = blockIdx.x, tid = threadIdx.x;
+  const int RP = padded_rows(R);
+  const int parts = kReduceThreads / RP;
+  const int r = tid % RP, pt = tid / RP;
+  float M = -INFINITY, L = 0.f;
+  if (pt < parts) {
+#pragma unroll 4
+    for (int t = pt; t < tiles; t += parts) {
+      const float2 v = stats[((int64_t)s * tiles + t) * RP + r];
+      merge_ml(M, L, v.x, v.y);
+    }
+  }
+  part[tid] = make_float2(M, L);
+  __syncthreads();
+  if (tid < RP) {
+    for (int q = 1; q < parts; ++q) merge_ml(M, L, part[q * RP + tid].x, part[q * RP + tid].y);
+    rowc[(int64_t)s * RP + tid] = (tid < R && L > 0.f) ? M + log2f(L) : INFINITY;
+  }
+}
+
+template <typename T, int D, int RBN>
 __global__ __launch_bounds__(kThreads) void score_final_kernel(
     const char* __restrict__ qw, const char* __restrict__ k, int64_t n, int hq, int hkv, int G,
     int w, int R, int64_t q_pos0, float c, const float* __restrict__ rowc,
@@ -198,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
 
   const int s = blockIdx.y, tile = blockIdx.x;
   const int b = s / hkv, kvh = s % hkv;
-  const int RP = (R + 31) & ~31, RBLK = RP / 32;
+  constexpr int RP = RBN * 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, half = lane >> 5;
   stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq);
   for (int r = tid; r < RP; r += kThreads) {
@@ -210,19 +265,12 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
 
   const char* kseg = k + (int64_t)s * n * Gm::RB;
   const int64_t tile0 = (int64_t)tile * kTileKeys;
-  for (int it = 0; it < kIter; ++it) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int64_t key0 = tile0 + (int64_t)((wid * kIter + it) * 2 + kb) * 32;
-      if (key0 >= n) break;
+  for_each_key_block<T, D>(kseg, tile0, wid, n, lane, [&](const u32x4* kf, int64_t key0) {
       const int64_t key = key0 + (lane & 31);
-      u32x4 kf[Gm::NA];
-      load_k<T, D>(kseg, key, n, half, kf);
       const bool need_mask = key0 + 31 >= n || key0 + 31 > q_pos0;
       float ssum = 0.f;
 #pragma unroll
-      for (int rb = 0; rb < kMaxRows / 32; ++rb) {
-        if (rb >= RBLK) break;
+      for (int rb = 0; rb < RBN; ++rb) {
         f32x16 acc = {};
         const char* qrow = sq + (rb * 32 + (lane & 31)) * Gm::PITCH + 16 * half;
 #pragma unroll
@@ -236,52 +284,67 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
           const float kk[4] = {kr.x, kr.y, kr.z, kr.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float p = exp2f(acc[g4 * 4 + e] * c - kk[e]);
-            if (need_mask && key > lim[r0 + e]) p = 0.f;
+            float p = __builtin_amdgcn_exp2f(acc[g4 * 4 + e] * c - kk[e]);
+            if (need_mask && (int)key > lim[r0 + e]) p = 0.f;
             ssum += p;
           }
         }
       }
       ssum += __shfl_xor(ssum, 32);
       if (half == 0 && key < n) scores[(int64_t)s * n + key] = ssum;
-    }
+  });
+}
+
+template <typename T, int D, int RBN>
+hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int64_t q_pos0,
+                    float c, const char* qp, const char* kp, float* scores, float2* stats,
+                    float* rowc, int tiles, hipStream_t stream) {
+  using Gm = SGeom<T, D>;
+  const size_t lds = (size_t)RBN * 32 * Gm::PITCH;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)score_stats_kernel<T, D, RBN>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)score_final_kernel<T, D, RBN>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
   }
+  const dim3 grid(tiles, S);
+  score_stats_kernel<T, D, RBN><<<grid, dim3(kThreads), lds, stream>>>(
+      qp, kp, n, hq, hkv, G, w, R, q_pos0, c, stats, tiles);
+  score_reduce_kernel<<<dim3(S), dim3(kReduceThreads), 0, stream>>>(stats, tiles, R, rowc);
+  score_final_kernel<T, D, RBN><<<grid, dim3(kThreads), lds, stream>>>(
+      qp, kp, n, hq, hkv, G, w, R, q_pos0, c, rowc, scores);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t run(int batch, int hq, int hkv, int w, int64_t n, int64_t q_pos0, float scale,
                const void* q_win, const void* k, float* scores, void* ws, hipStream_t stream) {
-  using Gm = SGeom<T, D>;
   const int S = batch * hkv, G = hq / hkv, R = G * w;
-  const int RP = (R + 31) & ~31;
+  const int RP = padded_rows(R);
   const int tiles = (int)((n + kTileKeys - 1) / kTileKeys);
   auto* stats = static_cast<float2*>(ws);
   auto* rowc = reinterpret_cast<float*>(stats + (size_t)S * tiles * RP);
   const float c = scale * kLog2e;
-  const size_t lds = (size_t)RP * Gm::PITCH;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)score_stats_kernel<T, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)score_final_kernel<T, D>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  const dim3 grid(tiles, S);
   auto qp = static_cast<const char*>(q_win);
   auto kp = static_cast<const char*>(k);
-  score_stats_kernel<T, D><<<grid, dim3(kThreads), lds, stream>>>(qp, kp, n, hq, hkv, G, w, R,
-                                                                  q_pos0, c, stats, tiles);
-  score_reduce_kernel<<<dim3(S), dim3(kMaxRows), 0, stream>>>(stats, tiles, R, rowc);
-  score_final_kernel<T, D><<<grid, dim3(kThreads), lds, stream>>>(qp, kp, n, hq, hkv, G, w, R,
-                                                                  q_pos0, c, rowc, scores);
-  return hipGetLastError();
+#define KVSEL_ROWS(RBN) \
+  return run_rows<T, D, RBN>(S, hq, hkv, G, w, R, n, q_pos0, c, qp, kp, scores, stats, rowc, \
+                             tiles, stream)
+  switch (RP / 32) {
+    case 1: KVSEL_ROWS(1);
+    case 2: KVSEL_ROWS(2);
+    case 4: KVSEL_ROWS(4);
+    default: KVSEL_ROWS(8);
+  }
+#undef KVSEL_ROWS
 }
 
 }  // namespace
 
 size_t score_workspace_bytes(int S, int64_t n, int rows) {
-  const int RP = (rows + 31) & ~31;
+  const int RP = padded_rows(rows);
   const int64_t tiles = (n + kTileKeys - 1) / kTileKeys;
   return (size_t)S * tiles * RP * sizeof(float2) + (size_t)S * RP * sizeof(float);
 }

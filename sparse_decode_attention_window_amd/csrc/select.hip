@@ -7,12 +7,16 @@
 // POLICY local / special-token / global head rules (FastGen page).
 //
 // TOPB and CHUNK share one weighted radix select: scores become order-
-// preserving 32-bit keys (NaN lowest, -0 folded into +0), three digit passes
-// (11, 11, 10 bits) over an LDS histogram find the threshold key T and how
-// much weight must come from keys equal to T, then an ordered sweep keeps
-// every key > T plus the first keys == T in index order.  Because kept
-// tokens are emitted by a block-wide prefix over index order, the output is
-// ascending and the tie-break is the lowest index, deterministically.
+// preserving 32-bit keys (NaN lowest, -0 folded into +0) held in LDS; four
+// 8-bit digit passes find the threshold key T and how much weight must come
+// from keys equal to T; an ordered sweep then keeps every key > T plus the
+// first keys == T in index order.  Histogram updates go to 16 replicas (lane
+// mod 16, padded so a bin's replicas sit in different banks), which keeps LDS
+// atomic conflicts low even when most scores share their top bits.  Kept
+// tokens are placed by wave ballots / DPP scans in index order, so the output
+// is ascending and the tie-break is the lowest index, deterministically.
+#include <type_traits>
+
 #include "kvsel_internal.h"
 
 namespace kvsel {
@@ -20,7 +24,10 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kHistBins = 2048;
+constexpr int kBins = 256;
+constexpr int kReps = 16;
+constexpr int kRepPitch = kBins + 1;   // bank offset between replicas
+constexpr int kHistWords = kReps * kRepPitch;
 
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t b = __float_as_uint(f);
@@ -29,32 +36,9 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
-// Exclusive block-wide scan in thread order (all kThreads threads must call).
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* wave_tot) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const uint32_t inc = wave_incl_scan(v);
-  if (lane == 63) wave_tot[wid] = inc;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < wid; ++w) before += wave_tot[w];
-  __syncthreads();
-  return before + inc - v;
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 template <bool WEIGHTED, bool CACHED>
@@ -64,11 +48,11 @@ __global__ __launch_bounds__(kThreads) void select_rank_kernel(
     const int64_t* __restrict__ seg_off, int32_t* __restrict__ seg_len,
     int32_t* __restrict__ idx, int64_t r_cap) {
   extern __shared__ uint32_t lds[];
-  uint32_t* hist = lds;                  // kHistBins
-  uint32_t* keys = lds + kHistBins;      // N (CACHED)
-  uint32_t* wts = keys + (CACHED ? N : 0);  // N (CACHED && WEIGHTED)
+  uint32_t* hist = lds;                           // kHistWords
+  uint32_t* keys = lds + kHistWords;              // N (CACHED)
+  uint32_t* wts = keys + (CACHED ? N : 0);        // N (CACHED && WEIGHTED)
   __shared__ uint32_t wave_tot[kWaves];
-  __shared__ uint32_t w_gt[kWaves], w_eq[kWaves], w_kept[kWaves];
+  __shared__ uint32_t w_eq[kWaves], w_kept[kWaves];
   __shared__ uint32_t sel_digit, sel_above;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -77,18 +61,16 @@ __global__ __launch_bounds__(kThreads) void select_rank_kernel(
   const float* sc = scores + (int64_t)s * N;
   const int64_t* ce = WEIGHTED ? chunk_end + (int64_t)b * N : nullptr;
 
-  int64_t off = seg_off[s];
+  const int64_t off = seg_off[s];
   const bool off_ok = off >= 0 && off <= r_cap;
   const int64_t room = off_ok ? r_cap - off : 0;  // rows we may write
 
   auto weight = [&](int64_t j) -> uint32_t {
     if (!WEIGHTED) return 1u;
     if (CACHED) return wts[j];
-    const int64_t lo = j ? ce[j - 1] : 0;
-    return (uint32_t)(ce[j] - lo);
+    return (uint32_t)(ce[j] - (j ? ce[j - 1] : 0));
   };
   auto key_of = [&](int64_t j) -> uint32_t { return CACHED ? keys[j] : score_key(sc[j]); };
-  auto chunk_start = [&](int64_t j) -> int64_t { return j ? ce[j - 1] : 0; };
 
   const int64_t total = WEIGHTED ? ce[N - 1] : N;
   int64_t tgt = WEIGHTED ? keep_tokens : (int64_t)budget[s];
@@ -102,46 +84,48 @@ __global__ __launch_bounds__(kThreads) void select_rank_kernel(
   }
 
   if (CACHED) {
+#pragma unroll 8
     for (int64_t j = tid; j < N; j += kThreads) {
       keys[j] = score_key(sc[j]);
       if (WEIGHTED) wts[j] = (uint32_t)(ce[j] - (j ? ce[j - 1] : 0));
     }
   }
 
-  // ---- radix select of the threshold key -------------------------------
+  // ---- radix select of the threshold key (4 x 8-bit digits) ----------
   uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)tgt;
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass];
-    const int nb = 1 << widths[pass];
-    const uint32_t dmask = (uint32_t)nb - 1u;
-    for (int i = tid; i < nb; i += kThreads) hist[i] = 0;
+  uint32_t* my_hist = hist + (lane & (kReps - 1)) * kRepPitch;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < kHistWords; i += kThreads) hist[i] = 0;
     __syncthreads();
+#pragma unroll 4
     for (int64_t j = tid; j < N; j += kThreads) {
       const uint32_t k = key_of(j);
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], weight(j));
+      if ((k & pmask) == prefix) atomicAdd(&my_hist[(k >> shift) & 0xffu], weight(j));
     }
     __syncthreads();
-    // thread t owns the bins (nb-1 - bpt*t - i), i < bpt: digits in descending order
-    const int bpt = nb / kThreads;
+    // thread t < 256 owns digit 255 - t (descending); sum its replicas
     uint32_t mine = 0;
-    for (int i = 0; i < bpt; ++i) mine += hist[nb - 1 - bpt * tid - i];
-    uint32_t above = block_excl_scan(mine, wave_tot);
-    for (int i = 0; i < bpt; ++i) {
-      const int d = nb - 1 - bpt * tid - i;
-      const uint32_t h = hist[d];
-      if (above < remaining && remaining <= above + h) {
-        sel_digit = (uint32_t)d;
+    if (tid < kBins) {
+#pragma unroll
+      for (int r = 0; r < kReps; ++r) mine += hist[r * kRepPitch + (kBins - 1 - tid)];
+    }
+    // exclusive scan over the 256 owners (waves 0..3)
+    const uint32_t inc = wave_incl_scan_u32(mine);
+    if (lane == 63) wave_tot[wid] = inc;
+    __syncthreads();
+    if (tid < kBins) {
+      uint32_t above = inc - mine;
+      for (int w = 0; w < wid; ++w) above += wave_tot[w];
+      if (above < remaining && remaining <= above + mine) {
+        sel_digit = (uint32_t)(kBins - 1 - tid);
         sel_above = above;
       }
-      above += h;
     }
     __syncthreads();
     prefix |= sel_digit << shift;
-    pmask |= dmask << shift;
+    pmask |= 0xffu << shift;
     remaining -= sel_above;
-    __syncthreads();
   }
   const uint32_t T = prefix;  // remaining = weight still needed from keys == T (>= 1)
 
@@ -151,35 +135,58 @@ __global__ __launch_bounds__(kThreads) void select_rank_kernel(
   const int64_t lo = (int64_t)wid * per;
   const int64_t hi = lo + per < N ? lo + per : N;
 
-  uint32_t gt = 0, eq = 0;
-  for (int64_t j = lo + lane; j < hi; j += 64) {
-    const uint32_t k = key_of(j), w = weight(j);
-    gt += k > T ? w : 0u;
-    eq += k == T ? w : 0u;
-  }
-  gt = wave_sum(gt);
-  eq = wave_sum(eq);
-  if (lane == 0) { w_gt[wid] = gt; w_eq[wid] = eq; }
+  uint32_t eq = 0;
+  for (int64_t j = lo + lane; j < hi; j += 64) eq += key_of(j) == T ? weight(j) : 0u;
+  eq = wave_sum_u32(eq);
+  if (lane == 0) w_eq[wid] = eq;
   __syncthreads();
   uint32_t eq_before = 0;
   for (int w = 0; w < wid; ++w) eq_before += w_eq[w];
 
   // an item equal to T is kept while the equal weight before it is short of `remaining`
-  uint32_t kept = 0;
-  {
-    uint32_t run = eq_before;
+  auto sweep = [&](bool write, uint32_t pos0) -> uint32_t {
+    uint32_t run = eq_before, kept = 0;
     for (int64_t base = lo; base < hi; base += 64) {
       const int64_t j = base + lane;
       uint32_t k = 0, w = 0;
       if (j < hi) { k = key_of(j); w = weight(j); }
-      const uint32_t e = (j < hi && k == T) ? w : 0u;
-      const uint32_t inc = wave_incl_scan(e);
-      const bool keep = j < hi && (k > T || (k == T && run + inc - e < remaining));
-      kept += keep ? w : 0u;
-      run += __shfl(inc, 63);
+      const bool is_eq = j < hi && k == T;
+      bool keep;
+      uint32_t step_eq, kbefore, step_kept;
+      if (!WEIGHTED) {
+        const uint64_t em = __ballot(is_eq);
+        keep = j < hi && (k > T || (is_eq && run + lanes_below(em) < remaining));
+        const uint64_t km = __ballot(keep);
+        step_eq = (uint32_t)__popcll(em);
+        kbefore = lanes_below(km);
+        step_kept = (uint32_t)__popcll(km);
+      } else {
+        const uint32_t e = is_eq ? w : 0u;
+        const uint32_t einc = wave_incl_scan_u32(e);
+        keep = j < hi && (k > T || (is_eq && run + einc - e < remaining));
+        const uint32_t kw = keep ? w : 0u;
+        const uint32_t kinc = wave_incl_scan_u32(kw);
+        step_eq = (uint32_t)__builtin_amdgcn_readlane((int)einc, 63);
+        kbefore = kinc - kw;
+        step_kept = (uint32_t)__builtin_amdgcn_readlane((int)kinc, 63);
+      }
+      if (write && keep) {
+        const int64_t pos = (int64_t)pos0 + kept + kbefore;
+        if (WEIGHTED) {
+          const int64_t st = j ? ce[j - 1] : 0;
+          for (uint32_t t = 0; t < w; ++t)
+            if (pos + t < room) idx[off + pos + t] = (int32_t)(st + t);
+        } else if (pos < room) {
+          idx[off + pos] = (int32_t)j;
+        }
+      }
+      run += step_eq;
+      kept += step_kept;
     }
-  }
-  kept = wave_sum(kept);
+    return kept;
+  };
+
+  const uint32_t kept = sweep(false, 0);
   if (lane == 0) w_kept[wid] = kept;
   __syncthreads();
   uint32_t out_before = 0, out_total = 0;
@@ -188,30 +195,185 @@ __global__ __launch_bounds__(kThreads) void select_rank_kernel(
     out_total += w_kept[w];
   }
   if (tid == 0) seg_len[s] = (int32_t)out_total;
+  sweep(true, out_before);
+}
 
-  {
-    uint32_t run = eq_before, pos0 = out_before;
-    for (int64_t base = lo; base < hi; base += 64) {
-      const int64_t j = base + lane;
-      uint32_t k = 0, w = 0;
-      if (j < hi) { k = key_of(j); w = weight(j); }
-      const uint32_t e = (j < hi && k == T) ? w : 0u;
-      const uint32_t inc = wave_incl_scan(e);
-      const bool keep = j < hi && (k > T || (k == T && run + inc - e < remaining));
-      const uint32_t kw = keep ? w : 0u;
-      const uint32_t kinc = wave_incl_scan(kw);
-      const int64_t pos = (int64_t)pos0 + kinc - kw;
-      if (keep) {
-        if (WEIGHTED) {
-          const int64_t st = chunk_start(j);
-          for (uint32_t t = 0; t < w; ++t)
-            if (pos + t < room) idx[off + pos + t] = (int32_t)(st + t);
-        } else if (pos < room) {
-          idx[off + pos] = (int32_t)j;
-        }
+// ---------------------------------------------------------------------------
+// Register-resident variant for N <= 1024 * KPT items: thread t holds items
+// j = k * 1024 + t (k < KPT) in registers, so the radix passes read no
+// memory; histograms use 11-bit digits (3 passes) over 8 padded replicas.
+// Emission orders items k-major, thread-minor (that is index order): per
+// (k, wavefront) block the kept count / weight is known from ballots or DPP
+// sums, one block-wide scan over the 16 * KPT blocks places them.
+// ---------------------------------------------------------------------------
+constexpr int kRBins = 2048;
+constexpr int kRReps = 8;
+constexpr int kRPitch = kRBins + 1;
+
+// Exclusive scan of vals[0..M) in LDS (M <= 1024) by the whole block.
+__device__ void block_scan_lds(uint32_t* vals, int M, uint32_t* wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const uint32_t v = tid < M ? vals[tid] : 0u;
+  const uint32_t inc = wave_incl_scan_u32(v);
+  if (lane == 63) wave_tot[wid] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int w = 0; w < wid; ++w) before += wave_tot[w];
+  if (tid < M) vals[tid] = before + inc - v;
+  __syncthreads();
+}
+
+template <bool WEIGHTED, int KPT>
+__global__ __launch_bounds__(kThreads) void select_reg_kernel(
+    const float* __restrict__ scores, int64_t N, int hkv, const int32_t* __restrict__ budget,
+    const int64_t* __restrict__ chunk_end, int64_t keep_tokens,
+    const int64_t* __restrict__ seg_off, int32_t* __restrict__ seg_len,
+    int32_t* __restrict__ idx, int64_t r_cap) {
+  __shared__ uint32_t hist[kRReps * kRPitch];
+  __shared__ uint32_t blk_a[kWaves * KPT], blk_b[kWaves * KPT];
+  __shared__ uint32_t wave_tot[kWaves];
+  __shared__ uint32_t sel_digit, sel_above;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int s = blockIdx.x;
+  const int b = s / hkv;
+  const float* sc = scores + (int64_t)s * N;
+  const int64_t* ce = WEIGHTED ? chunk_end + (int64_t)b * N : nullptr;
+  const int64_t off = seg_off[s];
+  const bool off_ok = off >= 0 && off <= r_cap;
+  const int64_t room = off_ok ? r_cap - off : 0;
+
+  const int64_t total = WEIGHTED ? ce[N - 1] : N;
+  int64_t tgt = WEIGHTED ? keep_tokens : (int64_t)budget[s];
+  tgt = tgt < 0 ? 0 : (tgt > total ? total : tgt);
+  if (tgt == 0 || tgt == total) {
+    for (int64_t r = tid; r < tgt && r < room; r += kThreads) idx[off + r] = (int32_t)r;
+    if (tid == 0) seg_len[s] = (int32_t)tgt;
+    return;
+  }
+
+  // ---- items into registers (all loads independent) --------------------
+  // Unweighted items have weight 1 (0 past N); weights of chunks are lengths.
+  uint32_t key[KPT];
+  uint32_t wt[WEIGHTED ? KPT : 1];
+  auto weight = [&](int k) -> uint32_t {
+    if constexpr (WEIGHTED) return wt[k];
+    else return (int64_t)k * kThreads + tid < N ? 1u : 0u;
+  };
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int64_t j = (int64_t)k * kThreads + tid;
+    const int64_t jc = j < N ? j : N - 1;
+    key[k] = score_key(sc[jc]);
+    if constexpr (WEIGHTED) {
+      const int64_t lo = jc ? ce[jc - 1] : 0;
+      wt[k] = j < N ? (uint32_t)(ce[jc] - lo) : 0u;
+    }
+  }
+
+  // ---- radix select: 11 + 11 + 10 bits ------------------------------------
+  uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)tgt;
+  uint32_t* my_hist = hist + (lane & (kRReps - 1)) * kRPitch;
+  auto pass = [&](auto shift_c, auto width_c) {
+    constexpr int shift = decltype(shift_c)::value;
+    constexpr int nb = 1 << decltype(width_c)::value;
+    constexpr uint32_t dmask = (uint32_t)nb - 1u;
+    for (int i = tid; i < kRReps * kRPitch; i += kThreads) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const uint32_t w = weight(k);
+      if (w && (key[k] & pmask) == prefix) atomicAdd(&my_hist[(key[k] >> shift) & dmask], w);
+    }
+    __syncthreads();
+    // thread t owns digits nb-1-2t and nb-2-2t (descending order)
+    uint32_t h2[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int d = nb - 1 - 2 * tid - i;
+      if (d >= 0)
+#pragma unroll
+        for (int r = 0; r < kRReps; ++r) h2[i] += hist[r * kRPitch + d];
+    }
+    const uint32_t mine = h2[0] + h2[1];
+    const uint32_t inc = wave_incl_scan_u32(mine);
+    if (lane == 63) wave_tot[wid] = inc;
+    __syncthreads();
+    uint32_t above = inc - mine;
+    for (int w = 0; w < wid; ++w) above += wave_tot[w];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int d = nb - 1 - 2 * tid - i;
+      if (d >= 0 && above < remaining && remaining <= above + h2[i]) {
+        sel_digit = (uint32_t)d;
+        sel_above = above;
       }
-      run += __shfl(inc, 63);
-      pos0 += __shfl(kinc, 63);
+      above += h2[i];
+    }
+    __syncthreads();
+    prefix |= sel_digit << shift;
+    pmask |= dmask << shift;
+    remaining -= sel_above;
+    __syncthreads();
+  };
+  pass(std::integral_constant<int, 21>{}, std::integral_constant<int, 11>{});
+  pass(std::integral_constant<int, 10>{}, std::integral_constant<int, 11>{});
+  pass(std::integral_constant<int, 0>{}, std::integral_constant<int, 10>{});
+  const uint32_t T = prefix;
+
+  // ---- ordered emission over (k, wave) blocks ------------------------------
+  // an item equal to T is kept while the equal weight before it (index order)
+  // is short of `remaining`; every item > T is kept
+  auto eq_w = [&](int k) -> uint32_t { return key[k] == T ? weight(k) : 0u; };
+  auto eq_before_in_wave = [&](int k) -> uint32_t {
+    const uint32_t e = eq_w(k);
+    return WEIGHTED ? wave_incl_scan_u32(e) - e : lanes_below(__ballot(e != 0u));
+  };
+  // 1) equal-key weight per block, scanned in index order
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const uint32_t e = eq_w(k);
+    const uint32_t es = WEIGHTED ? wave_sum_u32(e) : (uint32_t)__popcll(__ballot(e != 0u));
+    if (lane == 0) blk_a[k * kWaves + wid] = es;
+  }
+  __syncthreads();
+  block_scan_lds(blk_a, KPT * kWaves, wave_tot);
+  auto kept_w = [&](int k) -> uint32_t {
+    const uint32_t w = weight(k);
+    // cross-lane scan first, with every lane active
+    const uint32_t eb = blk_a[k * kWaves + wid] + eq_before_in_wave(k);
+    const bool keep = w && (key[k] > T || (key[k] == T && eb < remaining));
+    return keep ? w : 0u;
+  };
+  // 2) kept weight per block, scanned in index order
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const uint32_t kw = kept_w(k);
+    const uint32_t ks = WEIGHTED ? wave_sum_u32(kw) : (uint32_t)__popcll(__ballot(kw != 0u));
+    if (lane == 0) blk_b[k * kWaves + wid] = ks;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < KPT * kWaves; ++i) t += blk_b[i];
+    seg_len[s] = (int32_t)t;
+  }
+  block_scan_lds(blk_b, KPT * kWaves, wave_tot);
+  // 3) write the kept token positions
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int64_t j = (int64_t)k * kThreads + tid;
+    const uint32_t kw = kept_w(k);
+    const uint32_t before = WEIGHTED ? wave_incl_scan_u32(kw) - kw : lanes_below(__ballot(kw != 0u));
+    const int64_t pos = (int64_t)blk_b[k * kWaves + wid] + before;
+    if (kw) {
+      if (WEIGHTED) {
+        const int64_t st = j ? ce[j - 1] : 0;
+        for (uint32_t t = 0; t < kw; ++t)
+          if (pos + t < room) idx[off + pos + t] = (int32_t)(st + t);
+      } else if (pos < room) {
+        idx[off + pos] = (int32_t)j;
+      }
     }
   }
 }
@@ -258,6 +420,32 @@ hipError_t launch_rank(int S, int hkv, int64_t N, const float* scores, const int
   return hipGetLastError();
 }
 
+
+template <bool W, int KPT>
+hipError_t launch_reg(int S, int hkv, int64_t N, const float* scores, const int32_t* budget,
+                      const int64_t* chunk_end, int64_t keep_tokens, const int64_t* seg_off,
+                      int32_t* seg_len, int32_t* idx, int64_t r_cap, hipStream_t stream) {
+  select_reg_kernel<W, KPT><<<dim3(S), dim3(kThreads), 0, stream>>>(
+      scores, N, hkv, budget, chunk_end, keep_tokens, seg_off, seg_len, idx, r_cap);
+  return hipGetLastError();
+}
+
+template <bool W>
+hipError_t launch_reg_n(int S, int hkv, int64_t N, const float* scores, const int32_t* budget,
+                        const int64_t* chunk_end, int64_t keep_tokens, const int64_t* seg_off,
+                        int32_t* seg_len, int32_t* idx, int64_t r_cap, hipStream_t stream) {
+#define KVSEL_REG(K) \
+  return launch_reg<W, K>(S, hkv, N, scores, budget, chunk_end, keep_tokens, seg_off, seg_len, \
+                          idx, r_cap, stream)
+  if (N <= 1 * kThreads) KVSEL_REG(1);
+  if (N <= 2 * kThreads) KVSEL_REG(2);
+  if (N <= 4 * kThreads) KVSEL_REG(4);
+  if (N <= 8 * kThreads) KVSEL_REG(8);
+  if (N <= 16 * kThreads) KVSEL_REG(16);
+  KVSEL_REG(32);
+#undef KVSEL_REG
+}
+
 }  // namespace
 
 hipError_t launch_select_rank(int S, int hkv, int64_t n_items, const float* scores,
@@ -265,9 +453,15 @@ hipError_t launch_select_rank(int S, int hkv, int64_t n_items, const float* scor
                               const int64_t* seg_off, int32_t* seg_len, int32_t* idx,
                               int64_t r_cap, hipStream_t stream) {
   const bool weighted = chunk_end != nullptr;
-  const size_t base = kHistBins * sizeof(uint32_t);
+  if (n_items <= 32 * kThreads)
+    return weighted ? launch_reg_n<true>(S, hkv, n_items, scores, budget, chunk_end, keep_tokens,
+                                         seg_off, seg_len, idx, r_cap, stream)
+                    : launch_reg_n<false>(S, hkv, n_items, scores, budget, chunk_end, keep_tokens,
+                                          seg_off, seg_len, idx, r_cap, stream);
+  // longer segments: keys cached in LDS when they fit, else re-read from global
+  const size_t base = kHistWords * sizeof(uint32_t);
   const size_t per_item = weighted ? 8 : 4;
-  const size_t static_lds = 1024;  // wave totals and broadcast slots
+  const size_t static_lds = 2048;  // wave totals and broadcast slots
   const size_t want = base + per_item * (size_t)n_items;
   const bool cached = want + static_lds <= (size_t)device_info().max_lds;
   const size_t lds = cached ? want : base;

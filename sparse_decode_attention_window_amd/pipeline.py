@@ -93,7 +93,7 @@ class LayerRun:
         self.out = torch.empty((self.shape.batch, self.shape.hq, d), dtype=torch.float32,
                                device=dev)
         nb = K.kvsel_decode_workspace(self.shape, self.r_cap)
-        self.ws_dec = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        self.ws_dec = torch.zeros(max(nb, 1), dtype=torch.uint8, device=dev)
         return self
 
     def score(self, stream=None):

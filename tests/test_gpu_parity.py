@@ -354,3 +354,54 @@ def test_score_shapes(kv, dtype, d, G, w, n, q_pos0):
         ref = oracle.window_scores(oracle.to_f64(q[b, h * G:(h + 1) * G]), oracle.to_f64(Kf[b, h]),
                                    1 / math.sqrt(d), q_pos0)
         pu.check_scores(s_gpu[s], ref, G * w, f"score seg {s}")
+
+
+# ---------------------------------------------------------------------------
+# workspace state and graph replays
+# ---------------------------------------------------------------------------
+
+def test_decode_garbage_workspace(kv):
+    """The decode scratch needs no initialisation: fill it with junk bytes."""
+    kvsel, pipeline, torch = kv
+    cfg = kvsynth.get_config(1, n=2500)
+    _say(cfg.name, "decode with a junk-filled workspace")
+    inputs, run = _run(kv, cfg)
+    want = pu.to_host(run.out).copy()
+    for fill in (0xFF, 0x01, 0x7F):
+        run.ws_dec.fill_(fill)
+        run.decode()
+        torch.cuda.synchronize()
+        assert np.array_equal(pu.to_host(run.out), want), hex(fill)
+
+
+@pytest.mark.parametrize("cid", [1, 3, 4])
+def test_graph_replays_match_eager(kv, cid):
+    """Capture one layer (score, select, compact, decode) in a HIP graph; replay
+    it several times with eager work in between; every replay must reproduce
+    the eager results bit for bit."""
+    kvsel, pipeline, torch = kv
+    over = {1: dict(n=3000), 3: dict(batch=2, n=3000), 4: dict(n=9000)}[cid]
+    cfg = kvsynth.get_config(cid, **over)
+    _say(cfg.name, "graph replay")
+    inputs, run = _run(kv, cfg)
+    want = _host(run)
+    other_inputs, other = _run(kv, kvsynth.get_config(1, n=1111))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        run.out.zero_()
+        run.idx.fill_(-3)
+        other.run()                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = _host(run)
+        for key in ("seg_off", "seg_len", "scores", "out"):
+            if want[key] is not None:
+                assert np.array_equal(got[key], want[key]), (rep, key)
+        # packed rows: only each segment's written prefix is defined
+        for s, (o, n_) in enumerate(zip(want["seg_off"], want["seg_len"])):
+            for key in ("idx", "k_c", "v_c"):
+                assert np.array_equal(got[key][o:o + n_], want[key][o:o + n_]), (rep, key, s)
