@@ -32,16 +32,77 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 METRIC = "compacted decode-attn HBM GB/s (% peak) + select-and-compact µs/layer, 32K ctx"
 COUNTERS = os.path.join(ROOT, "profiles", "decode_c2_counters.json")
-DECODE_SRC = os.path.join(ROOT, "sparse_decode_attention_window_amd", "csrc", "decode.hip")
+CSRC = os.path.join(ROOT, "sparse_decode_attention_window_amd", "csrc")
+DECODE_SRCS = [os.path.join(CSRC, f) for f in ("decode.hip", "kvsel_internal.h")]
+DECODE_KERNELS = ("decode_split_kernel", "decode_combine_kernel")
+COPY_BYTES = 1 << 30           # plain device copy used as HBM reference and counter calibration
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def src_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def copy_reference(torch, reps: int = 5) -> float:
+    """GB/s (read + write) of a plain 1 GiB device-to-device copy on this GPU."""
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) / reps * 1e-3
+    del src, dst
+    return 2 * COPY_BYTES / t / 1e9
+
+
+def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes per decode launch from two rocprofv3 --pmc runs of this
+    script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by the
+    same counter's reading on the 1 GiB reference copy (known bytes)."""
+    import csv
+
+    def rows(path, counter):
+        with open(path) as f:
+            rs = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        rs.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rs]
+
+    def reference_copy(rs):
+        # copy_reference(): a bf16 fill of the source, then the first device copy after it
+        fill = next(i for i, (k, _) in enumerate(rs) if "FillFunctor<c10::BFloat16>" in k)
+        return next(v for k, v in rs[fill + 1:] if "copy" in k.lower())
+
+    out = {"source_sha256_16": src_hash(DECODE_SRCS), "copy_bytes": COPY_BYTES}
+    per_launch = 0.0
+    for counter, path, known in (("FETCH_SIZE", fetch_csv, COPY_BYTES),
+                                 ("WRITE_SIZE", write_csv, COPY_BYTES)):
+        rs = rows(path, counter)
+        copies = [reference_copy(rs)]
+        factor = known / (copies[0] * 1024)
+        kern = {}
+        for name in DECODE_KERNELS:
+            vals = [v for k, v in rs if name in k]
+            assert vals, f"no {name} dispatch in {path}"
+            kern[name] = {"dispatches": len(vals), "mean_KiB": sum(vals) / len(vals)}
+        launch_kib = sum(k["mean_KiB"] for k in kern.values())
+        out[counter] = {"copy_KiB": max(copies), "scale_factor": factor, "kernels": kern,
+                        "raw_KiB_per_launch": launch_kib,
+                        "bytes_per_launch": launch_kib * 1024 * factor}
+        per_launch += launch_kib * 1024 * factor
+    out["hbm_bytes_per_launch"] = int(per_launch)
+    return out
 
 
 def blas_threads() -> int:
@@ -108,7 +169,15 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the decode traffic file from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        res = summarize_counters(*args.summarize_counters)
+        with open(COUNTERS, "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res, indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path needs no collective; see the sharding notes in DESIGN.md)",
@@ -124,6 +193,8 @@ def main() -> int:
     kvsel.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    copy_gbs = copy_reference(torch)
+    log(f"[bench] reference 1 GiB device copy: {copy_gbs:.0f} GB/s (read + write)")
     cfg = kvsynth.get_config(2)
     L = cfg.layers
     profile = kvsynth.zigzag_profile(cfg)
@@ -209,7 +280,7 @@ def main() -> int:
     if os.path.exists(COUNTERS):
         with open(COUNTERS) as f:
             cnt = json.load(f)
-        if cnt.get("source_sha256_16") == src_hash(DECODE_SRC):
+        if cnt.get("source_sha256_16") == src_hash(DECODE_SRCS):
             traffic = cnt.get("hbm_bytes_per_launch")
 
     result = {
@@ -234,10 +305,14 @@ def main() -> int:
         "select_and_compact_us_per_layer": round(us["select"] + us["compact"], 2),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel": "kvsel_decode_attn (decode_split_kernel)",
+                     "traffic": traffic,
+                     "kernel": "kvsel_decode_attn (decode_split_kernel + decode_combine_kernel)",
                      "algorithmic_bytes_per_launch": int(dec_bytes),
                      "avg_launch_us": round(us["decode"], 3)},
         "stages_us_per_layer": {k: round(v, 3) for k, v in us.items()},
+        "hbm_copy_reference_GBps": round(copy_gbs, 1),
+        "decode_frac_of_copy_reference": round(dec_gbs / copy_gbs, 4),
+        "compact_frac_of_copy_reference": round(gbs(cmp_bytes, us["compact"]) / copy_gbs, 4),
         "stages_roofline": {
             "score": {"bound": "hbm", "GB/s": round(gbs(sc_bytes, us["score"]), 1),
                       "frac": round(gbs(sc_bytes, us["score"]) / PEAK_HBM_GBS, 4),

@@ -61,9 +61,11 @@ typedef enum {
 typedef enum { KVSEL_FP32 = 0, KVSEL_BF16 = 1 } kvsel_dtype;
 
 /* Shape of one layer's attention.
- *   batch, hq, hkv : batch size, query heads, KV heads; hq % hkv == 0 and the
- *                    group size G = hq / hkv is at most 8; query head h reads
- *                    KV head h / G.
+ *   batch, hq, hkv : batch size, query heads, KV heads; hq % hkv == 0;
+ *                    query head h reads KV head h / G with group size
+ *                    G = hq / hkv.  kvsel_score needs G * w <= 256 and
+ *                    kvsel_decode_attn G <= 4 (EUNSUPPORTED otherwise);
+ *                    batch * hkv <= 2048 segments.
  *   head_dim       : 64, 88 or 128 (88 = RAP pair-pruned layout).
  *   n              : cached keys per (batch, KV head); for chunk scoring the
  *                    number of chunk keys.  1 <= n < 2^31.
