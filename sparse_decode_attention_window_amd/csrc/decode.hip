@@ -5,7 +5,8 @@
 // Work items are (segment, chunk of 64*tpw rows) pairs flattened over all
 // segments, so segments of very different lengths (FastGen local / special /
 // global heads) load the chip evenly; tpw (16-row tiles per wavefront) is
-// picked from the cache size so a launch holds about a thousand workgroups.
+// picked from the cache size so that all items fit in one round of resident
+// workgroups.
 // A workgroup of four wavefronts owns one item; each wavefront streams its
 // rows in 16-row tiles with the next tile's loads in flight while the current
 // one is computed:
@@ -16,12 +17,12 @@
 //   PV    on the vector ALUs in fp32: lane (slot g, chunk c) owns 16 bytes
 //         of value row 4t+g and accumulates heads x elements.
 // Each item keeps (running max, sum of exponentials, unnormalised output) in
-// the workspace; a second kernel (one wavefront per segment and query head)
-// merges a segment's items (the split-softmax identity) and normalises.  The
-// merge is a separate launch on purpose: handing partials between workgroups
-// inside one kernel needs device-scope fences, which on this multi-XCD part
-// write back and invalidate the L2 of the issuing XCD.  Softmax runs in the
-// log2 domain with the scale folded into one multiply.
+// the workspace; a second kernel (one workgroup per segment) merges a
+// segment's items (the split-softmax identity) and normalises.  Softmax runs
+// in the log2 domain with the scale folded into one multiply.
+#include <algorithm>
+#include <atomic>
+
 #include "kvsel_internal.h"
 
 namespace kvsel {
@@ -62,11 +63,20 @@ __device__ __forceinline__ f32x4 qk_step(const u32x4& a, const u32x4& b, f32x4 a
   return acc;
 }
 
-// rows per work item for a packed cache of r_cap rows (host and device agree)
-__host__ __device__ inline int tiles_per_wave(int64_t r_cap) {
-  int64_t t = (r_cap + (int64_t)kWaves * kTile * kTargetItems - 1) /
-              ((int64_t)kWaves * kTile * kTargetItems);
-  return (int)(t < 1 ? 1 : (t > kMaxTpw ? kMaxTpw : t));
+// 16-row tiles per wavefront.  Items of equal size finish together, so the
+// launch is sized to ONE round of resident workgroups (slots): a second round
+// would run a handful of stragglers on an otherwise idle chip.  A segment
+// wastes at most one partial item, hence the S reserved slots.
+int tiles_per_wave(int64_t r_cap, int S, int slots) {
+  const int64_t avail = std::max<int64_t>(slots - S, slots / 2);
+  const int64_t rows = (int64_t)kWaves * kTile * std::max<int64_t>(avail, 1);
+  const int64_t t = (r_cap + rows - 1) / rows;
+  return (int)std::min<int64_t>(std::max<int64_t>(t, 1), kMaxTpw);
+}
+
+// Workspace items for any tpw >= 1 (the bound the workspace is sized for).
+int64_t max_items(int64_t r_cap, int S) {
+  return (r_cap + kWaves * kTile - 1) / (kWaves * kTile) + S;
 }
 
 template <typename T, int D>
@@ -170,6 +180,96 @@ __device__ __forceinline__ void compute_tile(WaveState<T, D, HG>& st, const Tile
   }
   // the next tile's write must not pass this tile's reads
   __builtin_amdgcn_wave_barrier();
+}
+
+// Merge `cnt` items (first .. first + cnt) of one segment for its G query
+// heads with the split-softmax identity and write the normalised rows to o
+// ([G][D]).  Wavefront h reduces head h's (max, sum); thread t owns output
+// float pair t and sums the weighted partial outputs over all items with up to
+// kBatch loads in flight; the first batch is requested before the statistics
+// so its latency overlaps the reduction.  Called by a whole workgroup.
+template <int HG, int D>
+__device__ void merge_segment(const float2* __restrict__ part_ml, const float* __restrict__ part_o,
+                              int64_t first, int cnt, float* __restrict__ o, int G) {
+  constexpr int kChunk = 64;                      // items weighted per pass
+  constexpr int kBatch = 16;                      // item loads in flight per thread
+  constexpr int E = HG * D;                       // partial-output floats per item
+  constexpr int NP = E / 2;                       // float pairs per item
+  static_assert(D % 2 == 0 && NP <= kThreads && HG <= kWaves, "merge layout");
+  __shared__ float sw[kChunk + kBatch][HG];
+  __shared__ float s_ms[HG], s_inv[HG];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int pr = min(tid, NP - 1);                // this thread's float pair
+  const int h = (2 * pr) / D;
+  const float* po = part_o + first * E + 2 * pr;
+
+  // first batch of partial outputs in flight before the statistics
+  float2 v0[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    v0[u] = *reinterpret_cast<const float2*>(po + (int64_t)min(u, cnt - 1) * E);
+  }
+  float2 mine = make_float2(-INFINITY, 0.f);
+  if (wid < HG) {
+    if (lane < cnt) mine = part_ml[(first + lane) * HG + wid];
+    float M = mine.x, L = mine.y;
+    for (int it = lane + 64; it < cnt; it += 64) {
+      const float2 ml = part_ml[(first + it) * HG + wid];
+      const float mn = fmaxf(M, ml.x);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      L = L * __builtin_amdgcn_exp2f(M - ms) + ml.y * __builtin_amdgcn_exp2f(ml.x - ms);
+      M = mn;
+    }
+    float Mw = M;
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) Mw = fmaxf(Mw, __shfl_xor(Mw, x));
+    const float Ms = Mw == -INFINITY ? 0.f : Mw;
+    float Lw = L * __builtin_amdgcn_exp2f(M - Ms);
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) Lw += __shfl_xor(Lw, x);
+    if (lane == 0) {
+      s_ms[wid] = Ms;
+      s_inv[wid] = (Mw == -INFINITY || !(Lw > 0.f)) ? 0.f : 1.f / Lw;
+    }
+  }
+  __syncthreads();
+
+  float2 acc = make_float2(0.f, 0.f);
+  for (int c0 = 0; c0 < cnt; c0 += kChunk) {
+    const int nn = min(kChunk, cnt - c0);
+    if (wid < HG) {
+      const int it = c0 + lane;
+      const float mx = it >= cnt ? -INFINITY
+                                 : (c0 == 0 ? mine.x : part_ml[(first + it) * HG + wid].x);
+      sw[lane][wid] = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - s_ms[wid]) * s_inv[wid];
+      if (lane < kBatch) sw[kChunk + lane][wid] = 0.f;
+    }
+    __syncthreads();
+    for (int j0 = 0; j0 < nn; j0 += kBatch) {
+      float2 v[kBatch];
+      if (c0 == 0 && j0 == 0) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) v[u] = v0[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          v[u] = *reinterpret_cast<const float2*>(po + (int64_t)(c0 + min(j0 + u, nn - 1)) * E);
+        }
+      }
+      // weights past the chunk's last item are zero (rows nn .. kChunk + kBatch of sw)
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float wgt = sw[j0 + u][h];
+        acc.x += wgt * v[u].x;
+        acc.y += wgt * v[u].y;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid < NP && h < G) {
+    o[2 * tid] = acc.x;
+    o[2 * tid + 1] = acc.y;
+  }
 }
 
 #ifndef KVSEL_DECODE_MIN_BLOCKS
@@ -315,80 +415,53 @@ __global__ __launch_bounds__(kThreads, KVSEL_DECODE_MIN_BLOCKS) void decode_spli
     part_o[(item * HG + h) * D + d] = o;
     if (d == 0) part_ml[item * HG + h] = make_float2(M, L);
   }
-
 }
 
-int hg_for(int G) { return G <= 1 ? 1 : (G <= 2 ? 2 : 4); }
-
-int64_t items_for(int64_t r_cap, int S) {
-  const int64_t rows = (int64_t)kWaves * kTile * tiles_per_wave(r_cap);
-  return (r_cap + rows - 1) / rows + S;
-}
-
-// One wavefront per (segment, query head): merge that head's items.
-template <int HG>
-__global__ __launch_bounds__(64) void decode_combine_kernel(
+// Second launch, one workgroup per segment: merge the segment's items.  The
+// merge runs in its own kernel on purpose: a hand-off between workgroups of one
+// launch needs device-scope visibility of the partials across the XCDs' L2
+// caches, and both ways of getting it (write-through atomic stores, or L2
+// write-back and invalidate fences) measured far slower than this launch.
+template <int HG, int D>
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     const float2* __restrict__ part_ml, const float* __restrict__ part_o,
     const int64_t* __restrict__ seg_off, const int32_t* __restrict__ seg_len, int64_t r_cap,
-    int hq, int hkv, int G, int D, int S, int tpw, int64_t items_max, float* __restrict__ out) {
-  const int s = blockIdx.x / G, g = blockIdx.x % G;
-  const int b = s / hkv, kvh = s % hkv;
-  const int lane = threadIdx.x;
+    int hq, int hkv, int G, int S, int tpw, int64_t items_max, float* __restrict__ out) {
+  const int s = blockIdx.x, b = s / hkv, kvh = s % hkv;
   const uint32_t rpi = (uint32_t)((int64_t)kWaves * kTile * tpw);
   const SegLoc loc = wave_locate(seg_off, seg_len, S, r_cap, s, false,
                                  [=](uint32_t l) { return (l + rpi - 1) / rpi; });
   // overlapping segments (a violated precondition) can ask for more items than
-  // the workspace holds; those were never computed, so clip the range
+  // were launched; those were never computed, so clip the range
   const int64_t first = min(loc.first, items_max);
   const int cnt = (int)(min(loc.first + loc.units, items_max) - first);
-  float* o = out + ((int64_t)b * hq + (int64_t)kvh * G + g) * D;
-  constexpr int kX = 2;  // output elements per lane (head_dim <= 128)
+  float* o = out + ((int64_t)b * hq + (int64_t)kvh * G) * D;
+  if (cnt <= 0) {  // empty segment: zero output
+    for (int e = threadIdx.x; e < G * D; e += kThreads) o[e] = 0.f;
+    return;
+  }
+  merge_segment<HG, D>(part_ml, part_o, first, cnt, o, G);
+}
 
-  // per-lane running merge over items lane, lane + 64, ...; then across lanes
-  float M = -INFINITY, L = 0.f;
-  for (int it = lane; it < cnt; it += 64) {
-    const float2 ml = part_ml[(first + it) * HG + g];
-    const float mn = fmaxf(M, ml.x);
-    const float ms = mn == -INFINITY ? 0.f : mn;
-    L = L * __builtin_amdgcn_exp2f(M - ms) + ml.y * __builtin_amdgcn_exp2f(ml.x - ms);
-    M = mn;
-  }
-  float Mw = M;
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) Mw = fmaxf(Mw, __shfl_xor(Mw, x));
-  const float Ms = Mw == -INFINITY ? 0.f : Mw;
-  float Lw = L * __builtin_amdgcn_exp2f(M - Ms);
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) Lw += __shfl_xor(Lw, x);
-  const float inv = (Mw == -INFINITY || !(Lw > 0.f)) ? 0.f : 1.f / Lw;
+int hg_for(int G) { return G <= 1 ? 1 : (G <= 2 ? 2 : 4); }
 
-  float acc[kX] = {0.f, 0.f};
-  for (int c0 = 0; c0 < cnt; c0 += 64) {
-    const int nn = min(64, cnt - c0);
-    const float wl = lane < nn
-        ? __builtin_amdgcn_exp2f(part_ml[(first + c0 + lane) * HG + g].x - Ms) * inv : 0.f;
-    const float* po = part_o + ((first + c0) * HG + g) * D;
-    // batches of 8 items: 8 independent loads per element in flight
-    for (int j0 = 0; j0 < nn; j0 += 8) {
-      float v[8][kX], w[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = min(j0 + u, nn - 1);           // tail rereads the last item, weight 0
-        w[u] = __shfl(wl, j0 + u < nn ? j0 + u : 63);
-#pragma unroll
-        for (int x = 0; x < kX; ++x) v[u][x] = po[(int64_t)j * HG * D + min(lane + 64 * x, D - 1)];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int x = 0; x < kX; ++x) acc[x] += (j0 + u < nn ? w[u] : 0.f) * v[u][x];
-    }
+// Workgroups of `kernel` that one compute unit holds at once (cached per device).
+template <typename K>
+int resident_blocks(K kernel) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kernel),
+                                                     kThreads, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    v = nb;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-#pragma unroll
-  for (int x = 0; x < kX; ++x) {
-    const int d = lane + 64 * x;
-    if (d < D) o[d] = acc[x];
-  }
+  return v;
 }
 
 template <typename T, int D, int HG>
@@ -396,16 +469,18 @@ hipError_t run(int batch, int hq, int hkv, float scale, const void* q, const voi
                const void* v_c, const int64_t* seg_off, const int32_t* seg_len, int64_t r_cap,
                float* out, void* ws, hipStream_t stream) {
   const int S = batch * hkv, G = hq / hkv;
-  const int tpw = tiles_per_wave(r_cap);
-  const int64_t items = items_for(r_cap, S);
+  const int slots = device_info().cus * resident_blocks(decode_split_kernel<T, D, HG>);
+  const int tpw = tiles_per_wave(r_cap, S, slots);
+  const int64_t rpi = (int64_t)kWaves * kTile * tpw;
+  const int64_t items = (r_cap + rpi - 1) / rpi + S;   // launched; <= max_items
   auto* ml = static_cast<float2*>(ws);
-  auto* po = reinterpret_cast<float*>(ml + items * HG);
+  auto* po = reinterpret_cast<float*>(ml + max_items(r_cap, S) * HG);
   const float c = scale * kLog2e;
   decode_split_kernel<T, D, HG><<<dim3((unsigned)items), dim3(kThreads), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(k_c),
       static_cast<const char*>(v_c), seg_off, seg_len, r_cap, S, hq, hkv, G, c, tpw, ml, po);
-  decode_combine_kernel<HG><<<dim3(S * G), dim3(64), 0, stream>>>(
-      ml, po, seg_off, seg_len, r_cap, hq, hkv, G, D, S, tpw, items, out);
+  decode_combine_kernel<HG, D><<<dim3(S), dim3(kThreads), 0, stream>>>(
+      ml, po, seg_off, seg_len, r_cap, hq, hkv, G, S, tpw, items, out);
   return hipGetLastError();
 }
 
@@ -424,7 +499,7 @@ hipError_t run_d(int batch, int hq, int hkv, float scale, const void* q, const v
 
 size_t decode_workspace_bytes(int S, int head_dim, int G, int64_t r_cap) {
   const int HG = hg_for(G);
-  return (size_t)items_for(r_cap, S) * HG * (sizeof(float2) + sizeof(float) * head_dim);
+  return (size_t)max_items(r_cap, S) * HG * (sizeof(float2) + sizeof(float) * head_dim);
 }
 
 hipError_t launch_decode(int dtype, int head_dim, int batch, int hq, int hkv, float scale,
