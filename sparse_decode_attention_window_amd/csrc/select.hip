@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void select_rank_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Register-resident variant for N <= 1024 * KPT items: thread t holds items
+// Register-resident weighted (chunk) variant for N <= 1024 * KPT items: thread t holds items
 // j = k * 1024 + t (k < KPT) in registers, so the radix passes read no
 // memory; histograms use 11-bit digits (3 passes) over 8 padded replicas.
 // Emission orders items k-major, thread-minor (that is index order): per
@@ -210,17 +210,23 @@ constexpr int kRBins = 2048;
 constexpr int kRReps = 8;
 constexpr int kRPitch = kRBins + 1;
 
-// Exclusive scan of vals[0..M) in LDS (M <= 1024) by the whole block.
-__device__ void block_scan_lds(uint32_t* vals, int M, uint32_t* wave_tot) {
+// Exclusive scan of vals[0..M) in LDS (M <= 1024) by the whole block;
+// returns the total to every thread.
+__device__ uint32_t block_scan_lds(uint32_t* vals, int M, uint32_t* wave_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const uint32_t v = tid < M ? vals[tid] : 0u;
   const uint32_t inc = wave_incl_scan_u32(v);
   if (lane == 63) wave_tot[wid] = inc;
   __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < wid; ++w) before += wave_tot[w];
+  uint32_t before = 0, total = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t t = wave_tot[w];
+    before += w < wid ? t : 0u;
+    total += t;
+  }
   if (tid < M) vals[tid] = before + inc - v;
   __syncthreads();
+  return total;
 }
 
 template <bool WEIGHTED, int KPT>
@@ -353,12 +359,8 @@ __global__ __launch_bounds__(kThreads) void select_reg_kernel(
     if (lane == 0) blk_b[k * kWaves + wid] = ks;
   }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t t = 0;
-    for (int i = 0; i < KPT * kWaves; ++i) t += blk_b[i];
-    seg_len[s] = (int32_t)t;
-  }
-  block_scan_lds(blk_b, KPT * kWaves, wave_tot);
+  const uint32_t kept_total = block_scan_lds(blk_b, KPT * kWaves, wave_tot);
+  if (tid == 0) seg_len[s] = (int32_t)kept_total;
   // 3) write the kept token positions
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
@@ -375,6 +377,322 @@ __global__ __launch_bounds__(kThreads) void select_reg_kernel(
         idx[off + pos] = (int32_t)j;
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-B (unweighted) for N <= 1024 * KPT items, one workgroup per segment.
+// One workgroup is issue-bound (every instruction per item costs N / 256
+// lane-slots of the CU), so the design minimises per-item instructions:
+//   * thread t holds R runs of RL contiguous items, item (r, t, e) =
+//     r * 1024 * RL + t * RL + e: 16-byte loads, and index order is
+//     (run, thread, element), so a thread's kept items are placed with one
+//     popcount per run and a block scan of per-thread counts;
+//   * the threshold key T is found by 8-bit digits, MSB first; the first two
+//     histograms run over the registers with one private copy per lane (no
+//     LDS atomic conflicts, whatever the score distribution); the items that
+//     share T's top 16 bits (candidates) are then compacted to LDS in index
+//     order and the last two digits, and the rank of ties, use only them (if
+//     too many items share those bits, the same steps run over the registers);
+//   * every item > T is kept, and of the items == T the first `remaining` in
+//     index order: ascending output, lowest index first among equal scores.
+// ---------------------------------------------------------------------------
+constexpr int kCandMax = 8192;
+constexpr int kLaneReps = 64;               // one histogram copy per lane
+constexpr int kBPitch = 257;                // 256 digits + 1: copies in different banks
+
+// order-preserving key with integer ops only (no FP arithmetic, so no
+// denormal flushing): NaN -> 0, -0 -> +0
+__device__ __forceinline__ uint32_t score_key_int(float f) {
+  uint32_t b = __float_as_uint(f);
+  b = b == 0x80000000u ? 0u : b;
+  const uint32_t k = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+  return (b & 0x7fffffffu) > 0x7f800000u ? 0u : k;
+}
+
+__device__ __forceinline__ void clear_bhist(uint32_t* hist) {
+  for (int i = threadIdx.x; i < kLaneReps * kBPitch; i += kThreads) hist[i] = 0;
+}
+
+// Digit holding the `remaining`-th largest item, from the per-lane histograms
+// of 256 digits; whole block.  `remaining` drops by the count above the
+// digit; `count` is the digit's own count.  Thread t sums 16 lane copies of
+// digit 255 - t / 4 (so increasing t = decreasing digit).
+__device__ __forceinline__ uint32_t pick_byte(const uint32_t* hist, uint32_t& remaining,
+                                              uint32_t& count, uint32_t* wave_tot,
+                                              uint32_t* sel) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int d = 255 - (tid >> 2), q = tid & 3;
+  uint32_t part = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part += hist[(q * 16 + r) * kBPitch + d];
+  const uint32_t inc = wave_incl_scan_u32(part);
+  if (lane == 63) wave_tot[wid] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int w = 0; w < wid; ++w) before += wave_tot[w];
+  // digit total = sum over its 4 threads (lanes 4k .. 4k+3 of one wavefront)
+  uint32_t dsum = part + __shfl_xor(part, 1);
+  dsum += __shfl_xor(dsum, 2);
+  const uint32_t incl = before + inc;           // items in digits >= d, through this thread
+  if (q == 3) {
+    const uint32_t above = incl - dsum;         // items in digits > d
+    if (above < remaining && remaining <= incl) {
+      sel[0] = (uint32_t)d;
+      sel[1] = above;
+      sel[2] = dsum;
+    }
+  }
+  __syncthreads();
+  const uint32_t dd = sel[0];
+  remaining -= sel[1];
+  count = sel[2];
+  __syncthreads();  // sel and wave_tot are reused
+  return dd;
+}
+
+// Exclusive block scan of R per-thread counts (each <= 0xffff in total over
+// the block), two counts packed per 32-bit word.  excl[r] = sum over threads
+// t' < t of count[r]; tot[r] = block total of count[r].
+template <int R>
+__device__ __forceinline__ void block_scan_runs(const uint32_t (&cnt)[R], uint32_t (&excl)[R],
+                                                uint32_t (&tot)[R], uint32_t* wave_tot) {
+  constexpr int W = (R + 1) / 2;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t v[W], inc[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    v[i] = cnt[2 * i] | (2 * i + 1 < R ? cnt[2 * i + 1] << 16 : 0u);
+    inc[i] = wave_incl_scan_u32(v[i]);
+    if (lane == 63) wave_tot[i * kWaves + wid] = inc[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    uint32_t before = 0, all = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t t = wave_tot[i * kWaves + w];
+      before += w < wid ? t : 0u;
+      all += t;
+    }
+    const uint32_t ex = before + inc[i] - v[i];
+    excl[2 * i] = ex & 0xffffu;
+    tot[2 * i] = all & 0xffffu;
+    if (2 * i + 1 < R) {
+      excl[2 * i + 1] = ex >> 16;
+      tot[2 * i + 1] = all >> 16;
+    }
+  }
+  __syncthreads();  // wave_tot is reused
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kThreads) void select_topb_kernel(
+    const float* __restrict__ scores, int64_t N, const int32_t* __restrict__ budget,
+    const int64_t* __restrict__ seg_off, int32_t* __restrict__ seg_len,
+    int32_t* __restrict__ idx, int64_t r_cap) {
+  constexpr int RL = KPT < 8 ? KPT : 8;     // items per run
+  constexpr int R = KPT / RL;               // runs per thread
+  static_assert(R * RL == KPT && R <= 4, "run layout");
+  __shared__ uint32_t hist[kLaneReps * kBPitch];
+  __shared__ uint32_t cand[kCandMax];
+  __shared__ uint32_t wave_tot[2 * kWaves];
+  __shared__ uint32_t sel[3];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int s = blockIdx.x;
+  const int n = (int)N;  // <= 1024 * KPT
+  const float* sc = scores + (int64_t)s * N;
+  const int64_t off = seg_off[s];
+  const int64_t room = (off >= 0 && off <= r_cap) ? r_cap - off : 0;
+  int tgt = budget[s];
+  tgt = tgt < 0 ? 0 : (tgt > n ? n : tgt);
+  if (tid == 0) seg_len[s] = tgt;
+  if (tgt == 0 || tgt == n) {
+    for (int r = tid; r < tgt && r < room; r += kThreads) idx[off + r] = r;
+    return;
+  }
+  auto item = [&](int r, int e) { return r * kThreads * RL + tid * RL + e; };
+
+  // ---- keys (slots past n get key 0; they are never counted or kept) -------
+  uint32_t key[KPT];
+  const bool vec = RL >= 4 && (n & 3) == 0 && ((uintptr_t)sc & 15) == 0;  // 16-byte aligned rows
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int j0 = item(r, 0);
+    if (vec && j0 + RL <= n) {
+#pragma unroll
+      for (int e = 0; e < RL; e += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(sc + j0 + e);
+        key[r * RL + e + 0] = score_key_int(f.x);
+        key[r * RL + e + 1] = score_key_int(f.y);
+        key[r * RL + e + 2] = score_key_int(f.z);
+        key[r * RL + e + 3] = score_key_int(f.w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < RL; ++e) {
+        const int j = j0 + e;
+        const uint32_t k = score_key_int(sc[min(j, n - 1)]);
+        key[r * RL + e] = j < n ? k : 0u;
+      }
+    }
+  }
+  uint32_t valid = 0;  // bit r*RL+e: item exists
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int e = 0; e < RL; ++e) valid |= (uint32_t)(item(r, e) < n) << (r * RL + e);
+
+  uint32_t* my_hist = hist + lane * kBPitch;
+  uint32_t remaining = (uint32_t)tgt, cnt = 0;
+
+  // ---- digit 1 (bits 31..24) over all items ----------------------------------
+  clear_bhist(hist);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) atomicAdd(&my_hist[key[i] >> 24], 1u);
+  __syncthreads();
+  if (tid == 0) hist[0] -= (uint32_t)(KPT * kThreads - n);  // the padded slots (key 0)
+  __syncthreads();
+  const uint32_t d1 = pick_byte(hist, remaining, cnt, wave_tot, sel);
+
+  // ---- digit 2 (bits 23..16) over the items with digit 1 == d1 ---------------
+  clear_bhist(hist);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < KPT; ++i)
+    if (((valid >> i) & 1u) && (key[i] >> 24) == d1) atomicAdd(&my_hist[(key[i] >> 16) & 0xffu], 1u);
+  __syncthreads();
+  const uint32_t d2 = pick_byte(hist, remaining, cnt, wave_tot, sel);
+  const uint32_t p2 = (d1 << 8) | d2;
+
+  uint32_t T;
+  uint32_t cbits = 0;               // fast path: bit i = item i is a candidate
+  uint32_t cexcl[R], ctot[R];
+  uint32_t eexcl[R], etot[R];       // slow path: equal keys before, per run
+  const bool fast = cnt <= (uint32_t)kCandMax;  // block-uniform
+  if (fast) {
+    // ---- candidates (top 16 bits == p2) to LDS in index order ---------------
+    uint32_t cc[R];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      cbits |= (uint32_t)(((valid >> i) & 1u) && (key[i] >> 16) == p2) << i;
+#pragma unroll
+    for (int r = 0; r < R; ++r) cc[r] = __popc((cbits >> (r * RL)) & ((1u << RL) - 1u));
+    block_scan_runs<R>(cc, cexcl, ctot, wave_tot);
+    uint32_t base = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t pos = base + cexcl[r];
+#pragma unroll
+      for (int e = 0; e < RL; ++e)
+        if ((cbits >> (r * RL + e)) & 1u) cand[pos++] = key[r * RL + e];
+      base += ctot[r];
+    }
+    const int C = (int)cnt;
+    // ---- digits 3 and 4 over the candidates ----------------------------------
+    clear_bhist(hist);
+    __syncthreads();
+    for (int i = tid; i < C; i += kThreads) atomicAdd(&my_hist[(cand[i] >> 8) & 0xffu], 1u);
+    __syncthreads();
+    const uint32_t d3 = pick_byte(hist, remaining, cnt, wave_tot, sel);
+    const uint32_t p3 = (p2 << 8) | d3;
+    clear_bhist(hist);
+    __syncthreads();
+    for (int i = tid; i < C; i += kThreads)
+      if ((cand[i] >> 8) == p3) atomicAdd(&my_hist[cand[i] & 0xffu], 1u);
+    __syncthreads();
+    const uint32_t d4 = pick_byte(hist, remaining, cnt, wave_tot, sel);
+    T = (p3 << 8) | d4;
+    // ---- kept flag of each candidate: > T, or == T among the first
+    //      `remaining` equal ones (LDS order is index order) ---------------------
+    const int per = (C + kThreads - 1) / kThreads;   // contiguous slice per thread
+    const int c0 = min(tid * per, C), c1 = min(c0 + per, C);
+    uint32_t eq = 0;
+    for (int i = c0; i < c1; ++i) eq += cand[i] == T;
+    uint32_t eqa[1] = {eq}, eqx[1], eqt[1];
+    block_scan_runs<1>(eqa, eqx, eqt, wave_tot);
+    uint32_t before = eqx[0];
+    for (int i = c0; i < c1; ++i) {
+      const uint32_t kv = cand[i];
+      const bool e = kv == T;
+      cand[i] = (kv > T || (e && before < remaining)) ? 1u : 0u;
+      before += e;
+    }
+    __syncthreads();
+  } else {
+    // ---- too many candidates: digits 3 and 4 and the tie rank over registers
+    clear_bhist(hist);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (((valid >> i) & 1u) && (key[i] >> 16) == p2) atomicAdd(&my_hist[(key[i] >> 8) & 0xffu], 1u);
+    __syncthreads();
+    const uint32_t d3 = pick_byte(hist, remaining, cnt, wave_tot, sel);
+    const uint32_t p3 = (p2 << 8) | d3;
+    clear_bhist(hist);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (((valid >> i) & 1u) && (key[i] >> 8) == p3) atomicAdd(&my_hist[key[i] & 0xffu], 1u);
+    __syncthreads();
+    const uint32_t d4 = pick_byte(hist, remaining, cnt, wave_tot, sel);
+    T = (p3 << 8) | d4;
+    uint32_t ec[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      ec[r] = 0;
+#pragma unroll
+      for (int e = 0; e < RL; ++e) ec[r] += ((valid >> (r * RL + e)) & 1u) && key[r * RL + e] == T;
+    }
+    block_scan_runs<R>(ec, eexcl, etot, wave_tot);
+  }
+
+  // ---- kept bits, one scan of per-run counts, writes ---------------------------
+  uint32_t kbits = 0;
+  {
+    uint32_t cbase = 0, ebase = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t cpos = fast ? cbase + cexcl[r] : 0u;
+      uint32_t ebefore = fast ? 0u : ebase + eexcl[r];
+#pragma unroll
+      for (int e = 0; e < RL; ++e) {
+        const int i = r * RL + e;
+        const bool v = (valid >> i) & 1u;
+        bool keep = v && key[i] > T;
+        if (fast) {
+          if ((cbits >> i) & 1u) {
+            keep = cand[cpos] != 0u;
+            ++cpos;
+          }
+        } else if (v && key[i] == T) {
+          keep = ebefore < remaining;
+          ++ebefore;
+        }
+        kbits |= (uint32_t)keep << i;
+      }
+      if (fast) cbase += ctot[r];
+      else ebase += etot[r];
+    }
+  }
+  uint32_t kc[R], kx[R], kt[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) kc[r] = __popc((kbits >> (r * RL)) & ((1u << RL) - 1u));
+  block_scan_runs<R>(kc, kx, kt, wave_tot);
+  uint32_t obase = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int64_t pos = (int64_t)obase + kx[r];
+#pragma unroll
+    for (int e = 0; e < RL; ++e) {
+      if ((kbits >> (r * RL + e)) & 1u) {
+        if (pos < room) idx[off + pos] = item(r, e);
+        ++pos;
+      }
+    }
+    obase += kt[r];
   }
 }
 
@@ -446,6 +764,28 @@ hipError_t launch_reg_n(int S, int hkv, int64_t N, const float* scores, const in
 #undef KVSEL_REG
 }
 
+template <int KPT>
+hipError_t launch_topb(int S, int64_t N, const float* scores, const int32_t* budget,
+                       const int64_t* seg_off, int32_t* seg_len, int32_t* idx, int64_t r_cap,
+                       hipStream_t stream) {
+  select_topb_kernel<KPT><<<dim3(S), dim3(kThreads), 0, stream>>>(scores, N, budget, seg_off,
+                                                                  seg_len, idx, r_cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_topb_n(int S, int64_t N, const float* scores, const int32_t* budget,
+                         const int64_t* seg_off, int32_t* seg_len, int32_t* idx, int64_t r_cap,
+                         hipStream_t stream) {
+#define KVSEL_TOPB(K) return launch_topb<K>(S, N, scores, budget, seg_off, seg_len, idx, r_cap, stream)
+  if (N <= 1 * kThreads) KVSEL_TOPB(1);
+  if (N <= 2 * kThreads) KVSEL_TOPB(2);
+  if (N <= 4 * kThreads) KVSEL_TOPB(4);
+  if (N <= 8 * kThreads) KVSEL_TOPB(8);
+  if (N <= 16 * kThreads) KVSEL_TOPB(16);
+  KVSEL_TOPB(32);
+#undef KVSEL_TOPB
+}
+
 }  // namespace
 
 hipError_t launch_select_rank(int S, int hkv, int64_t n_items, const float* scores,
@@ -456,8 +796,8 @@ hipError_t launch_select_rank(int S, int hkv, int64_t n_items, const float* scor
   if (n_items <= 32 * kThreads)
     return weighted ? launch_reg_n<true>(S, hkv, n_items, scores, budget, chunk_end, keep_tokens,
                                          seg_off, seg_len, idx, r_cap, stream)
-                    : launch_reg_n<false>(S, hkv, n_items, scores, budget, chunk_end, keep_tokens,
-                                          seg_off, seg_len, idx, r_cap, stream);
+                    : launch_topb_n(S, n_items, scores, budget, seg_off, seg_len, idx, r_cap,
+                                    stream);
   // longer segments: keys cached in LDS when they fit, else re-read from global
   const size_t base = kHistWords * sizeof(uint32_t);
   const size_t per_item = weighted ? 8 : 4;
