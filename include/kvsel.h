@@ -70,8 +70,8 @@ typedef enum { KVSEL_FP32 = 0, KVSEL_BF16 = 1 } kvsel_dtype;
  *   n              : cached keys per (batch, KV head); for chunk scoring the
  *                    number of chunk keys.  1 <= n < 2^31.
  *   dtype          : kvsel_dtype of q / K / V.
- *   scale          : softmax scale applied to q . k (usually 1/sqrt(head dim
- *                    of the unpruned model)). */
+ *   scale          : softmax scale applied to q . k, positive and finite
+ *                    (usually 1/sqrt(head dim of the unpruned model)). */
 typedef struct {
   int32_t batch, hq, hkv, head_dim;
   int64_t n;

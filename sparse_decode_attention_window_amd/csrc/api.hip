@@ -49,7 +49,8 @@ kvsel_status check_shape(const kvsel_shape* s, int* S, int* G, int max_group) {
     return fail(KVSEL_EUNSUPPORTED, "dtype %d is not fp32 (0) or bf16 (1)", s->dtype);
   if (!head_dim_ok(s->head_dim))
     return fail(KVSEL_EUNSUPPORTED, "head_dim %d not built (64, 88, 128)", s->head_dim);
-  if (!isfinite(s->scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  if (!(s->scale > 0.f) || !isfinite(s->scale))
+    return fail(KVSEL_EINVAL, "scale must be positive and finite");
   const long long segs = (long long)s->batch * s->hkv;
   if (segs > kMaxSegments)
     return fail(KVSEL_EUNSUPPORTED, "batch * hkv = %lld exceeds %d", segs, kMaxSegments);

@@ -16,6 +16,8 @@
 // and serve as A or B operand unchanged (both operands share one per-lane
 // layout).  Causal masking (query row i at position q_pos0 + i) is only
 // evaluated on tiles that reach past q_pos0.
+#include <type_traits>
+
 #include "kvsel_internal.h"
 
 namespace kvsel {
@@ -153,35 +155,38 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(
 #pragma unroll
   for (int rb = 0; rb < RBN; ++rb) { Mr[rb] = -INFINITY; Lr[rb] = 0.f; }
 
-  for_each_key_block<T, D>(kseg, tile0, wid, n, lane, [&](const u32x4* kf, int64_t key0) {
-      const bool need_mask = key0 + 31 >= n || key0 + 31 > q_pos0;
+  // one 32-key block; MASKED only on blocks that reach past n or q_pos0
+  auto block = [&](const u32x4* kf, int64_t key0, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const int kb0 = (int)key0;   // keys < n < 2^31
 #pragma unroll
-      for (int rb = 0; rb < RBN; ++rb) {
-        f32x16 acc = {};
-        const char* qrow = sq + (rb * 32 + (lane & 31)) * Gm::PITCH + 16 * half;
+    for (int rb = 0; rb < RBN; ++rb) {
+      f32x16 acc = {};
+      const char* qrow = sq + (rb * 32 + (lane & 31)) * Gm::PITCH + 16 * half;
 #pragma unroll
-        for (int a = 0; a < Gm::NA; ++a)
-          acc = mma_step(kf[a], *reinterpret_cast<const u32x4*>(qrow + 32 * a), acc, T{});
-        // lane owns query row rb*32 + lane%32 and 16 keys key0 + acc_row(j)
-        float x[16];
-        const int lr = lim[rb * 32 + (lane & 31)];
-        const int kb0 = (int)key0;   // keys < n < 2^31
+      for (int a = 0; a < Gm::NA; ++a)
+        acc = mma_step(kf[a], *reinterpret_cast<const u32x4*>(qrow + 32 * a), acc, T{});
+      // lane owns query row rb*32 + lane%32 and 16 keys key0 + acc_row(j);
+      // c > 0, so the largest logit is c times the largest product
+      const int lr = MASKED ? lim[rb * 32 + (lane & 31)] : 0;
+      float tm = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          x[j] = acc[j] * c;
-          if (need_mask && kb0 + acc_row(j, lane) > lr) x[j] = -INFINITY;
-        }
-        float tm = x[0];
-#pragma unroll
-        for (int j = 1; j < 16; ++j) tm = fmaxf(tm, x[j]);
-        const float mn = fmaxf(Mr[rb], tm);
-        const float ms = mn == -INFINITY ? 0.f : mn;
-        float sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sum += __builtin_amdgcn_exp2f(x[j] - ms);
-        Lr[rb] = Lr[rb] * __builtin_amdgcn_exp2f(Mr[rb] - ms) + sum;
-        Mr[rb] = mn;
+      for (int j = 0; j < 16; ++j) {
+        if (MASKED && kb0 + acc_row(j, lane) > lr) acc[j] = -INFINITY;
+        tm = fmaxf(tm, acc[j]);
       }
+      const float mn = fmaxf(Mr[rb], tm * c);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j], c, -ms));
+      Lr[rb] = Lr[rb] * __builtin_amdgcn_exp2f(Mr[rb] - ms) + sum;
+      Mr[rb] = mn;
+    }
+  };
+  for_each_key_block<T, D>(kseg, tile0, wid, n, lane, [&](const u32x4* kf, int64_t key0) {
+    if (key0 + 31 >= n || key0 + 31 > q_pos0) block(kf, key0, std::true_type{});
+    else block(kf, key0, std::false_type{});
   });
   // merge the two half-waves (same row, other 16 keys) and write per-wave stats
 #pragma unroll
@@ -265,33 +270,37 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
 
   const char* kseg = k + (int64_t)s * n * Gm::RB;
   const int64_t tile0 = (int64_t)tile * kTileKeys;
-  for_each_key_block<T, D>(kseg, tile0, wid, n, lane, [&](const u32x4* kf, int64_t key0) {
-      const int64_t key = key0 + (lane & 31);
-      const bool need_mask = key0 + 31 >= n || key0 + 31 > q_pos0;
-      float ssum = 0.f;
+  auto block = [&](const u32x4* kf, int64_t key0, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const int64_t key = key0 + (lane & 31);
+    float ssum = 0.f;
 #pragma unroll
-      for (int rb = 0; rb < RBN; ++rb) {
-        f32x16 acc = {};
-        const char* qrow = sq + (rb * 32 + (lane & 31)) * Gm::PITCH + 16 * half;
+    for (int rb = 0; rb < RBN; ++rb) {
+      f32x16 acc = {};
+      const char* qrow = sq + (rb * 32 + (lane & 31)) * Gm::PITCH + 16 * half;
 #pragma unroll
-        for (int a = 0; a < Gm::NA; ++a)
-          acc = mma_step(*reinterpret_cast<const u32x4*>(qrow + 32 * a), kf[a], acc, T{});
-        // lane owns key `key` and the 16 query rows rb*32 + acc_row(j)
+      for (int a = 0; a < Gm::NA; ++a)
+        acc = mma_step(*reinterpret_cast<const u32x4*>(qrow + 32 * a), kf[a], acc, T{});
+      // lane owns key `key` and the 16 query rows rb*32 + acc_row(j)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int r0 = rb * 32 + g4 * 8 + half * 4;
-          const float4 kr = *reinterpret_cast<const float4*>(&krow[r0]);
-          const float kk[4] = {kr.x, kr.y, kr.z, kr.w};
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = rb * 32 + g4 * 8 + half * 4;
+        const float4 kr = *reinterpret_cast<const float4*>(&krow[r0]);
+        const float kk[4] = {kr.x, kr.y, kr.z, kr.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float p = __builtin_amdgcn_exp2f(acc[g4 * 4 + e] * c - kk[e]);
-            if (need_mask && (int)key > lim[r0 + e]) p = 0.f;
-            ssum += p;
-          }
+        for (int e = 0; e < 4; ++e) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g4 * 4 + e], c, -kk[e]));
+          if (MASKED && (int)key > lim[r0 + e]) p = 0.f;
+          ssum += p;
         }
       }
-      ssum += __shfl_xor(ssum, 32);
-      if (half == 0 && key < n) scores[(int64_t)s * n + key] = ssum;
+    }
+    ssum += __shfl_xor(ssum, 32);
+    if (half == 0 && key < n) scores[(int64_t)s * n + key] = ssum;
+  };
+  for_each_key_block<T, D>(kseg, tile0, wid, n, lane, [&](const u32x4* kf, int64_t key0) {
+    if (key0 + 31 >= n || key0 + 31 > q_pos0) block(kf, key0, std::true_type{});
+    else block(kf, key0, std::false_type{});
   });
 }
 

@@ -51,6 +51,8 @@ def call_score(sh, w=8, q_pos0=0, q=FAKE, k=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 
     (dict(batch=0), _lib.KVSEL_EINVAL), (dict(hq=3), _lib.KVSEL_EINVAL),
     (dict(n=0), _lib.KVSEL_EINVAL), (dict(head_dim=96), _lib.KVSEL_EUNSUPPORTED),
     (dict(dtype=7), _lib.KVSEL_EUNSUPPORTED), (dict(scale=float("inf")), _lib.KVSEL_EINVAL),
+    (dict(scale=0.0), _lib.KVSEL_EINVAL), (dict(scale=-0.125), _lib.KVSEL_EINVAL),
+    (dict(scale=float("nan")), _lib.KVSEL_EINVAL),
     (dict(batch=2049, hkv=1, hq=1), _lib.KVSEL_EUNSUPPORTED)])
 def test_score_rejects_bad_shape(kw, code):
     assert call_score(shape(**kw)) == code
