@@ -98,8 +98,11 @@ __device__ __forceinline__ void load_k(const char* __restrict__ kseg, int64_t ke
   }
 }
 
-// Stream this wavefront's 32-key blocks of the tile with the next block's K
-// fragments in flight while the current one is processed.
+// Stream this wavefront's 32-key blocks of the tile with the K fragments of
+// the next kDepth blocks in flight while the current one is processed (the
+// loop is fully unrolled, so the buffers stay in registers).
+constexpr int kDepth = 2;
+
 template <typename T, int D, typename F>
 __device__ __forceinline__ void for_each_key_block(const char* __restrict__ kseg, int64_t tile0,
                                                    int wid, int64_t n, int lane, F&& process) {
@@ -109,22 +112,21 @@ __device__ __forceinline__ void for_each_key_block(const char* __restrict__ kseg
   auto key0_of = [&](int i) { return tile0 + (int64_t)(wid * kBlocks + i) * 32; };
   auto row_of = [&](int64_t key0) { return min(key0 + (lane & 31), n - 1); };
   if (key0_of(0) >= n) return;
-  u32x4 ka[Gm::NA], kb[Gm::NA];
-  // sched_barrier keeps the scheduler from hoisting the prefetch above the
-  // loads of the block being processed (vmcnt waits are in issue order)
-  load_k<T, D>(kseg, row_of(key0_of(0)), half, ka);
+  u32x4 kf[kDepth + 1][Gm::NA];
+#pragma unroll
+  for (int i = 0; i < kDepth && i < kBlocks; ++i)
+    load_k<T, D>(kseg, row_of(min(key0_of(i), n - 1)), half, kf[i]);
+  // sched_barrier keeps the scheduler from hoisting later loads above the
+  // ones the current block waits for (vmcnt waits count in issue order)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < kBlocks; i += 2) {
-    const int64_t k0 = key0_of(i), k1 = key0_of(i + 1);
-    load_k<T, D>(kseg, row_of(min(k1, n - 1)), half, kb);
+  for (int i = 0; i < kBlocks; ++i) {
+    if (i + kDepth < kBlocks)
+      load_k<T, D>(kseg, row_of(min(key0_of(i + kDepth), n - 1)), half,
+                   kf[(i + kDepth) % (kDepth + 1)]);
     __builtin_amdgcn_sched_barrier(0);
-    process(ka, k0);
-    if (i + 1 >= kBlocks || k1 >= n) break;
-    if (i + 2 < kBlocks) load_k<T, D>(kseg, row_of(min(key0_of(i + 2), n - 1)), half, ka);
-    __builtin_amdgcn_sched_barrier(0);
-    process(kb, k1);
-    if (i + 2 >= kBlocks || key0_of(i + 2) >= n) break;
+    if (key0_of(i) >= n) break;
+    process(kf[i % (kDepth + 1)], key0_of(i));
   }
 }
 
