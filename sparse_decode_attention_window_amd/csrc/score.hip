@@ -101,7 +101,7 @@ __device__ __forceinline__ void load_k(const char* __restrict__ kseg, int64_t ke
 // Stream this wavefront's 32-key blocks of the tile with the K fragments of
 // the next kDepth blocks in flight while the current one is processed (the
 // loop is fully unrolled, so the buffers stay in registers).
-constexpr int kDepth = 2;
+constexpr int kDepth = 1;
 
 template <typename T, int D, typename F>
 __device__ __forceinline__ void for_each_key_block(const char* __restrict__ kseg, int64_t tile0,
