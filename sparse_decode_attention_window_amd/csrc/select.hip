@@ -451,6 +451,32 @@ __device__ __forceinline__ uint32_t pick_byte(const uint32_t* hist, uint32_t& re
   return dd;
 }
 
+// Same choice from ONE 256-bin histogram copy (used on the compacted
+// candidates, a few items per thread, where replication does not pay).
+__device__ __forceinline__ uint32_t pick_byte_small(const uint32_t* h, uint32_t& remaining,
+                                                    uint32_t& count, uint32_t* wave_tot,
+                                                    uint32_t* sel) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int d = 255 - tid;
+  const uint32_t v = tid < 256 ? h[d] : 0u;
+  const uint32_t inc = wave_incl_scan_u32(v);
+  if (lane == 63) wave_tot[wid] = inc;
+  __syncthreads();
+  uint32_t above = inc - v;
+  for (int w = 0; w < wid; ++w) above += wave_tot[w];
+  if (tid < 256 && above < remaining && remaining <= above + v) {
+    sel[0] = (uint32_t)d;
+    sel[1] = above;
+    sel[2] = v;
+  }
+  __syncthreads();
+  const uint32_t dd = sel[0];
+  remaining -= sel[1];
+  count = sel[2];
+  __syncthreads();
+  return dd;
+}
+
 // Exclusive block scan of R per-thread counts (each <= 0xffff in total over
 // the block), two counts packed per 32-bit word.  excl[r] = sum over threads
 // t' < t of count[r]; tot[r] = block total of count[r].
@@ -591,19 +617,19 @@ __global__ __launch_bounds__(kThreads) void select_topb_kernel(
       base += ctot[r];
     }
     const int C = (int)cnt;
-    // ---- digits 3 and 4 over the candidates ----------------------------------
-    clear_bhist(hist);
+    // ---- digits 3 and 4 over the candidates (one histogram copy) -------------
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < C; i += kThreads) atomicAdd(&my_hist[(cand[i] >> 8) & 0xffu], 1u);
+    for (int i = tid; i < C; i += kThreads) atomicAdd(&hist[(cand[i] >> 8) & 0xffu], 1u);
     __syncthreads();
-    const uint32_t d3 = pick_byte(hist, remaining, cnt, wave_tot, sel);
+    const uint32_t d3 = pick_byte_small(hist, remaining, cnt, wave_tot, sel);
     const uint32_t p3 = (p2 << 8) | d3;
-    clear_bhist(hist);
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
     for (int i = tid; i < C; i += kThreads)
-      if ((cand[i] >> 8) == p3) atomicAdd(&my_hist[cand[i] & 0xffu], 1u);
+      if ((cand[i] >> 8) == p3) atomicAdd(&hist[cand[i] & 0xffu], 1u);
     __syncthreads();
-    const uint32_t d4 = pick_byte(hist, remaining, cnt, wave_tot, sel);
+    const uint32_t d4 = pick_byte_small(hist, remaining, cnt, wave_tot, sel);
     T = (p3 << 8) | d4;
     // ---- kept flag of each candidate: > T, or == T among the first
     //      `remaining` equal ones (LDS order is index order) ---------------------
@@ -651,30 +677,41 @@ __global__ __launch_bounds__(kThreads) void select_topb_kernel(
 
   // ---- kept bits, one scan of per-run counts, writes ---------------------------
   uint32_t kbits = 0;
-  {
-    uint32_t cbase = 0, ebase = 0;
+  if (fast) {
+    // non-candidates are kept iff their top 16 bits exceed T's; candidates
+    // carry their decision in LDS, visited in index order (set bits only)
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) kbits |= (uint32_t)((key[i] >> 16) > p2) << i;
+    kbits &= valid & ~cbits;
+    uint32_t cbase = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      uint32_t cpos = fast ? cbase + cexcl[r] : 0u;
-      uint32_t ebefore = fast ? 0u : ebase + eexcl[r];
+      uint32_t m = (cbits >> (r * RL)) & ((1u << RL) - 1u);
+      uint32_t cpos = cbase + cexcl[r];
+      while (m) {
+        const int e = __builtin_ctz(m);
+        m &= m - 1u;
+        if (cand[cpos++] != 0u) kbits |= 1u << (r * RL + e);
+      }
+      cbase += ctot[r];
+    }
+  } else {
+    uint32_t ebase = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t ebefore = ebase + eexcl[r];
 #pragma unroll
       for (int e = 0; e < RL; ++e) {
         const int i = r * RL + e;
         const bool v = (valid >> i) & 1u;
         bool keep = v && key[i] > T;
-        if (fast) {
-          if ((cbits >> i) & 1u) {
-            keep = cand[cpos] != 0u;
-            ++cpos;
-          }
-        } else if (v && key[i] == T) {
+        if (v && key[i] == T) {
           keep = ebefore < remaining;
           ++ebefore;
         }
         kbits |= (uint32_t)keep << i;
       }
-      if (fast) cbase += ctot[r];
-      else ebase += etot[r];
+      ebase += etot[r];
     }
   }
   uint32_t kc[R], kx[R], kt[R];
@@ -685,12 +722,12 @@ __global__ __launch_bounds__(kThreads) void select_topb_kernel(
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     int64_t pos = (int64_t)obase + kx[r];
-#pragma unroll
-    for (int e = 0; e < RL; ++e) {
-      if ((kbits >> (r * RL + e)) & 1u) {
-        if (pos < room) idx[off + pos] = item(r, e);
-        ++pos;
-      }
+    uint32_t m = (kbits >> (r * RL)) & ((1u << RL) - 1u);
+    while (m) {
+      const int e = __builtin_ctz(m);
+      m &= m - 1u;
+      if (pos < room) idx[off + pos] = item(r, e);
+      ++pos;
     }
     obase += kt[r];
   }
