@@ -17,6 +17,8 @@ from .gen import (
     head_kinds,
     special_positions,
     chunk_ends,
+    step_token,
+    step_inputs,
     HEAD_GLOBAL,
     HEAD_LOCAL,
     HEAD_SPECIAL,
@@ -25,5 +27,5 @@ from .gen import (
 __all__ = [
     "CONFIGS", "Config", "get_config", "bf16_bits_to_f32", "f32_to_bf16_bits",
     "layer_inputs", "segment_inputs", "zigzag_profile", "head_kinds",
-    "special_positions", "chunk_ends", "HEAD_GLOBAL", "HEAD_LOCAL", "HEAD_SPECIAL",
+    "special_positions", "chunk_ends", "step_token", "step_inputs", "HEAD_GLOBAL", "HEAD_LOCAL", "HEAD_SPECIAL",
 ]

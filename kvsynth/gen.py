@@ -32,6 +32,7 @@ SEED_ROOT = 20261203
 # tensor ids in the seed tuple
 T_U, T_K, T_V, T_QWIN, T_QDEC, T_HH, T_PROFILE, T_HHFRAC, T_HEADKIND, T_SPECIAL, \
     T_PAIRS, T_CHUNKS, T_PROJ = range(13)
+T_STEP = 13   # decode step t draws tensor ids T_STEP + 3t (key), + 1 (value), + 2 (queries)
 
 HEAD_GLOBAL, HEAD_LOCAL, HEAD_SPECIAL = 0, 1, 2
 
@@ -201,6 +202,44 @@ def segment_queries(cfg: Config, layer: int, b: int, kvh: int):
         pairs = kept_pairs(cfg, layer, kvh)
         qd = prune_pairs(rope_rotate(qd, np.full(G, cfg.n)), pairs, dg // 2).astype(np.float32)
     return qwin, _store(cfg, qd)
+
+
+def step_token(cfg: Config, layer: int, b: int, kvh: int, t: int):
+    """Decode step t of one segment: the token at position n + t.
+
+    Returns (k [d], v [d], q [G][d]) in storage format: the new key and value
+    drawn like the cache's bulk keys and values (no planted structure), the G
+    query heads drawn like the decode query.  C3 rotates key and queries at
+    position n + t and keeps the segment's RoPE pairs.
+    """
+    G, dg = cfg.G, cfg.d_gen
+    u = head_direction(cfg, layer, kvh)
+    k = _rng(cfg, layer, b, kvh, T_STEP + 3 * t).standard_normal(dg, dtype=np.float32)
+    v = _rng(cfg, layer, b, kvh, T_STEP + 3 * t + 1).standard_normal(dg, dtype=np.float32)
+    q = _rng(cfg, layer, b, kvh, T_STEP + 3 * t + 2).standard_normal((G, dg), dtype=np.float32)
+    q += np.float32(2.0) * u
+    if cfg.d_rope:
+        pairs = kept_pairs(cfg, layer, kvh)
+        half = dg // 2
+        pos = cfg.n + t
+        k = prune_pairs(rope_rotate(k[None, :], np.array([pos])), pairs, half)[0]
+        q = prune_pairs(rope_rotate(q, np.full(G, pos)), pairs, half)
+        v = prune_pairs(v, pairs, half)
+    return (_store(cfg, k.astype(np.float32)), _store(cfg, v.astype(np.float32)),
+            _store(cfg, q.astype(np.float32)))
+
+
+def step_inputs(cfg: Config, layer: int, t: int) -> dict:
+    """Decode step t for a whole layer: k_new, v_new [b][hkv][d], q [b][hq][d]."""
+    B, Hkv, G, d = cfg.batch, cfg.hkv, cfg.G, cfg.d
+    sdt = np.uint16 if cfg.dtype == "bf16" else np.float32
+    kn = np.empty((B, Hkv, d), sdt)
+    vn = np.empty((B, Hkv, d), sdt)
+    q = np.empty((B, cfg.hq, d), sdt)
+    for b in range(B):
+        for kvh in range(Hkv):
+            kn[b, kvh], vn[b, kvh], q[b, kvh * G:(kvh + 1) * G] = step_token(cfg, layer, b, kvh, t)
+    return {"k_new": kn, "v_new": vn, "q": q, "pos": cfg.n + t}
 
 
 def segment_chunk_inputs(cfg: Config, K_seg: np.ndarray, qdec_seg: np.ndarray,

@@ -42,7 +42,7 @@ __all__ = [
     "to_f64", "softmax", "window_scores", "lmba_row", "layer_lmba",
     "zigzag_budgets", "score_order", "select_topb", "select_chunks",
     "select_policy", "compact", "decode_attention", "decode_partial",
-    "combine_partials", "HEAD_GLOBAL", "HEAD_LOCAL", "HEAD_SPECIAL",
+    "combine_partials", "append_token", "HEAD_GLOBAL", "HEAD_LOCAL", "HEAD_SPECIAL",
 ]
 
 HEAD_GLOBAL, HEAD_LOCAL, HEAD_SPECIAL = 0, 1, 2
@@ -295,3 +295,38 @@ def combine_partials(parts) -> np.ndarray:
     L = sum(np.exp(m - M) * l for m, l, _ in parts)
     O = sum(np.exp(m - M) * o for m, _, o in parts)
     return O / L
+
+
+# ---------------------------------------------------------------------------
+# decode-time cache maintenance  [FG: the per-head eviction rule holds for the
+# rest of generation]
+# ---------------------------------------------------------------------------
+
+def append_token(idx, Kc, Vc, pos: int, k_new, v_new, cap: int, limit: int):
+    """Add the token just produced (position `pos`, rows k_new / v_new) to one
+    segment whose rows are (idx, Kc, Vc), under the segment's rule:
+
+      limit < 0   the token is not added (a special-token head, ordinary token)
+      limit == 0  the segment grows up to `cap` rows (a global head)
+      limit > 0   at most min(limit, cap) rows (a local head's window)
+
+    Below that bound the row is appended at the end; at (or above) it, the row
+    holding the smallest position -- the oldest token -- is overwritten in
+    place (the first such row).  Returns new (idx, Kc, Vc) arrays.
+    """
+    idx = np.array(idx, np.int64)
+    Kc = np.array(Kc)
+    Vc = np.array(Vc)
+    if limit < 0:
+        return idx, Kc, Vc
+    bound = cap if limit == 0 else min(cap, limit)
+    if bound <= 0:
+        return idx, Kc, Vc
+    if idx.size < bound:
+        return (np.append(idx, pos), np.concatenate([Kc, np.asarray(k_new)[None]]),
+                np.concatenate([Vc, np.asarray(v_new)[None]]))
+    j = int(np.argmin(idx))          # first row with the smallest position
+    idx[j] = pos
+    Kc[j] = k_new
+    Vc[j] = v_new
+    return idx, Kc, Vc

@@ -343,3 +343,51 @@ def test_bf16_widening_exact():
     got = oracle.to_f64(words)
     assert got.tolist()[:5] == [1.0, -1.0, 3.140625, 0.0, -0.0]
     assert got[5] == 255 * 2.0 ** 120          # largest finite bf16, (2 - 2^-7) * 2^127
+
+
+# ---------------------------------------------------------------------------
+# decode-time maintenance (FastGen page: eviction rules hold during generation)
+# ---------------------------------------------------------------------------
+
+def _rows(n, d=4, base=0):
+    return (np.arange(n * d, dtype=np.float32).reshape(n, d) + base)
+
+
+@pytest.mark.parametrize("W,steps", [(1, 3), (5, 12), (8, 8)])
+def test_append_sliding_window_closed_form(W, steps):
+    n = 100
+    idx = np.arange(n - W, n)
+    K, V = _rows(W), _rows(W, base=1000)
+    for t in range(steps):
+        idx, K, V = oracle.append_token(idx, K, V, n + t, np.full(4, -t, np.float32),
+                                        np.full(4, t, np.float32), cap=W + 50, limit=W)
+        # the window holds exactly the W most recent positions
+        assert sorted(idx.tolist()) == list(range(n - W + t + 1, n + t + 1))
+        # token n + t' sits in slot t' mod W (slots recycle oldest first)
+        assert idx[t % W] == n + t
+        assert K[t % W][0] == -t and V[t % W][0] == t
+
+
+def test_append_grows_to_capacity_then_replaces_oldest():
+    idx, K, V = np.array([5, 9]), _rows(2), _rows(2, base=100)
+    idx, K, V = oracle.append_token(idx, K, V, 20, np.ones(4), np.ones(4), cap=3, limit=0)
+    assert idx.tolist() == [5, 9, 20] and K.shape == (3, 4)
+    idx, K, V = oracle.append_token(idx, K, V, 21, np.full(4, 2.0), np.full(4, 3.0), cap=3, limit=0)
+    assert idx.tolist() == [21, 9, 20]            # position 5 was the oldest
+    assert K[0].tolist() == [2.0] * 4 and V[0].tolist() == [3.0] * 4
+
+
+def test_append_skip_and_bounds():
+    idx, K, V = np.array([3, 1, 2]), _rows(3), _rows(3)
+    a = oracle.append_token(idx, K, V, 7, np.zeros(4), np.zeros(4), cap=10, limit=-1)
+    assert a[0].tolist() == [3, 1, 2] and np.array_equal(a[1], K)
+    # the window bound is capped by the capacity
+    b = oracle.append_token(idx, K, V, 7, np.zeros(4), np.zeros(4), cap=3, limit=9)
+    assert b[0].tolist() == [3, 7, 2]
+    # a segment already above its bound keeps its length; the oldest row goes
+    c = oracle.append_token(idx, K, V, 7, np.zeros(4), np.zeros(4), cap=10, limit=2)
+    assert c[0].tolist() == [3, 7, 2]
+    # zero capacity: nothing changes
+    d = oracle.append_token(np.array([], np.int64), np.zeros((0, 4)), np.zeros((0, 4)), 7,
+                            np.zeros(4), np.zeros(4), cap=0, limit=0)
+    assert d[0].size == 0
