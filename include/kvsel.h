@@ -10,6 +10,7 @@
  *   kvsel_select       keep tokens per segment (top-B, chunk top-k or head policy)
  *   kvsel_compact      gather kept K/V rows into a packed variable-length cache
  *   kvsel_decode_attn  single-token GQA decode attention over that cache
+ *   kvsel_append       add each decoded token under the head's eviction rule
  *   kvsel_zigzag_budgets  (host) bounded per-layer budgets
  *
  * Sources, cited by page title and the equation / section on it:
@@ -162,6 +163,31 @@ kvsel_status kvsel_decode_attn(const kvsel_shape* s /*host*/, const void* q, con
                                const void* v_c, const int64_t* seg_off, const int32_t* seg_len,
                                int64_t r_cap, float* out, void* ws, size_t ws_bytes,
                                hipStream_t stream);
+
+/* --------------------------------------------------------------- append --
+ * Decode-time maintenance of the packed cache (FastGen page, core claim and
+ * method: the per-head eviction rule keeps holding during generation --
+ * local heads a sliding window, special-token heads only special tokens,
+ * global heads everything).  The token just produced, at position `pos`,
+ * joins segment s according to limit[s]:
+ *   limit[s] <  0  not added (e.g. a special-token head, ordinary token);
+ *   limit[s] == 0  the segment grows up to seg_cap[s] rows;
+ *   limit[s] >  0  the segment keeps at most min(limit[s], seg_cap[s]) rows.
+ * Below its bound the row goes to slot seg_len[s] and seg_len[s] grows by
+ * one; at (or above) the bound the row holding the smallest position in
+ * idx -- the oldest token, lowest slot on ties -- is overwritten in place.
+ * Rows of a segment are then no longer in position order; decode does not
+ * depend on their order.
+ *   k_new, v_new [batch][hkv][head_dim]  the token's key and value rows
+ *   seg_cap      [batch*hkv] int64: rows reserved from seg_off[s] on
+ *   limit        [batch*hkv] int32, or NULL (every segment grows)
+ *   seg_len, idx, k_c, v_c  updated in place; rows at or beyond r_cap are
+ *                never written.
+ * Errors: EINVAL for NULL pointers, pos or r_cap outside [0, 2^31). */
+kvsel_status kvsel_append(const kvsel_shape* s /*host*/, const void* k_new, const void* v_new,
+                          int64_t pos, const int64_t* seg_off, const int64_t* seg_cap,
+                          const int32_t* limit, int32_t* seg_len, int32_t* idx, void* k_c,
+                          void* v_c, int64_t r_cap, hipStream_t stream);
 
 /* --------------------------------------------------------------- budgets --
  * ZigZagkv page, Eq. 4 and Eq. 6 (host only, no GPU work):

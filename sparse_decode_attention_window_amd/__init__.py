@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     KvselError,
     Shape,
     SelectParams,
+    kvsel_append,
     kvsel_compact,
     kvsel_decode_attn,
     kvsel_decode_workspace,

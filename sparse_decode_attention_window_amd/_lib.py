@@ -61,6 +61,11 @@ _SIGS = {
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]),
+    "kvsel_append": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_void_p]),
     "kvsel_zigzag_budgets": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.c_int32,
                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.POINTER(ctypes.c_int32)]),
@@ -150,6 +155,13 @@ def kvsel_decode_attn(shape: Shape, q, k_c, v_c, seg_off, seg_len, r_cap: int, o
     _check(lib().kvsel_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k_c), _ptr(v_c),
                                    _ptr(seg_off), _ptr(seg_len), int(r_cap), _ptr(out), _ptr(ws),
                                    nbytes, _stream(stream)), "kvsel_decode_attn")
+
+
+def kvsel_append(shape: Shape, k_new, v_new, pos: int, seg_off, seg_cap, limit, seg_len, idx,
+                 k_c, v_c, r_cap: int, stream=None) -> None:
+    _check(lib().kvsel_append(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), int(pos),
+                              _ptr(seg_off), _ptr(seg_cap), _ptr(limit), _ptr(seg_len), _ptr(idx),
+                              _ptr(k_c), _ptr(v_c), int(r_cap), _stream(stream)), "kvsel_append")
 
 
 def kvsel_zigzag_budgets(profile, n: int, avg_budget: int, floor_budget: int):

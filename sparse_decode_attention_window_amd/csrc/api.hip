@@ -184,6 +184,25 @@ kvsel_status kvsel_compact(const kvsel_shape* s, const void* k, const void* v,
                     "kvsel_compact launch");
 }
 
+kvsel_status kvsel_append(const kvsel_shape* s, const void* k_new, const void* v_new, int64_t pos,
+                          const int64_t* seg_off, const int64_t* seg_cap, const int32_t* limit,
+                          int32_t* seg_len, int32_t* idx, void* k_c, void* v_c, int64_t r_cap,
+                          hipStream_t stream) {
+  g_err[0] = 0;
+  int S = 0, G = 0;
+  kvsel_status st = check_shape(s, &S, &G, 256);
+  if (st != KVSEL_OK) return st;
+  if (!k_new || !v_new || !seg_off || !seg_cap || !seg_len || !idx)
+    return fail(KVSEL_EINVAL, "k_new, v_new, seg_off, seg_cap, seg_len, idx must be non-NULL");
+  if (r_cap > 0 && (!k_c || !v_c)) return fail(KVSEL_EINVAL, "k_c and v_c must be non-NULL");
+  if (r_cap < 0 || r_cap > 0x7fffffffLL) return fail(KVSEL_EINVAL, "r_cap must be in [0, 2^31)");
+  if (pos < 0 || pos > 0x7fffffffLL) return fail(KVSEL_EINVAL, "pos must be in [0, 2^31)");
+  if (r_cap == 0) return KVSEL_OK;
+  return hip_status(launch_append(s->dtype, s->head_dim, S, k_new, v_new, (int32_t)pos, seg_off,
+                                  seg_cap, limit, seg_len, idx, k_c, v_c, r_cap, stream),
+                    "kvsel_append launch");
+}
+
 size_t kvsel_decode_workspace(const kvsel_shape* s, int64_t r_cap) {
   if (!s || s->batch < 1 || s->hkv < 1 || s->hq < s->hkv || r_cap < 0) return 0;
   return decode_workspace_bytes(s->batch * s->hkv, s->head_dim, s->hq / s->hkv, r_cap);

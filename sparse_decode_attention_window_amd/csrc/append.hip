@@ -1,0 +1,95 @@
+// Decode-time maintenance of the packed cache: the token just produced joins
+// every segment whose head rule admits it (FastGen page: the per-head eviction
+// rule keeps holding during generation -- local heads a sliding window,
+// special-token heads only special tokens, global heads everything).
+//
+// One workgroup per segment.  Below the segment's bound the row goes to the
+// next free slot; at the bound the slot holding the smallest position (the
+// oldest token) is found by a block-wide argmin over the segment's indices
+// and overwritten in place, so a sliding window costs one row write and one
+// read of the segment's indices per step, never a shift of the cache.
+#include "kvsel_internal.h"
+
+namespace kvsel {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+// (position, slot) packed so that the smaller position wins, then the lower slot
+__device__ __forceinline__ uint64_t pack(int32_t pos, int32_t slot) {
+  return ((uint64_t)(uint32_t)(pos ^ INT32_MIN) << 32) | (uint32_t)slot;
+}
+
+__global__ __launch_bounds__(kThreads) void append_kernel(
+    const char* __restrict__ k_new, const char* __restrict__ v_new, int32_t pos, int row_bytes,
+    const int64_t* __restrict__ seg_off, const int64_t* __restrict__ seg_cap,
+    const int32_t* __restrict__ limit, int32_t* __restrict__ seg_len,
+    int32_t* __restrict__ idx, char* __restrict__ k_c, char* __restrict__ v_c, int64_t r_cap) {
+  __shared__ uint64_t wmin[kWaves];
+  const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int32_t lim = limit ? limit[s] : 0;
+  if (lim < 0) return;  // the head's rule does not admit this token
+  int64_t off = seg_off[s];
+  if (off < 0 || off > r_cap) return;
+  const int64_t room = r_cap - off;
+  int64_t bound = seg_cap[s];
+  bound = bound < room ? bound : room;
+  if (lim > 0 && lim < bound) bound = lim;
+  if (bound <= 0) return;
+  int64_t len = seg_len[s];
+  len = len < 0 ? 0 : (len > room ? room : len);
+
+  int64_t slot;
+  if (len < bound) {
+    slot = len;
+  } else {
+    // oldest token: smallest position among the segment's rows
+    uint64_t best = ~0ull;
+    for (int64_t r = tid; r < len; r += kThreads) {
+      const uint64_t c = pack(idx[off + r], (int32_t)r);
+      best = c < best ? c : best;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t other = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), o) << 32) |
+                             (uint32_t)__shfl_xor((int)(uint32_t)best, o);
+      best = other < best ? other : best;
+    }
+    if (lane == 0) wmin[wid] = best;
+    __syncthreads();  // uniform: every thread of the block took this branch
+    best = wmin[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) best = wmin[w] < best ? wmin[w] : best;
+    slot = (int64_t)(uint32_t)best;
+  }
+  // all reads of idx are done before the slot is overwritten
+  __syncthreads();
+  const int64_t row = off + slot;
+  const char* ks = k_new + (int64_t)s * row_bytes;
+  const char* vs = v_new + (int64_t)s * row_bytes;
+  for (int c = tid; c < row_bytes / 16; c += kThreads) {
+    store16(k_c + row * row_bytes + 16 * c, load16(ks + 16 * c));
+    store16(v_c + row * row_bytes + 16 * c, load16(vs + 16 * c));
+  }
+  if (tid == 0) {
+    idx[row] = pos;
+    if (len < bound) seg_len[s] = (int32_t)(len + 1);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(int dtype, int head_dim, int S, const void* k_new,
+                         const void* v_new, int32_t pos, const int64_t* seg_off,
+                         const int64_t* seg_cap, const int32_t* limit, int32_t* seg_len,
+                         int32_t* idx, void* k_c, void* v_c, int64_t r_cap,
+                         hipStream_t stream) {
+  const int row_bytes = head_dim * (dtype == 1 ? 2 : 4);
+  append_kernel<<<dim3(S), dim3(kThreads), 0, stream>>>(
+      static_cast<const char*>(k_new), static_cast<const char*>(v_new), pos, row_bytes, seg_off, seg_cap, limit, seg_len, idx, static_cast<char*>(k_c), static_cast<char*>(v_c),
+      r_cap);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

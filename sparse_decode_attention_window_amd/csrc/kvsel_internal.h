@@ -246,6 +246,11 @@ hipError_t launch_decode(int dtype, int head_dim, int batch, int hq, int hkv, fl
                          const int64_t* seg_off, const int32_t* seg_len, int64_t r_cap,
                          float* out, void* ws, hipStream_t stream);
 
+hipError_t launch_append(int dtype, int head_dim, int S, const void* k_new, const void* v_new,
+                         int32_t pos, const int64_t* seg_off, const int64_t* seg_cap,
+                         const int32_t* limit, int32_t* seg_len, int32_t* idx, void* k_c,
+                         void* v_c, int64_t r_cap, hipStream_t stream);
+
 size_t score_workspace_bytes(int S, int64_t n, int rows);
 hipError_t launch_score(int dtype, int head_dim, int batch, int hq, int hkv, int w,
                         int64_t n, int64_t q_pos0, float scale, const void* q_win,

@@ -60,6 +60,7 @@ class LayerRun:
     mode: int
     r_cap: int
     seg_off: object
+    seg_cap: object = None                 # rows reserved per segment (int64)
     w: int = 0
     q_pos0: int = 0
     q_win: object = None
@@ -114,6 +115,11 @@ class LayerRun:
         K.kvsel_decode_attn(self.shape, self.q_dec, self.k_c, self.v_c, self.seg_off,
                             self.seg_len, self.r_cap, self.out, self.ws_dec, stream)
 
+    def append(self, k_new, v_new, pos: int, limit=None, stream=None):
+        """Add one decoded token to every segment under its head rule (limit)."""
+        K.kvsel_append(self.shape, k_new, v_new, pos, self.seg_off, self.seg_cap, limit,
+                       self.seg_len, self.idx, self.k_c, self.v_c, self.r_cap, stream)
+
     def run(self, stream=None):
         self.score(stream)
         self.select(stream)
@@ -122,8 +128,9 @@ class LayerRun:
         return self
 
 
-def build_layer(cfg, inputs: dict, *, budget=None, device="cuda") -> LayerRun:
-    """LayerRun for one synthetic layer (cfg: a kvsynth Config, inputs: layer_inputs())."""
+def build_layer(cfg, inputs: dict, *, budget=None, slack: int = 0, device="cuda") -> LayerRun:
+    """LayerRun for one synthetic layer (cfg: a kvsynth Config, inputs: layer_inputs()).
+    `slack` extra rows per segment leave room for tokens appended while decoding."""
     import torch
     B, hq, hkv, d, n = cfg.batch, cfg.hq, cfg.hkv, cfg.d, cfg.n
     shape = K.make_shape(B, hq, hkv, d, n, cfg.dtype, cfg.scale)
@@ -165,8 +172,10 @@ def build_layer(cfg, inputs: dict, *, budget=None, device="cuda") -> LayerRun:
         params = K.select_params(mode, head_kind=kt, local_window=cfg.local_window,
                                  special_pos=st, n_special=sp.shape[1])
         run = LayerRun(shape, k, v, qd, mode, 0, None, params=params)
+    cap = cap + int(slack)
     off, r_cap = offsets(cap)
     run.seg_off = device_tensor(off, device)
+    run.seg_cap = device_tensor(cap.astype(np.int64), device)
     run.r_cap = r_cap
     run.keep = keep
     return run.allocate()

@@ -106,6 +106,24 @@ def test_compact_and_decode_reject_bad_args():
                                  FAKE, 1 << 30, None) == _lib.KVSEL_EUNSUPPORTED
 
 
+def test_append_rejects_bad_args():
+    sh = shape()
+    lib = kvsel.lib()
+
+    def app(k_new=FAKE, seg_cap=FAKE, pos=600, r_cap=16, k_c=FAKE):
+        return lib.kvsel_append(ctypes.byref(sh), k_new, FAKE, pos, FAKE, seg_cap, None, FAKE,
+                                FAKE, k_c, FAKE, r_cap, None)
+    assert app(k_new=None) == _lib.KVSEL_EINVAL
+    assert app(seg_cap=None) == _lib.KVSEL_EINVAL
+    assert app(k_c=None) == _lib.KVSEL_EINVAL
+    assert app(pos=-1) == _lib.KVSEL_EINVAL
+    assert app(pos=1 << 31) == _lib.KVSEL_EINVAL
+    assert app(r_cap=-1) == _lib.KVSEL_EINVAL
+    assert app(r_cap=0) == _lib.KVSEL_OK          # an empty cache: nothing to do, nothing launched
+    assert lib.kvsel_append(ctypes.byref(shape(head_dim=96)), FAKE, FAKE, 1, FAKE, FAKE, None,
+                            FAKE, FAKE, FAKE, FAKE, 16, None) == _lib.KVSEL_EUNSUPPORTED
+
+
 # ---------------------------------------------------------------------------
 # host budget helper vs the oracle (ZigZagkv page, Eq. 4 + Eq. 6): exact
 # ---------------------------------------------------------------------------

@@ -405,3 +405,124 @@ def test_graph_replays_match_eager(kv, cid):
         for s, (o, n_) in enumerate(zip(want["seg_off"], want["seg_len"])):
             for key in ("idx", "k_c", "v_c"):
                 assert np.array_equal(got[key][o:o + n_], want[key][o:o + n_]), (rep, key, s)
+
+
+# ---------------------------------------------------------------------------
+# decode-time maintenance: append / sliding window (FastGen eviction rules)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d", [("fp32", 64), ("bf16", 88), ("bf16", 128)])
+def test_append_steps_match_oracle(kv, dtype, d):
+    """Six appends in a row on ragged segments with every kind of rule:
+    skip, grow, grow into capacity, sliding windows (also already over the
+    window); state compared bit for bit with the oracle after every step."""
+    kvsel, pipeline, torch = kv
+    rng = np.random.default_rng(7 + d)
+    B, hkv, n = 3, 3, 500
+    S = B * hkv
+    _say("append", dtype, d)
+    sdt = np.uint16 if dtype == "bf16" else np.float32
+
+    def rows(k):
+        x = rng.standard_normal((k, d)).astype(np.float32)
+        return kvsynth.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+    caps = np.array([0, 5, 9, 4, 12, 6, 3, 7, 10], np.int64)
+    limits = np.array([0, 0, 3, -1, 4, 0, 1, 2, 5], np.int32)
+    lens = np.array([0, 2, 3, 2, 6, 6, 0, 5, 1], np.int64)       # seg 4, 7: above the window
+    gaps = np.array([1, 0, 2, 0, 3, 1, 0, 2, 1], np.int64)         # unused rows between segments
+    off = np.zeros(S, np.int64)
+    for s in range(1, S):
+        off[s] = off[s - 1] + caps[s - 1] + gaps[s - 1]
+    r_cap = int(off[-1] + caps[-1] + gaps[-1])
+    idx_h = np.full(r_cap, -7, np.int32)
+    kc_h = rows(r_cap)
+    vc_h = rows(r_cap)
+    segs = []
+    for s in range(S):
+        pos = rng.choice(n, size=lens[s], replace=False).astype(np.int64)
+        idx_h[off[s]:off[s] + lens[s]] = pos
+        segs.append([pos, kc_h[off[s]:off[s] + lens[s]].copy(), vc_h[off[s]:off[s] + lens[s]].copy()])
+    shape = kvsel.make_shape(B, B * hkv, hkv, d, n, dtype, 0.125)
+    dev = lambda a: pipeline.device_tensor(a)
+    t_off, t_cap, t_lim = dev(off), dev(caps), dev(limits)
+    t_len, t_idx = dev(lens.astype(np.int32)), dev(idx_h)
+    t_kc, t_vc = dev(kc_h), dev(vc_h)
+    for t in range(6):
+        kn, vn = rows(S), rows(S)
+        pos = n + t
+        kvsel.kvsel_append(shape, dev(kn.reshape(B, hkv, d)), dev(vn.reshape(B, hkv, d)), pos,
+                           t_off, t_cap, t_lim, t_len, t_idx, t_kc, t_vc, r_cap)
+        torch.cuda.synchronize()
+        g_len, g_idx = pu.to_host(t_len), pu.to_host(t_idx)
+        g_kc, g_vc = pu.to_host(t_kc), pu.to_host(t_vc)
+        for s in range(S):
+            segs[s] = list(oracle.append_token(segs[s][0], segs[s][1], segs[s][2], pos, kn[s], vn[s],
+                                               int(caps[s]), int(limits[s])))
+            want_idx, want_k, want_v = segs[s]
+            ln = int(g_len[s])
+            what = f"append step {t} seg {s}"
+            assert ln == want_idx.size, f"{what}: len {ln} != {want_idx.size}"
+            o = int(off[s])
+            assert np.array_equal(g_idx[o:o + ln], want_idx.astype(np.int32)), what
+            assert np.array_equal(g_kc[o:o + ln], want_k), what
+            assert np.array_equal(g_vc[o:o + ln], want_v), what
+        # rows outside every segment's current rows are untouched
+        used = np.zeros(r_cap, bool)
+        for s in range(S):
+            used[off[s]:off[s] + int(g_len[s])] = True
+        assert np.all(g_idx[~used] == -7), f"append step {t}: rows outside segments written"
+
+
+def test_c3_decode_loop_with_append(kv):
+    """FastGen serving loop on a reduced C3 layer: policy select, compact, then
+    three decode steps; before each step the new token joins the cache under
+    its head rule (local: sliding window, special: not added, global: grows),
+    and the step's decode output is checked against the oracle."""
+    kvsel, pipeline, torch = kv
+    steps = 3
+    cfg = kvsynth.get_config(3, batch=2, n=3000 + 5)
+    _say(cfg.name, "decode loop with append, n", cfg.n)
+    inputs = kvsynth.layer_inputs(cfg, 0)
+    run = pipeline.build_layer(cfg, inputs, slack=steps)
+    run.select()
+    run.compact()
+    torch.cuda.synchronize()
+    h = _host(run)
+    kinds = np.asarray(inputs["head_kind"])
+    rule = {kvsynth.HEAD_LOCAL: cfg.local_window, kvsynth.HEAD_SPECIAL: -1,
+            kvsynth.HEAD_GLOBAL: 0}
+    S = cfg.batch * cfg.hkv
+    limits = np.array([rule[int(kinds[s % cfg.hkv])] for s in range(S)], np.int32)
+    caps = pu.to_host(run.seg_cap)
+    t_lim = pipeline.device_tensor(limits)
+    segs = []
+    for s in range(S):
+        b, kvh = divmod(s, cfg.hkv)
+        o, ln = int(h["seg_off"][s]), int(h["seg_len"][s])
+        idx = h["idx"][o:o + ln].astype(np.int64)
+        Kc, Vc = oracle.compact(inputs["K"][b, kvh], inputs["V"][b, kvh], idx)
+        segs.append([idx, Kc, Vc])
+    worst = 0.0
+    for t in range(steps):
+        st = kvsynth.step_inputs(cfg, 0, t)
+        run.append(pipeline.device_tensor(st["k_new"]), pipeline.device_tensor(st["v_new"]),
+                   st["pos"], t_lim)
+        q = pipeline.device_tensor(st["q"])
+        kvsel.kvsel_decode_attn(run.shape, q, run.k_c, run.v_c, run.seg_off, run.seg_len,
+                                run.r_cap, run.out, run.ws_dec)
+        torch.cuda.synchronize()
+        out = pu.to_host(run.out)
+        for s in range(S):
+            b, kvh = divmod(s, cfg.hkv)
+            segs[s] = list(oracle.append_token(segs[s][0], segs[s][1], segs[s][2], st["pos"],
+                                               st["k_new"][b, kvh], st["v_new"][b, kvh],
+                                               int(caps[s]), int(limits[s])))
+            Kc, Vc = oracle.to_f64(segs[s][1]), oracle.to_f64(segs[s][2])
+            for g in range(cfg.G):
+                h_ = kvh * cfg.G + g
+                want = oracle.decode_attention(oracle.to_f64(st["q"][b, h_]), Kc, Vc, cfg.scale)
+                err = float(np.max(np.abs(out[b, h_] - want)))
+                worst = max(worst, err)
+                assert err <= pu.OUT_ATOL[cfg.dtype], f"step {t} seg {s} head {g}: err {err}"
+    print(f"  decode loop: max abs err {worst:.2e}", flush=True)
