@@ -256,6 +256,27 @@ def main() -> int:
     wall = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {wall:.3f} s")
 
+    # serving-loop extra, outside the timed steps: one decoded token joins
+    # every segment of every layer (segments are full, so each append
+    # replaces the oldest token: the sliding-window path)
+    step_tok = kvsynth.step_inputs(cfg, 0, 0)
+    kn = pipeline.device_tensor(step_tok["k_new"])
+    vn = pipeline.device_tensor(step_tok["v_new"])
+    for run in layers:
+        run.append(kn, vn, step_tok["pos"])
+    torch.cuda.synchronize()
+    g_app = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_app):
+        for run in layers:
+            run.append(kn, vn, step_tok["pos"])
+    a_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    a_ev[0].record()
+    for _ in range(5):
+        g_app.replay()
+    a_ev[1].record()
+    torch.cuda.synchronize()
+    append_us = a_ev[0].elapsed_time(a_ev[1]) / (5 * L) * 1e3
+
     # per-phase GPU time (ms) averaged over steps, then per layer
     st = {name: 0.0 for name in phases}
     for ev in evs:
@@ -311,6 +332,10 @@ def main() -> int:
                      "avg_launch_us": round(us["decode"], 3)},
         "stages_us_per_layer": {k: round(v, 3) for k, v in us.items()},
         "hbm_copy_reference_GBps": round(copy_gbs, 1),
+        "extras": {"append_us_per_layer": round(append_us, 3),
+                   "append_note": "kvsel_append of one decoded token into all 32 full "
+                                  "segments of a layer (oldest-token replacement), "
+                                  "outside the timed step"},
         "decode_frac_of_copy_reference": round(dec_gbs / copy_gbs, 4),
         "compact_frac_of_copy_reference": round(gbs(cmp_bytes, us["compact"]) / copy_gbs, 4),
         "stages_roofline": {
