@@ -6,15 +6,16 @@
 //        keep_tokens (ChunkLLM page, §2.2-§2.3); a chunk's weight is its length.
 // POLICY local / special-token / global head rules (FastGen page).
 //
-// TOPB and CHUNK share one weighted radix select: scores become order-
-// preserving 32-bit keys (NaN lowest, -0 folded into +0) held in LDS; four
-// 8-bit digit passes find the threshold key T and how much weight must come
-// from keys equal to T; an ordered sweep then keeps every key > T plus the
-// first keys == T in index order.  Histogram updates go to 16 replicas (lane
-// mod 16, padded so a bin's replicas sit in different banks), which keeps LDS
-// atomic conflicts low even when most scores share their top bits.  Kept
-// tokens are placed by wave ballots / DPP scans in index order, so the output
-// is ascending and the tie-break is the lowest index, deterministically.
+// All selections are radix selects over order-preserving 32-bit keys made
+// from the fp32 scores (NaN lowest, -0 folded into +0): digit passes find the
+// threshold key T and how much weight must come from keys equal to T; every
+// key > T is kept plus the first keys == T in index order.  Kept positions
+// are placed by scans in index order, so the output is ascending and the
+// tie-break is the lowest index, deterministically, without a sort.
+//   select_topb_kernel   TOPB, segments of up to 32768 items, keys in registers
+//   select_reg_kernel    CHUNK (weighted), up to 32768 chunks, keys in registers
+//   select_rank_kernel   longer segments, keys in LDS or re-read from memory
+//   select_policy_kernel POLICY, closed-form index ranges
 #include <type_traits>
 
 #include "kvsel_internal.h"
