@@ -2,11 +2,11 @@
 // cache: the decode-step attention of the RAP page (Fig. 2 / Eq. 2) run over
 // only the kept tokens (ChunkLLM page §2.3; ZigZagkv page Eq. 6 budgets).
 //
-// Work items are (segment, chunk of 64*tpw rows) pairs flattened over all
+// Work items are (segment, chunk of 4*rpw rows) pairs flattened over all
 // segments, so segments of very different lengths (FastGen local / special /
-// global heads) load the chip evenly; tpw (16-row tiles per wavefront) is
-// picked from the cache size so that all items fit in one round of resident
-// workgroups.
+// global heads) load the chip evenly; rpw (rows per wavefront, not tied to
+// the 16-row tile: a wavefront's last tile may be partial) is picked from the
+// cache size so that all items fit in one round of resident workgroups.
 // A workgroup of four wavefronts owns one item; each wavefront streams its
 // rows in 16-row tiles with the next tile's loads in flight while the current
 // one is computed:
@@ -63,18 +63,23 @@ __device__ __forceinline__ f32x4 qk_step(const u32x4& a, const u32x4& b, f32x4 a
   return acc;
 }
 
-// 16-row tiles per wavefront.  Items of equal size finish together, so the
-// launch is sized to ONE round of resident workgroups (slots): a second round
-// would run a handful of stragglers on an otherwise idle chip.  A segment
-// wastes at most one partial item, hence the S reserved slots.
-int tiles_per_wave(int64_t r_cap, int S, int slots) {
+// Rows per wavefront.  Items of equal size finish together, so the launch is
+// sized to ONE round of resident workgroups (slots): a second round would run
+// a handful of stragglers on an otherwise idle chip.  A segment wastes at
+// most one partial item, hence the S reserved slots.  At least two tiles: on
+// small caches fewer, longer items beat more, shorter ones (each item pays a
+// segment lookup, a first-tile latency and a partial write).
+constexpr int kMinRows = 2 * kTile;
+
+int rows_per_wave(int64_t r_cap, int S, int slots) {
   const int64_t avail = std::max<int64_t>(slots - S, slots / 2);
-  const int64_t rows = (int64_t)kWaves * kTile * std::max<int64_t>(avail, 1);
-  const int64_t t = (r_cap + rows - 1) / rows;
-  return (int)std::min<int64_t>(std::max<int64_t>(t, 1), kMaxTpw);
+  const int64_t per = (int64_t)kWaves * std::max<int64_t>(avail, 1);
+  const int64_t r = (r_cap + per - 1) / per;
+  return (int)std::min<int64_t>(std::max<int64_t>(r, kMinRows), (int64_t)kMaxTpw * kTile);
 }
 
-// Workspace items for any tpw >= 1 (the bound the workspace is sized for).
+// Workspace items for any rpw >= kTile (the bound the workspace is sized for;
+// rows_per_wave never goes below kMinRows).
 int64_t max_items(int64_t r_cap, int S) {
   return (r_cap + kWaves * kTile - 1) / (kWaves * kTile) + S;
 }
@@ -283,7 +288,7 @@ template <typename T, int D, int HG>
 __global__ __launch_bounds__(kThreads, KVSEL_DECODE_MIN_BLOCKS) void decode_split_kernel(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
     const int64_t* __restrict__ seg_off, const int32_t* __restrict__ seg_len, int64_t r_cap,
-    int S, int hq, int hkv, int G, float c, int tpw, float2* __restrict__ part_ml,
+    int S, int hq, int hkv, int G, float c, int rpw, float2* __restrict__ part_ml,
     float* __restrict__ part_o) {
   using Gm = Geom<T, D>;
   __shared__ float4 sp_all[kWaves][kTile];
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(kThreads, KVSEL_DECODE_MIN_BLOCKS) void decode_spli
   __shared__ float sm_m[kWaves][HG], sm_l[kWaves][HG];
 
   const int64_t item = blockIdx.x;
-  const int64_t rows_per_item = (int64_t)kWaves * kTile * tpw;
+  const int64_t rows_per_item = (int64_t)kWaves * rpw;
   const uint32_t rpi = (uint32_t)rows_per_item;
   const SegLoc loc = wave_locate(seg_off, seg_len, S, r_cap, item, true,
                                  [=](uint32_t l) { return (l + rpi - 1) / rpi; });
@@ -303,8 +308,8 @@ __global__ __launch_bounds__(kThreads, KVSEL_DECODE_MIN_BLOCKS) void decode_spli
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int grp = lane >> 4, l16 = lane & 15;
-  const int64_t wr0 = row0 + (int64_t)wid * kTile * tpw;
-  const int64_t wr1 = min(row_end, wr0 + (int64_t)kTile * tpw);
+  const int64_t wr0 = row0 + (int64_t)wid * rpw;
+  const int64_t wr1 = min(row_end, wr0 + (int64_t)rpw);
   const char* kseg = kc + loc.off * Gm::RB;
   const char* vseg = vc + loc.off * Gm::RB;
   float4* sp = sp_all[wid];
@@ -426,9 +431,9 @@ template <int HG, int D>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     const float2* __restrict__ part_ml, const float* __restrict__ part_o,
     const int64_t* __restrict__ seg_off, const int32_t* __restrict__ seg_len, int64_t r_cap,
-    int hq, int hkv, int G, int S, int tpw, int64_t items_max, float* __restrict__ out) {
+    int hq, int hkv, int G, int S, int rpw, int64_t items_max, float* __restrict__ out) {
   const int s = blockIdx.x, b = s / hkv, kvh = s % hkv;
-  const uint32_t rpi = (uint32_t)((int64_t)kWaves * kTile * tpw);
+  const uint32_t rpi = (uint32_t)((int64_t)kWaves * rpw);
   const SegLoc loc = wave_locate(seg_off, seg_len, S, r_cap, s, false,
                                  [=](uint32_t l) { return (l + rpi - 1) / rpi; });
   // overlapping segments (a violated precondition) can ask for more items than
@@ -470,17 +475,17 @@ hipError_t run(int batch, int hq, int hkv, float scale, const void* q, const voi
                float* out, void* ws, hipStream_t stream) {
   const int S = batch * hkv, G = hq / hkv;
   const int slots = device_info().cus * resident_blocks(decode_split_kernel<T, D, HG>);
-  const int tpw = tiles_per_wave(r_cap, S, slots);
-  const int64_t rpi = (int64_t)kWaves * kTile * tpw;
+  const int rpw = rows_per_wave(r_cap, S, slots);
+  const int64_t rpi = (int64_t)kWaves * rpw;
   const int64_t items = (r_cap + rpi - 1) / rpi + S;   // launched; <= max_items
   auto* ml = static_cast<float2*>(ws);
   auto* po = reinterpret_cast<float*>(ml + max_items(r_cap, S) * HG);
   const float c = scale * kLog2e;
   decode_split_kernel<T, D, HG><<<dim3((unsigned)items), dim3(kThreads), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(k_c),
-      static_cast<const char*>(v_c), seg_off, seg_len, r_cap, S, hq, hkv, G, c, tpw, ml, po);
+      static_cast<const char*>(v_c), seg_off, seg_len, r_cap, S, hq, hkv, G, c, rpw, ml, po);
   decode_combine_kernel<HG, D><<<dim3(S), dim3(kThreads), 0, stream>>>(
-      ml, po, seg_off, seg_len, r_cap, hq, hkv, G, S, tpw, items, out);
+      ml, po, seg_off, seg_len, r_cap, hq, hkv, G, S, rpw, items, out);
   return hipGetLastError();
 }
 
