@@ -222,19 +222,31 @@ def select_topb(s: np.ndarray, budget: int) -> np.ndarray:
     return np.sort(score_order(s)[:b]).astype(np.int64)
 
 
-def select_chunks(chunk_scores: np.ndarray, chunk_end: np.ndarray, keep_tokens: int) -> np.ndarray:
-    """Take chunks in score order until their token count reaches keep_tokens.
+def select_chunks(chunk_scores: np.ndarray, chunk_end: np.ndarray, keep_tokens: int,
+                  local_chunks: int = 0, top_chunks: int = 0) -> np.ndarray:
+    """Chunk selection [CK §2.3; the operating points of §3.2]: the last
+    `local_chunks` chunks are always kept; then
+
+      top_chunks > 0   the `top_chunks` highest-scoring other chunks are kept
+                       (a fixed chunk count, the top_k = 256 setting);
+      top_chunks == 0  other chunks are taken in score order until the kept
+                       token count (local chunks included) reaches keep_tokens.
 
     chunk_end is the exclusive end of each chunk (the first starts at 0).
     Returns the kept token positions ascending (chunks are kept whole).
     """
     ends = np.asarray(chunk_end, np.int64)
     starts = np.concatenate([[0], ends[:-1]])
-    chosen = []
-    got = 0
-    if keep_tokens > 0:
-        for c in score_order(chunk_scores):
-            chosen.append(int(c))
+    nc = ends.size
+    n_local = max(0, min(int(local_chunks), nc))
+    chosen = list(range(nc - n_local, nc))
+    got = int(sum(int(ends[c] - starts[c]) for c in chosen))
+    others = [int(c) for c in score_order(chunk_scores) if c < nc - n_local]
+    if top_chunks > 0:
+        chosen += others[:int(top_chunks)]
+    elif got < keep_tokens:
+        for c in others:
+            chosen.append(c)
             got += int(ends[c] - starts[c])
             if got >= keep_tokens:
                 break

@@ -391,3 +391,69 @@ def test_append_skip_and_bounds():
     d = oracle.append_token(np.array([], np.int64), np.zeros((0, 4)), np.zeros((0, 4)), 7,
                             np.zeros(4), np.zeros(4), cap=0, limit=0)
     assert d[0].size == 0
+
+
+# ---------------------------------------------------------------------------
+# chunk selection with forced local chunks and a fixed chunk count
+# (ChunkLLM page, §2.3 and the §3.2 operating points)
+# ---------------------------------------------------------------------------
+
+def _chunks_of(kept, ends):
+    starts = np.concatenate([[0], ends[:-1]])
+    return sorted({int(np.searchsorted(ends, p, side="right")) for p in kept}), starts
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_chunk_local_and_count_modes(seed):
+    """Properties that define the two modes (no restated algorithm): local
+    chunks always kept; the kept non-local chunks outrank every dropped one
+    (score, then lower index); count mode keeps exactly k of them; token mode
+    keeps the fewest that reach the target."""
+    r = np.random.default_rng(500 + seed)
+    nc = int(r.integers(1, 60))
+    lens = r.integers(1, 9, size=nc)
+    ends = np.cumsum(lens)
+    cs = r.random(nc)
+    if seed % 3 == 0:
+        cs = np.round(cs, 1)                      # ties
+    L = int(r.integers(0, nc + 2))
+    k = int(r.integers(1, nc + 3))
+    local = set(range(nc - min(L, nc), nc))
+    others = [c for c in range(nc) if c not in local]
+
+    def outranks(a, b):
+        return cs[a] > cs[b] or (cs[a] == cs[b] and a < b)
+
+    def check_ranked(kept_set):
+        kept_o = [c for c in others if c in kept_set]
+        drop_o = [c for c in others if c not in kept_set]
+        assert all(outranks(a, b) for a in kept_o for b in drop_o)
+        return kept_o
+
+    for kept, mode in ((oracle.select_chunks(cs, ends, 0, local_chunks=L, top_chunks=k), "count"),
+                       (None, "token")):
+        if mode == "token":
+            target = int(r.integers(0, ends[-1] + 5))
+            kept = oracle.select_chunks(cs, ends, target, local_chunks=L)
+        chunks, _ = _chunks_of(kept, ends)
+        assert np.all(np.diff(kept) > 0)
+        assert len(kept) == sum(int(lens[c]) for c in chunks)      # whole chunks only
+        assert local <= set(chunks)
+        kept_o = check_ranked(set(chunks))
+        if mode == "count":
+            assert len(kept_o) == min(k, len(others))
+        else:
+            tok = len(kept)
+            assert tok >= min(target, int(ends[-1]))
+            if kept_o:   # minimal: without the lowest-ranked extra chunk the target is missed
+                worst = min(kept_o, key=lambda c: (cs[c], -c))
+                assert tok - int(lens[worst]) < target
+
+
+def test_chunk_local_zero_matches_plain():
+    r = np.random.default_rng(9)
+    ends = np.cumsum(r.integers(1, 6, size=40))
+    cs = r.random(40)
+    for target in (0, 1, 17, int(ends[-1])):
+        assert np.array_equal(oracle.select_chunks(cs, ends, target),
+                              oracle.select_chunks(cs, ends, target, local_chunks=0, top_chunks=0))
