@@ -106,10 +106,14 @@ kvsel_status kvsel_score(const kvsel_shape* s /*host*/, int32_t w, int64_t q_pos
  * number and -0 equals +0.
  *   TOPB   (ZigZagkv page, Eq. 7 + Eq. 6): keep the min(budget[s], n)
  *          highest-score tokens.  scores [batch][hkv][n].
- *   CHUNK  (ChunkLLM page, §2.2-§2.3): chunks are taken in score order until
- *          their token count reaches keep_tokens; kept chunks are whole and
+ *   CHUNK  (ChunkLLM page, §2.2-§2.3 and the §3.2 operating points): the
+ *          last local_chunks chunks are always kept; then either the
+ *          top_chunks best other chunks (top_chunks > 0), or other chunks in
+ *          score order until the kept token count (local chunks included)
+ *          reaches keep_tokens (top_chunks == 0).  Kept chunks are whole and
  *          expanded to their token positions.  scores [batch][hkv][n_chunks];
  *          chunk c of batch b covers [chunk_end[b][c-1], chunk_end[b][c]).
+ *          local_chunks / top_chunks > 0 need n_chunks <= 32768.
  *   POLICY (FastGen page, core claim): per KV head kind: GLOBAL keeps all n,
  *          LOCAL keeps the last min(local_window, n), SPECIAL keeps
  *          special_pos[b][0 .. n_special).  scores unused (may be NULL).
@@ -130,6 +134,8 @@ typedef struct {
   int64_t local_window;         /* POLICY: tokens LOCAL heads keep, >= 0 */
   const int32_t* special_pos;   /* POLICY: [batch][n_special], ascending, unique, in [0, n) */
   int64_t n_special;            /* POLICY: entries per batch element, >= 0 */
+  int64_t local_chunks;         /* CHUNK:  trailing chunks always kept, >= 0 */
+  int64_t top_chunks;           /* CHUNK:  > 0: keep this many other chunks; 0: keep_tokens */
 } kvsel_select_params;
 
 kvsel_status kvsel_select(const kvsel_shape* s /*host*/, const kvsel_select_params* p /*host*/,

@@ -39,7 +39,8 @@ class SelectParams(ctypes.Structure):
                 ("n_chunks", ctypes.c_int64), ("chunk_end", ctypes.c_void_p),
                 ("keep_tokens", ctypes.c_int64), ("head_kind", ctypes.c_void_p),
                 ("local_window", ctypes.c_int64), ("special_pos", ctypes.c_void_p),
-                ("n_special", ctypes.c_int64)]
+                ("n_special", ctypes.c_int64), ("local_chunks", ctypes.c_int64),
+                ("top_chunks", ctypes.c_int64)]
 
 
 _lib = None
@@ -126,9 +127,11 @@ def kvsel_score(shape: Shape, w: int, q_pos0: int, q_win, k, scores, ws, stream=
 
 
 def select_params(mode, budget=None, n_chunks=0, chunk_end=None, keep_tokens=0,
-                  head_kind=None, local_window=0, special_pos=None, n_special=0) -> SelectParams:
+                  head_kind=None, local_window=0, special_pos=None, n_special=0,
+                  local_chunks=0, top_chunks=0) -> SelectParams:
     return SelectParams(int(mode), _ptr(budget), int(n_chunks), _ptr(chunk_end), int(keep_tokens),
-                        _ptr(head_kind), int(local_window), _ptr(special_pos), int(n_special))
+                        _ptr(head_kind), int(local_window), _ptr(special_pos), int(n_special),
+                        int(local_chunks), int(top_chunks))
 
 
 def kvsel_select(shape: Shape, params: SelectParams, scores, seg_off, seg_len, idx, r_cap: int,

@@ -143,15 +143,20 @@ kvsel_status kvsel_select(const kvsel_shape* s, const kvsel_select_params* p, co
   switch (p->mode) {
     case KVSEL_SEL_TOPB:
       if (!scores || !p->budget) return fail(KVSEL_EINVAL, "TOPB needs scores and budget");
-      return hip_status(launch_select_rank(S, s->hkv, s->n, scores, p->budget, nullptr, 0, seg_off,
-                                           seg_len, idx, r_cap, stream),
+      return hip_status(launch_select_rank(S, s->hkv, s->n, scores, p->budget, nullptr, 0, 0, 0,
+                                           seg_off, seg_len, idx, r_cap, stream),
                         "kvsel_select launch");
     case KVSEL_SEL_CHUNK:
       if (!scores || !p->chunk_end) return fail(KVSEL_EINVAL, "CHUNK needs scores and chunk_end");
       if (p->n_chunks < 1 || p->n_chunks > s->n)
         return fail(KVSEL_EINVAL, "n_chunks must be in [1, n] (got %lld)", (long long)p->n_chunks);
+      if (p->local_chunks < 0 || p->top_chunks < 0)
+        return fail(KVSEL_EINVAL, "local_chunks and top_chunks must be >= 0");
+      if ((p->local_chunks > 0 || p->top_chunks > 0) && p->n_chunks > 32768)
+        return fail(KVSEL_EUNSUPPORTED, "local_chunks / top_chunks need n_chunks <= 32768");
       return hip_status(launch_select_rank(S, s->hkv, p->n_chunks, scores, nullptr, p->chunk_end,
-                                           p->keep_tokens, seg_off, seg_len, idx, r_cap, stream),
+                                           p->keep_tokens, p->local_chunks, p->top_chunks, seg_off,
+                                           seg_len, idx, r_cap, stream),
                         "kvsel_select launch");
     case KVSEL_SEL_POLICY:
       if (!p->head_kind) return fail(KVSEL_EINVAL, "POLICY needs head_kind");

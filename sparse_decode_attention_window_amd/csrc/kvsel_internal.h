@@ -232,6 +232,7 @@ hipError_t launch_compact(int dtype, int head_dim, const void* k, const void* v,
 
 hipError_t launch_select_rank(int S, int hkv, int64_t n_items, const float* scores,
                               const int32_t* budget, const int64_t* chunk_end, int64_t keep_tokens,
+                              int64_t local_chunks, int64_t top_chunks,
                               const int64_t* seg_off, int32_t* seg_len, int32_t* idx,
                               int64_t r_cap, hipStream_t stream);
 

@@ -13,7 +13,8 @@
 // are placed by scans in index order, so the output is ascending and the
 // tie-break is the lowest index, deterministically, without a sort.
 //   select_topb_kernel   TOPB, segments of up to 32768 items, keys in registers
-//   select_reg_kernel    CHUNK (weighted), up to 32768 chunks, keys in registers
+//   select_chunk_kernel  CHUNK, up to 32768 chunks, keys in registers; forced
+//                        local chunks and a fixed chunk count as options
 //   select_rank_kernel   longer segments, keys in LDS or re-read from memory
 //   select_policy_kernel POLICY, closed-form index ranges
 #include <type_traits>
@@ -200,16 +201,23 @@ __global__ __launch_bounds__(kThreads) void select_rank_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Register-resident weighted (chunk) variant for N <= 1024 * KPT items: thread t holds items
-// j = k * 1024 + t (k < KPT) in registers, so the radix passes read no
-// memory; histograms use 11-bit digits (3 passes) over 8 padded replicas.
-// Emission orders items k-major, thread-minor (that is index order): per
-// (k, wavefront) block the kept count / weight is known from ballots or DPP
-// sums, one block-wide scan over the 16 * KPT blocks places them.
+// Chunk selection for N <= 1024 * KPT chunks (ChunkLLM page, §2.3 and the
+// §3.2 operating points): the last `local_chunks` chunks are always kept
+// (their keys are forced above every score key), then either the
+// `top_chunks` best other chunks (selection weight 1 per chunk) or, with
+// top_chunks == 0, other chunks in score order until the kept token count
+// reaches keep_tokens (selection weight = chunk length; the target is raised
+// to the local chunks' tokens so that they are always all kept).  Thread t
+// holds chunks j = k * 1024 + t in registers; histograms use 11-bit digits
+// (3 passes) over 8 padded replicas.  Emission orders chunks k-major,
+// thread-minor (index order): per (k, wavefront) block the kept token count
+// is known from DPP sums, one block-wide scan over the 16 * KPT blocks places
+// them, and each kept chunk writes its token range.
 // ---------------------------------------------------------------------------
 constexpr int kRBins = 2048;
 constexpr int kRReps = 8;
 constexpr int kRPitch = kRBins + 1;
+constexpr uint32_t kForcedKey = 0xffffffffu;  // above the key of every score (+inf: 0xff800000)
 
 // Exclusive scan of vals[0..M) in LDS (M <= 1024) by the whole block;
 // returns the total to every thread.
@@ -230,10 +238,10 @@ __device__ uint32_t block_scan_lds(uint32_t* vals, int M, uint32_t* wave_tot) {
   return total;
 }
 
-template <bool WEIGHTED, int KPT>
-__global__ __launch_bounds__(kThreads) void select_reg_kernel(
-    const float* __restrict__ scores, int64_t N, int hkv, const int32_t* __restrict__ budget,
-    const int64_t* __restrict__ chunk_end, int64_t keep_tokens,
+template <int KPT>
+__global__ __launch_bounds__(kThreads) void select_chunk_kernel(
+    const float* __restrict__ scores, int64_t N, int hkv, const int64_t* __restrict__ chunk_end,
+    int64_t keep_tokens, int64_t local_chunks, int64_t top_chunks,
     const int64_t* __restrict__ seg_off, int32_t* __restrict__ seg_len,
     int32_t* __restrict__ idx, int64_t r_cap) {
   __shared__ uint32_t hist[kRReps * kRPitch];
@@ -245,38 +253,40 @@ __global__ __launch_bounds__(kThreads) void select_reg_kernel(
   const int s = blockIdx.x;
   const int b = s / hkv;
   const float* sc = scores + (int64_t)s * N;
-  const int64_t* ce = WEIGHTED ? chunk_end + (int64_t)b * N : nullptr;
+  const int64_t* ce = chunk_end + (int64_t)b * N;
   const int64_t off = seg_off[s];
   const bool off_ok = off >= 0 && off <= r_cap;
   const int64_t room = off_ok ? r_cap - off : 0;
 
-  const int64_t total = WEIGHTED ? ce[N - 1] : N;
-  int64_t tgt = WEIGHTED ? keep_tokens : (int64_t)budget[s];
+  const int64_t n_local = local_chunks < 0 ? 0 : (local_chunks > N ? N : local_chunks);
+  const int64_t first_local = N - n_local;
+  const bool by_count = top_chunks > 0;
+  const int64_t tokens = ce[N - 1];
+  const int64_t local_tokens = tokens - (first_local > 0 ? ce[first_local - 1] : 0);
+  // target and total in selection units (chunks or tokens)
+  const int64_t total = by_count ? N : tokens;
+  int64_t tgt = by_count ? n_local + top_chunks
+                         : (keep_tokens > local_tokens ? keep_tokens : local_tokens);
   tgt = tgt < 0 ? 0 : (tgt > total ? total : tgt);
   if (tgt == 0 || tgt == total) {
-    for (int64_t r = tid; r < tgt && r < room; r += kThreads) idx[off + r] = (int32_t)r;
-    if (tid == 0) seg_len[s] = (int32_t)tgt;
+    const int64_t keep = tgt == 0 ? 0 : tokens;   // nothing, or every chunk: [0, tokens)
+    for (int64_t r = tid; r < keep && r < room; r += kThreads) idx[off + r] = (int32_t)r;
+    if (tid == 0) seg_len[s] = (int32_t)keep;
     return;
   }
 
-  // ---- items into registers (all loads independent) --------------------
-  // Unweighted items have weight 1 (0 past N); weights of chunks are lengths.
-  uint32_t key[KPT];
-  uint32_t wt[WEIGHTED ? KPT : 1];
-  auto weight = [&](int k) -> uint32_t {
-    if constexpr (WEIGHTED) return wt[k];
-    else return (int64_t)k * kThreads + tid < N ? 1u : 0u;
-  };
+  // ---- chunks into registers (all loads independent) ----------------------
+  uint32_t key[KPT], wt[KPT];   // wt: the chunk's token count (0 past N)
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const int64_t j = (int64_t)k * kThreads + tid;
     const int64_t jc = j < N ? j : N - 1;
-    key[k] = score_key(sc[jc]);
-    if constexpr (WEIGHTED) {
-      const int64_t lo = jc ? ce[jc - 1] : 0;
-      wt[k] = j < N ? (uint32_t)(ce[jc] - lo) : 0u;
-    }
+    key[k] = jc >= first_local ? kForcedKey : score_key(sc[jc]);
+    const int64_t lo = jc ? ce[jc - 1] : 0;
+    wt[k] = j < N ? (uint32_t)(ce[jc] - lo) : 0u;
   }
+  // selection weight: 1 per chunk (count mode) or its token count
+  auto wsel = [&](int k) -> uint32_t { return by_count ? (wt[k] ? 1u : 0u) : wt[k]; };
 
   // ---- radix select: 11 + 11 + 10 bits ------------------------------------
   uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)tgt;
@@ -289,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void select_reg_kernel(
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < KPT; ++k) {
-      const uint32_t w = weight(k);
+      const uint32_t w = wsel(k);
       if (w && (key[k] & pmask) == prefix) atomicAdd(&my_hist[(key[k] >> shift) & dmask], w);
     }
     __syncthreads();
@@ -329,54 +339,44 @@ __global__ __launch_bounds__(kThreads) void select_reg_kernel(
   const uint32_t T = prefix;
 
   // ---- ordered emission over (k, wave) blocks ------------------------------
-  // an item equal to T is kept while the equal weight before it (index order)
-  // is short of `remaining`; every item > T is kept
-  auto eq_w = [&](int k) -> uint32_t { return key[k] == T ? weight(k) : 0u; };
-  auto eq_before_in_wave = [&](int k) -> uint32_t {
-    const uint32_t e = eq_w(k);
-    return WEIGHTED ? wave_incl_scan_u32(e) - e : lanes_below(__ballot(e != 0u));
-  };
+  // a chunk equal to T is kept while the equal selection weight before it
+  // (index order) is short of `remaining`; every chunk > T is kept
+  auto eq_w = [&](int k) -> uint32_t { return key[k] == T ? wsel(k) : 0u; };
   // 1) equal-key weight per block, scanned in index order
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
-    const uint32_t e = eq_w(k);
-    const uint32_t es = WEIGHTED ? wave_sum_u32(e) : (uint32_t)__popcll(__ballot(e != 0u));
+    const uint32_t es = wave_sum_u32(eq_w(k));
     if (lane == 0) blk_a[k * kWaves + wid] = es;
   }
   __syncthreads();
   block_scan_lds(blk_a, KPT * kWaves, wave_tot);
-  auto kept_w = [&](int k) -> uint32_t {
-    const uint32_t w = weight(k);
+  auto kept_tokens = [&](int k) -> uint32_t {
     // cross-lane scan first, with every lane active
-    const uint32_t eb = blk_a[k * kWaves + wid] + eq_before_in_wave(k);
-    const bool keep = w && (key[k] > T || (key[k] == T && eb < remaining));
-    return keep ? w : 0u;
+    const uint32_t e = eq_w(k);
+    const uint32_t eb = blk_a[k * kWaves + wid] + wave_incl_scan_u32(e) - e;
+    const bool keep = wsel(k) && (key[k] > T || (key[k] == T && eb < remaining));
+    return keep ? wt[k] : 0u;
   };
-  // 2) kept weight per block, scanned in index order
+  // 2) kept tokens per block, scanned in index order
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
-    const uint32_t kw = kept_w(k);
-    const uint32_t ks = WEIGHTED ? wave_sum_u32(kw) : (uint32_t)__popcll(__ballot(kw != 0u));
+    const uint32_t ks = wave_sum_u32(kept_tokens(k));
     if (lane == 0) blk_b[k * kWaves + wid] = ks;
   }
   __syncthreads();
   const uint32_t kept_total = block_scan_lds(blk_b, KPT * kWaves, wave_tot);
   if (tid == 0) seg_len[s] = (int32_t)kept_total;
-  // 3) write the kept token positions
+  // 3) write the kept chunks' token ranges
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const int64_t j = (int64_t)k * kThreads + tid;
-    const uint32_t kw = kept_w(k);
-    const uint32_t before = WEIGHTED ? wave_incl_scan_u32(kw) - kw : lanes_below(__ballot(kw != 0u));
+    const uint32_t kw = kept_tokens(k);
+    const uint32_t before = wave_incl_scan_u32(kw) - kw;
     const int64_t pos = (int64_t)blk_b[k * kWaves + wid] + before;
     if (kw) {
-      if (WEIGHTED) {
-        const int64_t st = j ? ce[j - 1] : 0;
-        for (uint32_t t = 0; t < kw; ++t)
-          if (pos + t < room) idx[off + pos + t] = (int32_t)(st + t);
-      } else if (pos < room) {
-        idx[off + pos] = (int32_t)j;
-      }
+      const int64_t st = j ? ce[j - 1] : 0;
+      for (uint32_t t = 0; t < kw; ++t)
+        if (pos + t < room) idx[off + pos + t] = (int32_t)(st + t);
     }
   }
 }
@@ -777,29 +777,31 @@ hipError_t launch_rank(int S, int hkv, int64_t N, const float* scores, const int
 }
 
 
-template <bool W, int KPT>
-hipError_t launch_reg(int S, int hkv, int64_t N, const float* scores, const int32_t* budget,
-                      const int64_t* chunk_end, int64_t keep_tokens, const int64_t* seg_off,
-                      int32_t* seg_len, int32_t* idx, int64_t r_cap, hipStream_t stream) {
-  select_reg_kernel<W, KPT><<<dim3(S), dim3(kThreads), 0, stream>>>(
-      scores, N, hkv, budget, chunk_end, keep_tokens, seg_off, seg_len, idx, r_cap);
+template <int KPT>
+hipError_t launch_chunk(int S, int hkv, int64_t N, const float* scores, const int64_t* chunk_end,
+                        int64_t keep_tokens, int64_t local_chunks, int64_t top_chunks,
+                        const int64_t* seg_off, int32_t* seg_len, int32_t* idx, int64_t r_cap,
+                        hipStream_t stream) {
+  select_chunk_kernel<KPT><<<dim3(S), dim3(kThreads), 0, stream>>>(
+      scores, N, hkv, chunk_end, keep_tokens, local_chunks, top_chunks, seg_off, seg_len, idx,
+      r_cap);
   return hipGetLastError();
 }
 
-template <bool W>
-hipError_t launch_reg_n(int S, int hkv, int64_t N, const float* scores, const int32_t* budget,
-                        const int64_t* chunk_end, int64_t keep_tokens, const int64_t* seg_off,
-                        int32_t* seg_len, int32_t* idx, int64_t r_cap, hipStream_t stream) {
-#define KVSEL_REG(K) \
-  return launch_reg<W, K>(S, hkv, N, scores, budget, chunk_end, keep_tokens, seg_off, seg_len, \
-                          idx, r_cap, stream)
-  if (N <= 1 * kThreads) KVSEL_REG(1);
-  if (N <= 2 * kThreads) KVSEL_REG(2);
-  if (N <= 4 * kThreads) KVSEL_REG(4);
-  if (N <= 8 * kThreads) KVSEL_REG(8);
-  if (N <= 16 * kThreads) KVSEL_REG(16);
-  KVSEL_REG(32);
-#undef KVSEL_REG
+hipError_t launch_chunk_n(int S, int hkv, int64_t N, const float* scores, const int64_t* chunk_end,
+                          int64_t keep_tokens, int64_t local_chunks, int64_t top_chunks,
+                          const int64_t* seg_off, int32_t* seg_len, int32_t* idx, int64_t r_cap,
+                          hipStream_t stream) {
+#define KVSEL_CHUNK(K) \
+  return launch_chunk<K>(S, hkv, N, scores, chunk_end, keep_tokens, local_chunks, top_chunks, \
+                         seg_off, seg_len, idx, r_cap, stream)
+  if (N <= 1 * kThreads) KVSEL_CHUNK(1);
+  if (N <= 2 * kThreads) KVSEL_CHUNK(2);
+  if (N <= 4 * kThreads) KVSEL_CHUNK(4);
+  if (N <= 8 * kThreads) KVSEL_CHUNK(8);
+  if (N <= 16 * kThreads) KVSEL_CHUNK(16);
+  KVSEL_CHUNK(32);
+#undef KVSEL_CHUNK
 }
 
 template <int KPT>
@@ -828,12 +830,13 @@ hipError_t launch_topb_n(int S, int64_t N, const float* scores, const int32_t* b
 
 hipError_t launch_select_rank(int S, int hkv, int64_t n_items, const float* scores,
                               const int32_t* budget, const int64_t* chunk_end, int64_t keep_tokens,
+                              int64_t local_chunks, int64_t top_chunks,
                               const int64_t* seg_off, int32_t* seg_len, int32_t* idx,
                               int64_t r_cap, hipStream_t stream) {
   const bool weighted = chunk_end != nullptr;
   if (n_items <= 32 * kThreads)
-    return weighted ? launch_reg_n<true>(S, hkv, n_items, scores, budget, chunk_end, keep_tokens,
-                                         seg_off, seg_len, idx, r_cap, stream)
+    return weighted ? launch_chunk_n(S, hkv, n_items, scores, chunk_end, keep_tokens, local_chunks,
+                                     top_chunks, seg_off, seg_len, idx, r_cap, stream)
                     : launch_topb_n(S, n_items, scores, budget, seg_off, seg_len, idx, r_cap,
                                     stream);
   // longer segments: keys cached in LDS when they fit, else re-read from global

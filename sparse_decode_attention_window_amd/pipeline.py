@@ -28,13 +28,19 @@ def device_tensor(arr: np.ndarray, device="cuda"):
 
 
 def capacities(mode: int, batch: int, hkv: int, n: int, *, budget=None, keep_tokens=0,
-               max_chunk=0, head_kind=None, local_window=0, n_special=0) -> np.ndarray:
+               max_chunk=0, head_kind=None, local_window=0, n_special=0, local_chunks=0,
+               top_chunks=0) -> np.ndarray:
     """Rows reserved per segment (int64 [batch*hkv])."""
     S = batch * hkv
     if mode == K.KVSEL_SEL_TOPB:
         cap = np.minimum(np.maximum(np.asarray(budget, np.int64).reshape(S), 0), n)
     elif mode == K.KVSEL_SEL_CHUNK:
-        rows = 0 if keep_tokens <= 0 else min(n, keep_tokens + max(0, max_chunk - 1))
+        local = local_chunks * max_chunk
+        if top_chunks > 0:
+            rows = min(n, (local_chunks + top_chunks) * max_chunk)
+        else:
+            rows = 0 if keep_tokens <= 0 and local == 0 else \
+                min(n, max(keep_tokens + max(0, max_chunk - 1), local))
         cap = np.full(S, rows, np.int64)
     else:
         per_kind = {K.KVSEL_HEAD_GLOBAL: n, K.KVSEL_HEAD_LOCAL: min(local_window, n),
@@ -128,9 +134,11 @@ class LayerRun:
         return self
 
 
-def build_layer(cfg, inputs: dict, *, budget=None, slack: int = 0, device="cuda") -> LayerRun:
+def build_layer(cfg, inputs: dict, *, budget=None, slack: int = 0, local_chunks: int = 0,
+                top_chunks: int = 0, device="cuda") -> LayerRun:
     """LayerRun for one synthetic layer (cfg: a kvsynth Config, inputs: layer_inputs()).
-    `slack` extra rows per segment leave room for tokens appended while decoding."""
+    `slack` extra rows per segment leave room for tokens appended while decoding;
+    `local_chunks` / `top_chunks` select the chunk-selection options (chunk mode)."""
     import torch
     B, hq, hkv, d, n = cfg.batch, cfg.hq, cfg.hkv, cfg.d, cfg.n
     shape = K.make_shape(B, hq, hkv, d, n, cfg.dtype, cfg.scale)
@@ -152,11 +160,14 @@ def build_layer(cfg, inputs: dict, *, budget=None, slack: int = 0, device="cuda"
         mode = K.KVSEL_SEL_CHUNK
         ends = np.asarray(inputs["chunk_end"], np.int64)
         nc = ends.shape[1]
-        lens = np.diff(np.concatenate([[0], ends[0]]))
-        cap = capacities(mode, B, hkv, n, keep_tokens=cfg.keep_tokens, max_chunk=int(lens.max()))
+        cap = capacities(mode, B, hkv, n, keep_tokens=cfg.keep_tokens,
+                         max_chunk=int(np.diff(np.concatenate([np.zeros((B, 1), np.int64), ends],
+                                                              axis=1)).max()),
+                         local_chunks=local_chunks, top_chunks=top_chunks)
         et = device_tensor(ends, device)
         keep.append(et)
-        params = K.select_params(mode, n_chunks=nc, chunk_end=et, keep_tokens=cfg.keep_tokens)
+        params = K.select_params(mode, n_chunks=nc, chunk_end=et, keep_tokens=cfg.keep_tokens,
+                                 local_chunks=local_chunks, top_chunks=top_chunks)
         sshape = K.make_shape(B, hq, hkv, cfg.chunk_dim, nc, cfg.dtype, cfg.scale)
         run = LayerRun(shape, k, v, qd, mode, 0, None, w=1, q_pos0=nc - 1,
                        q_win=device_tensor(inputs["chunk_q"], device), score_shape=sshape,

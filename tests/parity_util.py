@@ -58,14 +58,17 @@ def check_topb_selection(idx_gpu: np.ndarray, s_gpu: np.ndarray, s_ref: np.ndarr
         assert out.size == 0, f"{what}: {out.size} selections differ outside the tie band"
 
 
-def check_chunk_selection(idx_gpu, cs_gpu, cs_ref, ends, keep, what):
-    want = oracle.select_chunks(cs_gpu.astype(np.float64), ends, keep)
+def check_chunk_selection(idx_gpu, cs_gpu, cs_ref, ends, keep, what, local=0, top=0):
+    want = oracle.select_chunks(cs_gpu.astype(np.float64), ends, keep, local, top)
     assert np.array_equal(idx_gpu, want), f"{what}: chunk select differs on GPU scores"
-    ref = oracle.select_chunks(cs_ref, ends, keep)
+    ref = oracle.select_chunks(cs_ref, ends, keep, local, top)
     if np.array_equal(ref, idx_gpu):
         return
     chunk_of = lambda toks: set(np.searchsorted(ends, toks, side="right").tolist())
-    cg, cr = chunk_of(idx_gpu), chunk_of(ref)
+    nc = len(ends)
+    forced = set(range(nc - min(local, nc), nc))
+    cg, cr = chunk_of(idx_gpu) - forced, chunk_of(ref) - forced
+    assert cr, f"{what}: selections differ with only forced chunks kept"
     last = max(cr, key=lambda c: (-cs_ref[c], c))
     band = TIE_BAND * abs(cs_ref[last])
     for c in cg ^ cr:

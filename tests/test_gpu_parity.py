@@ -52,7 +52,7 @@ def _host(run):
     return h
 
 
-def _check_segments(cfg, inputs, run, segs, budgets=None, layer=0):
+def _check_segments(cfg, inputs, run, segs, budgets=None, layer=0, local=0, top=0):
     h = _host(run)
     G, w, d = cfg.G, cfg.w, cfg.d
     stats = {"score_rel": 0.0, "out_abs": 0.0}
@@ -79,7 +79,7 @@ def _check_segments(cfg, inputs, run, segs, budgets=None, layer=0):
                                           oracle.to_f64(inputs["chunk_keys"][b, kvh]), cfg.scale,
                                           nc - 1)
             stats["score_rel"] = max(stats["score_rel"], pu.check_scores(cs_gpu, cs_ref, G, what))
-            pu.check_chunk_selection(idx, cs_gpu, cs_ref, ends, cfg.keep_tokens, what)
+            pu.check_chunk_selection(idx, cs_gpu, cs_ref, ends, cfg.keep_tokens, what, local, top)
         else:
             want = oracle.select_policy(int(inputs["head_kind"][kvh]), cfg.n, cfg.local_window,
                                         inputs["special_pos"][b])
@@ -159,6 +159,20 @@ def test_c4_reduced(kv):
     _check_segments(cfg, inputs, run, range(cfg.batch * cfg.hkv))
 
 
+@pytest.mark.parametrize("local,top,keep_frac", [(16, 256, 0.48), (15, 0, 0.45)])
+def test_c4_chunk_operating_points(kv, local, top, keep_frac):
+    """ChunkLLM's two operating points on a reduced C4 layer: 16 forced local
+    chunks + the 256 best others; 15 local chunks + a 45 % token target."""
+    kvsel, pipeline, torch = kv
+    cfg = kvsynth.get_config(4, n=20000 + 3, keep_frac=keep_frac)
+    _say(cfg.name, "reduced, local", local, "top", top, "keep", cfg.keep_tokens)
+    inputs = kvsynth.layer_inputs(cfg, 0)
+    run = pipeline.build_layer(cfg, inputs, local_chunks=local, top_chunks=top)
+    run.run()
+    torch.cuda.synchronize()
+    _check_segments(cfg, inputs, run, range(cfg.batch * cfg.hkv), local=local, top=top)
+
+
 def test_c4_full_sampled(kv):
     cfg = kvsynth.get_config(4)
     _say(cfg.name, "full")
@@ -236,24 +250,28 @@ def test_select_chunk_exact(kv):
     nc = ends.size
     hkv = 3
     cs = np.stack([r.random(nc), r.integers(0, 3, nc), np.full(nc, 1.0)]).astype(np.float32)
-    for keep in [1, 777, 2400, n, n + 10, 0]:
+    cases = [(keep, 0, 0) for keep in [1, 777, 2400, n, n + 10, 0]]
+    cases += [(777, 5, 0), (0, 16, 0), (n, 3, 0), (0, 16, 50), (0, 0, 1), (0, 3, nc), (0, nc + 4, 2)]
+    for keep, local, top in cases:
         shape = kvsel.make_shape(1, hkv, hkv, 64, n, "bf16", 1.0)
         maxc = int(np.diff(np.concatenate([[0], ends])).max())
-        cap = pipeline.capacities(kvsel.KVSEL_SEL_CHUNK, 1, hkv, n, keep_tokens=keep, max_chunk=maxc)
+        cap = pipeline.capacities(kvsel.KVSEL_SEL_CHUNK, 1, hkv, n, keep_tokens=keep, max_chunk=maxc,
+                                  local_chunks=local, top_chunks=top)
         off, r_cap = pipeline.offsets(cap)
         et = pipeline.device_tensor(ends[None, :].astype(np.int64))
         st = pipeline.device_tensor(cs.ravel())
         ot = pipeline.device_tensor(off)
         lt = torch.empty(hkv, dtype=torch.int32, device="cuda")
         it = torch.full((max(r_cap, 1),), -7, dtype=torch.int32, device="cuda")
-        p = kvsel.select_params(kvsel.KVSEL_SEL_CHUNK, n_chunks=nc, chunk_end=et, keep_tokens=keep)
+        p = kvsel.select_params(kvsel.KVSEL_SEL_CHUNK, n_chunks=nc, chunk_end=et, keep_tokens=keep,
+                                local_chunks=local, top_chunks=top)
         kvsel.kvsel_select(shape, p, st, ot, lt, it, r_cap)
         torch.cuda.synchronize()
         ln, ix = pu.to_host(lt), pu.to_host(it)
         for s in range(hkv):
-            want = oracle.select_chunks(cs[s].astype(np.float64), ends, keep)
-            assert ln[s] == want.size, (keep, s)
-            assert np.array_equal(ix[off[s]:off[s] + ln[s]], want), (keep, s)
+            want = oracle.select_chunks(cs[s].astype(np.float64), ends, keep, local, top)
+            assert ln[s] == want.size, (keep, local, top, s)
+            assert np.array_equal(ix[off[s]:off[s] + ln[s]], want), (keep, local, top, s)
 
 
 def test_compact_gaps_empty_and_bad_indices(kv):
