@@ -42,7 +42,8 @@ __all__ = [
     "to_f64", "softmax", "window_scores", "lmba_row", "layer_lmba",
     "zigzag_budgets", "score_order", "select_topb", "select_chunks",
     "select_policy", "compact", "decode_attention", "decode_partial",
-    "combine_partials", "append_token", "HEAD_GLOBAL", "HEAD_LOCAL", "HEAD_SPECIAL",
+    "combine_partials", "append_token", "window_probabilities", "attention_loss",
+    "HEAD_GLOBAL", "HEAD_LOCAL", "HEAD_SPECIAL",
 ]
 
 HEAD_GLOBAL, HEAD_LOCAL, HEAD_SPECIAL = 0, 1, 2
@@ -93,6 +94,33 @@ def window_scores(q_win: np.ndarray, k: np.ndarray, scale: float, q_pos0: int) -
             row = np.where(pos <= q_pos0 + i, logits[i], -np.inf)
             s += softmax(row)
     return s
+
+
+def window_probabilities(q_win: np.ndarray, k: np.ndarray, scale: float, q_pos0: int) -> np.ndarray:
+    """The attention rows behind window_scores: P [G*w][n], row h*w + i is the
+    softmax of window query i of head h over the keys it sees (j <= q_pos0 + i,
+    zero elsewhere) [ZZ Eq. 1 / Eq. 7]."""
+    q_win = np.asarray(q_win, np.float64)
+    k = np.asarray(k, np.float64)
+    G, w, _ = q_win.shape
+    n = k.shape[0]
+    pos = np.arange(n)
+    P = np.zeros((G * w, n))
+    for h in range(G):
+        logits = scale * (q_win[h] @ k.T)
+        for i in range(w):
+            P[h * w + i] = softmax(np.where(pos <= q_pos0 + i, logits[i], -np.inf))
+    return P
+
+
+def attention_loss(P: np.ndarray, kept, mass: float = 0.9) -> np.ndarray:
+    """Per-row attention loss of a kept token set [ZZ §5.5, Table 3: the
+    deviation from keeping 0.9 of the attention]: max(0, mass - sum of the
+    row's weights on the kept tokens).  The reported figure is the mean."""
+    P = np.asarray(P, np.float64)
+    kept = np.asarray(kept, np.int64)
+    got = P[:, kept].sum(axis=1) if kept.size else np.zeros(P.shape[0])
+    return np.maximum(0.0, mass - got)
 
 
 # ---------------------------------------------------------------------------

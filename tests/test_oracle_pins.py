@@ -457,3 +457,40 @@ def test_chunk_local_zero_matches_plain():
     for target in (0, 1, 17, int(ends[-1])):
         assert np.array_equal(oracle.select_chunks(cs, ends, target),
                               oracle.select_chunks(cs, ends, target, local_chunks=0, top_chunks=0))
+
+
+# ---------------------------------------------------------------------------
+# attention rows, LMBA on them, attention loss (ZigZagkv Eq. 3, §5.5 Table 3)
+# ---------------------------------------------------------------------------
+
+def test_window_probabilities_rows_and_mask():
+    r = np.random.default_rng(31)
+    G, w, n, d, q0 = 2, 3, 40, 8, 30
+    q, k = r.standard_normal((G, w, d)), r.standard_normal((n, d))
+    P = oracle.window_probabilities(q, k, 0.3, q0)
+    assert P.shape == (G * w, n)
+    assert np.allclose(P.sum(axis=1), 1.0, atol=1e-13)
+    for h in range(G):
+        for i in range(w):
+            assert np.all(P[h * w + i, q0 + i + 1:] == 0.0)          # causal
+            assert np.all(P[h * w + i, :q0 + i + 1] > 0.0)
+
+
+def test_lmba_zero_query_is_ceil_nine_tenths_of_visible():
+    n, w, q0 = 53, 4, 40
+    P = oracle.window_probabilities(np.zeros((1, w, 8)), np.ones((n, 8)), 1.0, q0)
+    for i in range(w):
+        vis = q0 + i + 1
+        assert oracle.lmba_row(P[i]) == math.ceil(0.9 * vis)
+
+
+def test_attention_loss_closed_forms():
+    # two keys, logits a and 0: p = logistic(a); keeping key 0 loses max(0, 0.9 - p)
+    for a in (-1.0, 0.5, 2.0, 4.0):
+        q = np.array([[[a]]])
+        k = np.array([[1.0], [0.0]])
+        P = oracle.window_probabilities(q, k, 1.0, 1)
+        p0 = 1.0 / (1.0 + math.exp(-a))
+        assert abs(oracle.attention_loss(P, [0])[0] - max(0.0, 0.9 - p0)) < 1e-15
+        assert oracle.attention_loss(P, [0, 1])[0] == 0.0
+        assert abs(oracle.attention_loss(P, [])[0] - 0.9) < 1e-15
