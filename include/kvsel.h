@@ -7,6 +7,8 @@
  * "segment" s = b * hkv + kvh):
  *
  *   kvsel_score        window-mass score of every cached key
+ *   kvsel_lmba         per-row 90 %-mass minimum budget (layer uncertainty)
+ *                      and the attention a selection keeps
  *   kvsel_select       keep tokens per segment (top-B, chunk top-k or head policy)
  *   kvsel_compact      gather kept K/V rows into a packed variable-length cache
  *   kvsel_decode_attn  single-token GQA decode attention over that cache
@@ -98,6 +100,29 @@ size_t kvsel_score_workspace(const kvsel_shape* s /*host*/, int32_t w);
 kvsel_status kvsel_score(const kvsel_shape* s /*host*/, int32_t w, int64_t q_pos0,
                          const void* q_win, const void* k, float* scores,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------- lmba --
+ * Layer uncertainty (ZigZagkv page, Eq. 3) and attention kept by a selection
+ * (the page's §5.5 / Table 3 attention loss is max(0, 0.9 - kept)).  For
+ * every attention row of the window queries -- row g*w + i of segment s is
+ * window query i of query head kvh*G + g, causal as in kvsel_score --
+ *   lmba[s][row]  = smallest k such that the k largest attention weights of
+ *                   the row reach 90 % of its mass (weights taken in fixed
+ *                   point, floor(p * 2^40), so the count is exact for them);
+ *   kept_mass[s][row] = sum of the row's weights on idx[seg_off[s] ..
+ *                   seg_off[s] + seg_len[s]) (optional: NULL skips it).
+ * A layer's LMBA, the ZigZagkv uncertainty, is the mean of lmba over rows.
+ *   lmba       [batch][hkv][G*w] int32 (out)
+ *   kept_mass  [batch][hkv][G*w] fp32 (out) or NULL; then seg_off, seg_len
+ *              and idx may be NULL
+ *   ws         at least kvsel_lmba_workspace(s, w) bytes (it holds the
+ *              attention rows: batch*hkv*G*w*n floats)
+ * Constraints as for kvsel_score. */
+size_t kvsel_lmba_workspace(const kvsel_shape* s /*host*/, int32_t w);
+kvsel_status kvsel_lmba(const kvsel_shape* s /*host*/, int32_t w, int64_t q_pos0,
+                        const void* q_win, const void* k, int32_t* lmba, const int64_t* seg_off,
+                        const int32_t* seg_len, const int32_t* idx, int64_t r_cap,
+                        float* kept_mass, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* --------------------------------------------------------------- select --
  * Writes, per segment s, the kept token positions in ascending order to

@@ -20,6 +20,8 @@ from ._lib import (  # noqa: F401
     kvsel_decode_attn,
     kvsel_decode_workspace,
     kvsel_last_error,
+    kvsel_lmba,
+    kvsel_lmba_workspace,
     kvsel_score,
     kvsel_score_workspace,
     kvsel_select,

@@ -62,6 +62,12 @@ _SIGS = {
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]),
+    "kvsel_lmba_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32]),
+    "kvsel_lmba": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_size_t, ctypes.c_void_p]),
     "kvsel_append": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -158,6 +164,18 @@ def kvsel_decode_attn(shape: Shape, q, k_c, v_c, seg_off, seg_len, r_cap: int, o
     _check(lib().kvsel_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k_c), _ptr(v_c),
                                    _ptr(seg_off), _ptr(seg_len), int(r_cap), _ptr(out), _ptr(ws),
                                    nbytes, _stream(stream)), "kvsel_decode_attn")
+
+
+def kvsel_lmba_workspace(shape: Shape, w: int) -> int:
+    return int(lib().kvsel_lmba_workspace(ctypes.byref(shape), int(w)))
+
+
+def kvsel_lmba(shape: Shape, w: int, q_pos0: int, q_win, k, lmba, ws, seg_off=None, seg_len=None,
+               idx=None, r_cap: int = 0, kept_mass=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().kvsel_lmba(ctypes.byref(shape), int(w), int(q_pos0), _ptr(q_win), _ptr(k),
+                            _ptr(lmba), _ptr(seg_off), _ptr(seg_len), _ptr(idx), int(r_cap),
+                            _ptr(kept_mass), _ptr(ws), nbytes, _stream(stream)), "kvsel_lmba")
 
 
 def kvsel_append(shape: Shape, k_new, v_new, pos: int, seg_off, seg_cap, limit, seg_len, idx,

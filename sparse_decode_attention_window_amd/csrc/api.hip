@@ -130,6 +130,49 @@ kvsel_status kvsel_score(const kvsel_shape* s, int32_t w, int64_t q_pos0, const 
                     "kvsel_score launch");
 }
 
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t kvsel_lmba_workspace(const kvsel_shape* s, int32_t w) {
+  if (!s || w < 1 || s->batch < 1 || s->hkv < 1 || s->hq < s->hkv || s->n < 1) return 0;
+  const size_t S = (size_t)s->batch * s->hkv, R = (size_t)(s->hq / s->hkv) * w;
+  return align256(score_workspace_bytes((int)S, s->n, (int)R)) + S * R * (size_t)s->n * 4;
+}
+
+kvsel_status kvsel_lmba(const kvsel_shape* s, int32_t w, int64_t q_pos0, const void* q_win,
+                        const void* k, int32_t* lmba, const int64_t* seg_off,
+                        const int32_t* seg_len, const int32_t* idx, int64_t r_cap,
+                        float* kept_mass, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  int S = 0, G = 0;
+  kvsel_status st = check_shape(s, &S, &G, 256);
+  if (st != KVSEL_OK) return st;
+  if (w < 1) return fail(KVSEL_EINVAL, "w must be >= 1 (got %d)", w);
+  if ((long long)G * w > 256)
+    return fail(KVSEL_EUNSUPPORTED, "G*w = %lld query rows exceeds 256", (long long)G * w);
+  if (q_pos0 < 0) return fail(KVSEL_EINVAL, "q_pos0 must be >= 0");
+  if (!q_win || !k || !lmba) return fail(KVSEL_EINVAL, "q_win, k and lmba must be non-NULL");
+  if (kept_mass && (!seg_off || !seg_len || !idx))
+    return fail(KVSEL_EINVAL, "kept_mass needs seg_off, seg_len and idx");
+  if (r_cap < 0 || r_cap > 0x7fffffffLL) return fail(KVSEL_EINVAL, "r_cap must be in [0, 2^31)");
+  if (S > 65535) return fail(KVSEL_EUNSUPPORTED, "too many segments for the grid");
+  int RP = 32;
+  while (RP < G * w) RP *= 2;
+  const size_t lds = (size_t)RP * (s->head_dim * elem_size(s) + 16);
+  if (lds + 8192 > (size_t)device_info().max_lds)
+    return fail(KVSEL_EUNSUPPORTED, "query block of %zu bytes does not fit in LDS", lds);
+  const size_t need = kvsel_lmba_workspace(s, w);
+  if (ws_bytes < need || !ws)
+    return fail(KVSEL_ENOSPC, "lmba workspace needs %zu bytes, got %zu", need, ws_bytes);
+  const int R = G * w;
+  char* base = static_cast<char*>(ws);
+  float* probs = reinterpret_cast<float*>(base + align256(score_workspace_bytes(S, s->n, R)));
+  hipError_t e = launch_probs(s->dtype, s->head_dim, s->batch, s->hq, s->hkv, w, s->n, q_pos0,
+                              s->scale, q_win, k, probs, ws, stream);
+  if (e == hipSuccess)
+    e = launch_lmba_rows(probs, S, R, s->n, lmba, seg_off, seg_len, idx, r_cap, kept_mass, stream);
+  return hip_status(e, "kvsel_lmba launch");
+}
+
 kvsel_status kvsel_select(const kvsel_shape* s, const kvsel_select_params* p, const float* scores,
                           const int64_t* seg_off, int32_t* seg_len, int32_t* idx, int64_t r_cap,
                           hipStream_t stream) {

@@ -257,4 +257,16 @@ hipError_t launch_score(int dtype, int head_dim, int batch, int hq, int hkv, int
                         int64_t n, int64_t q_pos0, float scale, const void* q_win,
                         const void* k, float* scores, void* ws, hipStream_t stream);
 
+// Attention rows of the window queries, probs [S][G*w][n] fp32 (same passes as
+// launch_score; the score workspace holds the row statistics).
+hipError_t launch_probs(int dtype, int head_dim, int batch, int hq, int hkv, int w, int64_t n,
+                        int64_t q_pos0, float scale, const void* q_win, const void* k,
+                        float* probs, void* ws, hipStream_t stream);
+
+// Per attention row: the 90 %-mass minimum token count, and optionally the
+// mass on a selection (seg_off / seg_len / idx) of the row's segment.
+hipError_t launch_lmba_rows(const float* probs, int S, int R, int64_t n, int32_t* lmba,
+                            const int64_t* seg_off, const int32_t* seg_len, const int32_t* idx,
+                            int64_t r_cap, float* kept_mass, hipStream_t stream);
+
 }  // namespace kvsel

@@ -247,7 +247,10 @@ __global__ __launch_bounds__(kReduceThreads) void score_reduce_kernel(
   }
 }
 
-template <typename T, int D, int RBN>
+// PROBS = false: per key, the sum over rows of 2^(x - K_r) (the scores).
+// PROBS = true: every row's probabilities, probs[s][r][key] for r < R (the
+// attention rows behind the scores, for the LMBA and attention-mass kernels).
+template <typename T, int D, int RBN, bool PROBS = false>
 __global__ __launch_bounds__(kThreads) void score_final_kernel(
     const char* __restrict__ qw, const char* __restrict__ k, int64_t n, int hq, int hkv, int G,
     int w, int R, int64_t q_pos0, float c, const float* __restrict__ rowc,
@@ -293,12 +296,18 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
         for (int e = 0; e < 4; ++e) {
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g4 * 4 + e], c, -kk[e]));
           if (MASKED && (int)key > lim[r0 + e]) p = 0.f;
-          ssum += p;
+          if (PROBS) {
+            if (r0 + e < R && key < n) scores[((int64_t)s * R + r0 + e) * n + key] = p;
+          } else {
+            ssum += p;
+          }
         }
       }
     }
-    ssum += __shfl_xor(ssum, 32);
-    if (half == 0 && key < n) scores[(int64_t)s * n + key] = ssum;
+    if (!PROBS) {
+      ssum += __shfl_xor(ssum, 32);
+      if (half == 0 && key < n) scores[(int64_t)s * n + key] = ssum;
+    }
   };
   for_each_key_block<T, D>(kseg, tile0, wid, n, lane, [&](const u32x4* kf, int64_t key0) {
     if (key0 + 31 >= n || key0 + 31 > q_pos0) block(kf, key0, std::true_type{});
@@ -306,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
   });
 }
 
-template <typename T, int D, int RBN>
+template <typename T, int D, int RBN, bool PROBS = false>
 hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int64_t q_pos0,
                     float c, const char* qp, const char* kp, float* scores, float2* stats,
                     float* rowc, int tiles, hipStream_t stream) {
@@ -316,7 +325,7 @@ hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int6
     hipError_t e = hipFuncSetAttribute((const void*)score_stats_kernel<T, D, RBN>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)score_final_kernel<T, D, RBN>,
+    e = hipFuncSetAttribute((const void*)score_final_kernel<T, D, RBN, PROBS>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
@@ -324,12 +333,12 @@ hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int6
   score_stats_kernel<T, D, RBN><<<grid, dim3(kThreads), lds, stream>>>(
       qp, kp, n, hq, hkv, G, w, R, q_pos0, c, stats, tiles);
   score_reduce_kernel<<<dim3(S), dim3(kReduceThreads), 0, stream>>>(stats, tiles, R, rowc);
-  score_final_kernel<T, D, RBN><<<grid, dim3(kThreads), lds, stream>>>(
+  score_final_kernel<T, D, RBN, PROBS><<<grid, dim3(kThreads), lds, stream>>>(
       qp, kp, n, hq, hkv, G, w, R, q_pos0, c, rowc, scores);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PROBS = false>
 hipError_t run(int batch, int hq, int hkv, int w, int64_t n, int64_t q_pos0, float scale,
                const void* q_win, const void* k, float* scores, void* ws, hipStream_t stream) {
   const int S = batch * hkv, G = hq / hkv, R = G * w;
@@ -341,8 +350,8 @@ hipError_t run(int batch, int hq, int hkv, int w, int64_t n, int64_t q_pos0, flo
   auto qp = static_cast<const char*>(q_win);
   auto kp = static_cast<const char*>(k);
 #define KVSEL_ROWS(RBN) \
-  return run_rows<T, D, RBN>(S, hq, hkv, G, w, R, n, q_pos0, c, qp, kp, scores, stats, rowc, \
-                             tiles, stream)
+  return run_rows<T, D, RBN, PROBS>(S, hq, hkv, G, w, R, n, q_pos0, c, qp, kp, scores, stats, \
+                                    rowc, tiles, stream)
   switch (RP / 32) {
     case 1: KVSEL_ROWS(1);
     case 2: KVSEL_ROWS(2);
@@ -358,6 +367,24 @@ size_t score_workspace_bytes(int S, int64_t n, int rows) {
   const int RP = padded_rows(rows);
   const int64_t tiles = (n + kTileKeys - 1) / kTileKeys;
   return (size_t)S * tiles * RP * sizeof(float2) + (size_t)S * RP * sizeof(float);
+}
+
+hipError_t launch_probs(int dtype, int head_dim, int batch, int hq, int hkv, int w, int64_t n,
+                        int64_t q_pos0, float scale, const void* q_win, const void* k,
+                        float* probs, void* ws, hipStream_t stream) {
+#define KVSEL_PR(T, D) \
+  return run<T, D, true>(batch, hq, hkv, w, n, q_pos0, scale, q_win, k, probs, ws, stream)
+  if (dtype == 1) {
+    if (head_dim == 64) KVSEL_PR(bf16_t, 64);
+    if (head_dim == 88) KVSEL_PR(bf16_t, 88);
+    if (head_dim == 128) KVSEL_PR(bf16_t, 128);
+  } else {
+    if (head_dim == 64) KVSEL_PR(float, 64);
+    if (head_dim == 88) KVSEL_PR(float, 88);
+    if (head_dim == 128) KVSEL_PR(float, 128);
+  }
+#undef KVSEL_PR
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_score(int dtype, int head_dim, int batch, int hq, int hkv, int w, int64_t n,

@@ -90,3 +90,15 @@ def check_decode(out_gpu, q_dec, K, V, idx, scale, dtype, what) -> float:
         err = max(err, float(np.max(np.abs(out_gpu[g].astype(np.float64) - ref))) if ref.size else 0)
     assert err <= OUT_ATOL[dtype], f"{what}: decode max-abs error {err}"
     return err
+
+
+def check_lmba(k_gpu, P_rows, what, eps=1e-5):
+    """GPU per-row LMBA against float64 attention rows: the count must lie in
+    the band of counts whose top-k mass reaches 0.9 of the row within a
+    relative eps (fp32 rows and fixed-point masses on the GPU)."""
+    for r, row in enumerate(np.asarray(P_rows)):
+        cum = np.cumsum(np.sort(row)[::-1])
+        tot = cum[-1]
+        lo = int(np.searchsorted(cum, 0.9 * (1 - eps) * tot)) + 1
+        hi = int(np.searchsorted(cum, 0.9 * (1 + eps) * tot)) + 1
+        assert lo <= int(k_gpu[r]) <= hi, f"{what} row {r}: lmba {k_gpu[r]} outside [{lo}, {hi}]"

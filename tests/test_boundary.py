@@ -106,6 +106,23 @@ def test_compact_and_decode_reject_bad_args():
                                  FAKE, 1 << 30, None) == _lib.KVSEL_EUNSUPPORTED
 
 
+def test_lmba_rejects_bad_args():
+    sh = shape()
+    lib = kvsel.lib()
+    need = kvsel.kvsel_lmba_workspace(sh, 8)
+    assert need >= 2 * (2 * 8) * 512 * 4       # holds the fp32 attention rows
+
+    def lm(w=8, q_pos0=0, out=FAKE, km=None, off=None, ws_bytes=1 << 40):
+        return lib.kvsel_lmba(ctypes.byref(sh), w, q_pos0, FAKE, FAKE, out, off, None, None, 0,
+                              km, FAKE, ws_bytes, None)
+    assert lm(w=0) == _lib.KVSEL_EINVAL
+    assert lm(w=200) == _lib.KVSEL_EUNSUPPORTED
+    assert lm(q_pos0=-1) == _lib.KVSEL_EINVAL
+    assert lm(out=None) == _lib.KVSEL_EINVAL
+    assert lm(km=FAKE) == _lib.KVSEL_EINVAL        # kept mass without a selection
+    assert lm(ws_bytes=need - 1) == _lib.KVSEL_ENOSPC
+
+
 def test_append_rejects_bad_args():
     sh = shape()
     lib = kvsel.lib()

@@ -544,3 +544,67 @@ def test_c3_decode_loop_with_append(kv):
                 worst = max(worst, err)
                 assert err <= pu.OUT_ATOL[cfg.dtype], f"step {t} seg {s} head {g}: err {err}"
     print(f"  decode loop: max abs err {worst:.2e}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# LMBA and kept attention (ZigZagkv Eq. 3, §5.5 Table 3)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d,G,w,n,q_pos0", [("fp32", 64, 2, 8, 512, 504),
+                                                 ("bf16", 128, 4, 32, 3001, 2969),
+                                                 ("bf16", 88, 4, 5, 700, 10)])
+def test_lmba_uniform_rows_exact(kv, dtype, d, G, w, n, q_pos0):
+    """Zero queries give uniform rows over the visible keys: LMBA is exactly
+    ceil(0.9 * visible) for every row."""
+    kvsel, pipeline, torch = kv
+    _say("lmba uniform", dtype, d, G, w, n, q_pos0)
+    B, hkv = 2, 2
+    sdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    shape = kvsel.make_shape(B, G * hkv, hkv, d, n, dtype, 1 / math.sqrt(d))
+    q = torch.zeros(B, G * hkv, w, d, dtype=sdt, device="cuda")
+    k = torch.randn(B, hkv, n, d, device="cuda").to(sdt)
+    lm = torch.empty(B * hkv * G * w, dtype=torch.int32, device="cuda")
+    ws = torch.empty(kvsel.kvsel_lmba_workspace(shape, w), dtype=torch.uint8, device="cuda")
+    kvsel.kvsel_lmba(shape, w, q_pos0, q, k, lm, ws)
+    torch.cuda.synchronize()
+    got = pu.to_host(lm).reshape(B * hkv, G * w)
+    for s in range(B * hkv):
+        for r in range(G * w):
+            vis = min(q_pos0 + r % w, n - 1) + 1
+            assert got[s, r] == math.ceil(0.9 * vis - 1e-12), (s, r, got[s, r], vis)
+
+
+@pytest.mark.parametrize("cid", [0, 1])
+def test_lmba_and_kept_mass_match_oracle(kv, cid):
+    """Per-row LMBA within the float64 band, and the attention the pipeline's
+    top-B selection keeps per row within 1e-5, on whole C0 / C1 layers."""
+    kvsel, pipeline, torch = kv
+    cfg = kvsynth.get_config(cid)
+    _say(cfg.name, "lmba + kept mass")
+    inputs, run = _run(kv, cfg)
+    R, S = cfg.G * cfg.w, cfg.batch * cfg.hkv
+    lm = torch.empty(S * R, dtype=torch.int32, device="cuda")
+    km = torch.empty(S * R, dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvsel.kvsel_lmba_workspace(run.shape, cfg.w), dtype=torch.uint8, device="cuda")
+    kvsel.kvsel_lmba(run.shape, cfg.w, cfg.n - cfg.w, run.q_win, run.k, lm, ws, run.seg_off,
+                     run.seg_len, run.idx, run.r_cap, km)
+    torch.cuda.synchronize()
+    got_k = pu.to_host(lm).reshape(S, R)
+    got_m = pu.to_host(km).reshape(S, R)
+    h = _host(run)
+    worst = 0.0
+    for s in range(S):
+        b, kvh = divmod(s, cfg.hkv)
+        P = oracle.window_probabilities(oracle.to_f64(inputs["q_win"][b, kvh * cfg.G:(kvh + 1) * cfg.G]),
+                                        oracle.to_f64(inputs["K"][b, kvh]), cfg.scale, cfg.n - cfg.w)
+        pu.check_lmba(got_k[s], P, f"{cfg.name} seg {s}")
+        off, ln = int(h["seg_off"][s]), int(h["seg_len"][s])
+        kept = h["idx"][off:off + ln].astype(np.int64)
+        want = 0.9 - oracle.attention_loss(P, kept)      # kept mass where below 0.9
+        ref_mass = P[:, kept].sum(axis=1)
+        err = float(np.max(np.abs(got_m[s] - ref_mass)))
+        worst = max(worst, err)
+        assert err <= 1e-5, f"{cfg.name} seg {s}: kept mass err {err}"
+        assert np.all(np.minimum(got_m[s], 0.9) <= want + 1e-5)
+    print(f"  {cfg.name}: layer LMBA {got_k.mean():.1f} of n={cfg.n}, kept-mass err {worst:.1e}, "
+          f"mean attention loss {np.maximum(0, 0.9 - got_m).mean():.4f}", flush=True)
