@@ -256,6 +256,38 @@ def main() -> int:
     wall = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {wall:.3f} s")
 
+    # calibration extra, outside the timed steps: per-row LMBA of every layer
+    # (ZigZagkv Eq. 3) and the attention the layer's top-B selection keeps
+    # (Table 3's attention loss is max(0, 0.9 - kept)); one workspace serves
+    # every layer since the launches are ordered on one stream
+    R, B_S = cfg.G * cfg.w, cfg.batch * cfg.hkv
+    lm_ws = torch.empty(kvsel.kvsel_lmba_workspace(layers[0].shape, cfg.w), dtype=torch.uint8,
+                        device="cuda")
+    lm = torch.empty(L, B_S * R, dtype=torch.int32, device="cuda")
+    km = torch.empty(L, B_S * R, dtype=torch.float32, device="cuda")
+
+    def lmba_all():
+        for l, run in enumerate(layers):
+            kvsel.kvsel_lmba(run.shape, cfg.w, cfg.n - cfg.w, run.q_win, run.k, lm[l], lm_ws,
+                             run.seg_off, run.seg_len, run.idx, run.r_cap, km[l])
+    lmba_all()
+    torch.cuda.synchronize()
+    g_lm = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_lm):
+        lmba_all()
+    l_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    l_ev[0].record()
+    for _ in range(2):
+        g_lm.replay()
+    l_ev[1].record()
+    torch.cuda.synchronize()
+    lmba_us = l_ev[0].elapsed_time(l_ev[1]) / (2 * L) * 1e3
+    layer_lmba = lm.float().mean(dim=1).cpu().tolist()
+    att_loss = (0.9 - km).clamp_min(0).mean(dim=1).cpu().tolist()
+    del lm_ws
+    log(f"[bench] LMBA + kept mass: {lmba_us:.1f} us per layer; mean LMBA "
+        f"{sum(layer_lmba) / L:.0f} tokens, mean attention loss {sum(att_loss) / L:.4f}")
+
     # serving-loop extra, outside the timed steps: one decoded token joins
     # every segment of every layer (segments are full, so each append
     # replaces the oldest token: the sliding-window path)
@@ -335,7 +367,14 @@ def main() -> int:
         "extras": {"append_us_per_layer": round(append_us, 3),
                    "append_note": "kvsel_append of one decoded token into all 32 full "
                                   "segments of a layer (oldest-token replacement), "
-                                  "outside the timed step"},
+                                  "outside the timed step",
+                   "lmba_us_per_layer": round(lmba_us, 1),
+                   "lmba_note": "kvsel_lmba over the 128 window-attention rows of each of the "
+                                "32 segments of a layer (rows materialised, 90 %-mass radix "
+                                "select per row, kept mass of the top-B selection), outside "
+                                "the timed step",
+                   "layer_lmba_mean_tokens": [round(x, 1) for x in layer_lmba],
+                   "attention_loss_topb_per_layer": [round(x, 5) for x in att_loss]},
         "decode_frac_of_copy_reference": round(dec_gbs / copy_gbs, 4),
         "compact_frac_of_copy_reference": round(gbs(cmp_bytes, us["compact"]) / copy_gbs, 4),
         "stages_roofline": {

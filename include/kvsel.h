@@ -17,8 +17,9 @@
  *
  * Sources, cited by page title and the equation / section on it:
  *   ZigZagkv: Dynamic KV Cache Compression for Long-context Modeling based on
- *     Layer Uncertainty (arXiv 2412.09036): Eq. 7 token score, Eq. 4 and
- *     Eq. 6 bounded layer budgets.
+ *     Layer Uncertainty (arXiv 2412.09036): Eq. 7 token score, Eq. 3 minimum
+ *     budget for 90 % of the attention (LMBA), §5.5 / Table 3 attention loss,
+ *     Eq. 4 and Eq. 6 bounded layer budgets.
  *   Model Tells You What to Discard: Adaptive KV Cache Compression for LLMs
  *     (arXiv 2310.01801): local / special-token / global head policies.
  *   ChunkLLM: A Lightweight Pluggable Framework for Accelerating LLMs
@@ -109,15 +110,20 @@ kvsel_status kvsel_score(const kvsel_shape* s /*host*/, int32_t w, int64_t q_pos
  *   lmba[s][row]  = smallest k such that the k largest attention weights of
  *                   the row reach 90 % of its mass (weights taken in fixed
  *                   point, floor(p * 2^40), so the count is exact for them);
- *   kept_mass[s][row] = sum of the row's weights on idx[seg_off[s] ..
- *                   seg_off[s] + seg_len[s]) (optional: NULL skips it).
+ *   kept_mass[s][row] = sum of the row's weights at the positions listed in
+ *                   idx[seg_off[s] .. seg_off[s] + seg_len[s]) (optional:
+ *                   NULL skips it).  The positions are taken as a set: one
+ *                   listed twice counts once, one outside [0, n) counts 0;
+ *                   the sum is taken in the same fixed point.
  * A layer's LMBA, the ZigZagkv uncertainty, is the mean of lmba over rows.
  *   lmba       [batch][hkv][G*w] int32 (out)
  *   kept_mass  [batch][hkv][G*w] fp32 (out) or NULL; then seg_off, seg_len
  *              and idx may be NULL
  *   ws         at least kvsel_lmba_workspace(s, w) bytes (it holds the
  *              attention rows: batch*hkv*G*w*n floats)
- * Constraints as for kvsel_score. */
+ * Constraints as for kvsel_score; with kept_mass, n/8 bytes of position
+ * mask plus 32 KB must fit in one workgroup's LDS (n up to about 1M on
+ * gfx950), else KVSEL_EUNSUPPORTED. */
 size_t kvsel_lmba_workspace(const kvsel_shape* s /*host*/, int32_t w);
 kvsel_status kvsel_lmba(const kvsel_shape* s /*host*/, int32_t w, int64_t q_pos0,
                         const void* q_win, const void* k, int32_t* lmba, const int64_t* seg_off,

@@ -135,7 +135,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t kvsel_lmba_workspace(const kvsel_shape* s, int32_t w) {
   if (!s || w < 1 || s->batch < 1 || s->hkv < 1 || s->hq < s->hkv || s->n < 1) return 0;
   const size_t S = (size_t)s->batch * s->hkv, R = (size_t)(s->hq / s->hkv) * w;
-  return align256(score_workspace_bytes((int)S, s->n, (int)R)) + S * R * (size_t)s->n * 4;
+  return align256(score_workspace_bytes((int)S, s->n, (int)R)) +
+         align256(S * R * (size_t)s->n * 4) + lmba_mask_bytes((int)S, s->n);
 }
 
 kvsel_status kvsel_lmba(const kvsel_shape* s, int32_t w, int64_t q_pos0, const void* q_win,
@@ -160,16 +161,23 @@ kvsel_status kvsel_lmba(const kvsel_shape* s, int32_t w, int64_t q_pos0, const v
   const size_t lds = (size_t)RP * (s->head_dim * elem_size(s) + 16);
   if (lds + 8192 > (size_t)device_info().max_lds)
     return fail(KVSEL_EUNSUPPORTED, "query block of %zu bytes does not fit in LDS", lds);
+  if (kept_mass && (size_t)((s->n + 31) / 32) * 4 + 36864 > (size_t)device_info().max_lds)
+    return fail(KVSEL_EUNSUPPORTED, "kept_mass: the %lld-bit position mask does not fit in LDS",
+                (long long)s->n);
   const size_t need = kvsel_lmba_workspace(s, w);
   if (ws_bytes < need || !ws)
     return fail(KVSEL_ENOSPC, "lmba workspace needs %zu bytes, got %zu", need, ws_bytes);
   const int R = G * w;
   char* base = static_cast<char*>(ws);
-  float* probs = reinterpret_cast<float*>(base + align256(score_workspace_bytes(S, s->n, R)));
+  const size_t probs_at = align256(score_workspace_bytes(S, s->n, R));
+  float* probs = reinterpret_cast<float*>(base + probs_at);
+  uint32_t* mask =
+      reinterpret_cast<uint32_t*>(base + probs_at + align256((size_t)S * R * s->n * 4));
   hipError_t e = launch_probs(s->dtype, s->head_dim, s->batch, s->hq, s->hkv, w, s->n, q_pos0,
                               s->scale, q_win, k, probs, ws, stream);
   if (e == hipSuccess)
-    e = launch_lmba_rows(probs, S, R, s->n, lmba, seg_off, seg_len, idx, r_cap, kept_mass, stream);
+    e = launch_lmba_rows(probs, S, R, s->n, lmba, seg_off, seg_len, idx, r_cap, kept_mass, mask,
+                         stream);
   return hip_status(e, "kvsel_lmba launch");
 }
 

@@ -267,6 +267,9 @@ hipError_t launch_probs(int dtype, int head_dim, int batch, int hq, int hkv, int
 // mass on a selection (seg_off / seg_len / idx) of the row's segment.
 hipError_t launch_lmba_rows(const float* probs, int S, int R, int64_t n, int32_t* lmba,
                             const int64_t* seg_off, const int32_t* seg_len, const int32_t* idx,
-                            int64_t r_cap, float* kept_mass, hipStream_t stream);
+                            int64_t r_cap, float* kept_mass, uint32_t* mask,
+                            hipStream_t stream);
+// bytes of the per-segment kept-position masks launch_lmba_rows needs
+size_t lmba_mask_bytes(int S, int64_t n);
 
 }  // namespace kvsel
