@@ -564,14 +564,30 @@ def test_lmba_uniform_rows_exact(kv, dtype, d, G, w, n, q_pos0):
     q = torch.zeros(B, G * hkv, w, d, dtype=sdt, device="cuda")
     k = torch.randn(B, hkv, n, d, device="cuda").to(sdt)
     lm = torch.empty(B * hkv * G * w, dtype=torch.int32, device="cuda")
+    km = torch.empty(B * hkv * G * w, dtype=torch.float32, device="cuda")
     ws = torch.empty(kvsel.kvsel_lmba_workspace(shape, w), dtype=torch.uint8, device="cuda")
+    # segment s lists positions 0 .. 37*(s+1)-1, then one of them again and two
+    # outside [0, n): the kept mass counts each listed position once
+    S = B * hkv
+    lists = [list(range(37 * (s + 1))) + [5, -1, n] for s in range(S)]
+    off = np.cumsum([0] + [len(x) for x in lists])
+    idx = pipeline.device_tensor(np.concatenate(lists).astype(np.int32))
+    seg_off = pipeline.device_tensor(off[:-1].astype(np.int64))
+    seg_len = pipeline.device_tensor(np.diff(off).astype(np.int32))
     kvsel.kvsel_lmba(shape, w, q_pos0, q, k, lm, ws)
     torch.cuda.synchronize()
-    got = pu.to_host(lm).reshape(B * hkv, G * w)
-    for s in range(B * hkv):
+    got = pu.to_host(lm).reshape(S, G * w)
+    lm.fill_(-7)
+    kvsel.kvsel_lmba(shape, w, q_pos0, q, k, lm, ws, seg_off, seg_len, idx, int(off[-1]), km)
+    torch.cuda.synchronize()
+    assert np.array_equal(pu.to_host(lm).reshape(S, G * w), got)
+    kept = pu.to_host(km).reshape(S, G * w)
+    for s in range(S):
         for r in range(G * w):
             vis = min(q_pos0 + r % w, n - 1) + 1
             assert got[s, r] == math.ceil(0.9 * vis - 1e-12), (s, r, got[s, r], vis)
+            want = min(37 * (s + 1), vis) / vis
+            assert abs(kept[s, r] - want) <= 1e-6, (s, r, kept[s, r], want)
 
 
 @pytest.mark.parametrize("cid", [0, 1])
