@@ -614,6 +614,15 @@ def test_lmba_and_kept_mass_match_oracle(kv, cid):
         P = oracle.window_probabilities(oracle.to_f64(inputs["q_win"][b, kvh * cfg.G:(kvh + 1) * cfg.G]),
                                         oracle.to_f64(inputs["K"][b, kvh]), cfg.scale, cfg.n - cfg.w)
         pu.check_lmba(got_k[s], P, f"{cfg.name} seg {s}")
+        if cid == 0:   # the exact oracle on every row: inside the band, equal when it is one value
+            for r in range(R):
+                exact = oracle.lmba_row(P[r])
+                cum = np.cumsum(np.sort(P[r])[::-1])
+                lo = int(np.searchsorted(cum, 0.9 * (1 - 1e-5) * cum[-1])) + 1
+                hi = int(np.searchsorted(cum, 0.9 * (1 + 1e-5) * cum[-1])) + 1
+                assert lo <= exact <= hi
+                if lo == hi:
+                    assert got_k[s, r] == exact, (s, r, got_k[s, r], exact)
         off, ln = int(h["seg_off"][s]), int(h["seg_len"][s])
         kept = h["idx"][off:off + ln].astype(np.int64)
         want = 0.9 - oracle.attention_loss(P, kept)      # kept mass where below 0.9
