@@ -158,6 +158,15 @@ def rope_rotate(x: np.ndarray, pos: np.ndarray) -> np.ndarray:
     return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
 
 
+def rope_table(max_pos: int, half: int = 64) -> np.ndarray:
+    """The model's RoPE table: [max_pos][half][2] float32 (cos, sin) of the
+    angle t * base^(-p / half) of rotary pair p at position t (computed in
+    float64, rounded once).  Model constants, like the weights."""
+    theta = ROPE_BASE ** (-np.arange(half, dtype=np.float64) / half)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * theta[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+
 def prune_pairs(x: np.ndarray, pairs: np.ndarray, half: int) -> np.ndarray:
     """Keep pair p as dims (p, p + half); store as [firsts | seconds]."""
     return np.concatenate([x[..., pairs], x[..., pairs + half]], axis=-1)
@@ -204,13 +213,14 @@ def segment_queries(cfg: Config, layer: int, b: int, kvh: int):
     return qwin, _store(cfg, qd)
 
 
-def step_token(cfg: Config, layer: int, b: int, kvh: int, t: int):
+def step_token(cfg: Config, layer: int, b: int, kvh: int, t: int, rotated: bool = True):
     """Decode step t of one segment: the token at position n + t.
 
     Returns (k [d], v [d], q [G][d]) in storage format: the new key and value
     drawn like the cache's bulk keys and values (no planted structure), the G
     query heads drawn like the decode query.  C3 rotates key and queries at
-    position n + t and keeps the segment's RoPE pairs.
+    position n + t and keeps the segment's RoPE pairs; with rotated=False it
+    keeps the pairs but leaves the rotation to the consumer.
     """
     G, dg = cfg.G, cfg.d_gen
     u = head_direction(cfg, layer, kvh)
@@ -222,14 +232,17 @@ def step_token(cfg: Config, layer: int, b: int, kvh: int, t: int):
         pairs = kept_pairs(cfg, layer, kvh)
         half = dg // 2
         pos = cfg.n + t
-        k = prune_pairs(rope_rotate(k[None, :], np.array([pos])), pairs, half)[0]
-        q = prune_pairs(rope_rotate(q, np.full(G, pos)), pairs, half)
+        if rotated:
+            k = rope_rotate(k[None, :], np.array([pos]))[0]
+            q = rope_rotate(q, np.full(G, pos))
+        k = prune_pairs(k[None, :], pairs, half)[0]
+        q = prune_pairs(q, pairs, half)
         v = prune_pairs(v, pairs, half)
     return (_store(cfg, k.astype(np.float32)), _store(cfg, v.astype(np.float32)),
             _store(cfg, q.astype(np.float32)))
 
 
-def step_inputs(cfg: Config, layer: int, t: int) -> dict:
+def step_inputs(cfg: Config, layer: int, t: int, rotated: bool = True) -> dict:
     """Decode step t for a whole layer: k_new, v_new [b][hkv][d], q [b][hq][d]."""
     B, Hkv, G, d = cfg.batch, cfg.hkv, cfg.G, cfg.d
     sdt = np.uint16 if cfg.dtype == "bf16" else np.float32
@@ -238,7 +251,8 @@ def step_inputs(cfg: Config, layer: int, t: int) -> dict:
     q = np.empty((B, cfg.hq, d), sdt)
     for b in range(B):
         for kvh in range(Hkv):
-            kn[b, kvh], vn[b, kvh], q[b, kvh * G:(kvh + 1) * G] = step_token(cfg, layer, b, kvh, t)
+            kn[b, kvh], vn[b, kvh], q[b, kvh * G:(kvh + 1) * G] = step_token(cfg, layer, b, kvh, t,
+                                                                              rotated)
     return {"k_new": kn, "v_new": vn, "q": q, "pos": cfg.n + t}
 
 

@@ -19,7 +19,9 @@ Sources (pages are cited by title and the equation / section they give):
         only the top-k chunks stay in the KV cache.
   [RAP] "RAP: KV-Cache Compression via RoPE-Aligned Pruning" (arXiv
         2602.02599) -- decode-step attention over the cached keys and values
-        (Fig. 2 / Eq. 2).
+        (Fig. 2 / Eq. 2); RoPE turns 2-D pairs, so a head that keeps whole
+        pairs is rotated pair by pair with each kept pair's frequency and
+        pruning commutes with the rotation (§3, Eq. 5-10).
 
 Readings where the pages are silent (each is also listed with the design
 notes): window query i sits at position q_pos0 + i and sees keys j <= q_pos0+i;
@@ -29,8 +31,10 @@ budgets are integerised by largest remainder (ties to the lower layer) and
 capped at n with the excess spread over the uncapped layers in proportion to
 their uncertainty.
 
-Every floating-point step is float64.  bf16 inputs arrive as uint16 words and
-are widened exactly.
+Every floating-point step is float64, except the RoPE rotation, whose
+arithmetic is fixed as fp32 (each product and sum rounded on its own, then
+rounded to the storage type) so that a rotated bf16 row has exactly one
+correct value.  bf16 inputs arrive as uint16 words and are widened exactly.
 """
 from __future__ import annotations
 
@@ -43,6 +47,7 @@ __all__ = [
     "zigzag_budgets", "score_order", "select_topb", "select_chunks",
     "select_policy", "compact", "decode_attention", "decode_partial",
     "combine_partials", "append_token", "window_probabilities", "attention_loss",
+    "round_bf16", "rope_pairs",
     "HEAD_GLOBAL", "HEAD_LOCAL", "HEAD_SPECIAL",
 ]
 
@@ -370,3 +375,59 @@ def append_token(idx, Kc, Vc, pos: int, k_new, v_new, cap: int, limit: int):
     Kc[j] = k_new
     Vc[j] = v_new
     return idx, Kc, Vc
+
+
+# ---------------------------------------------------------------------------
+# pair-pruned RoPE  [RAP §3, Eq. 5-10]
+# ---------------------------------------------------------------------------
+
+def round_bf16(x) -> np.ndarray:
+    """float32 values rounded to the nearest bf16 (ties to the even pattern),
+    as uint16 words.  Written from the definition: the two bf16 values that
+    bracket x are its pattern truncated to 16 bits and the next pattern away
+    from zero; the nearer one wins, a tie goes to the one whose last bit is 0.
+    NaN becomes a quiet NaN."""
+    f = np.asarray(x, np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lo = u & 0xFFFF0000
+    hi = lo + 0x10000
+    with np.errstate(invalid="ignore"):     # inf and NaN bracket themselves with NaNs
+        f64 = f.astype(np.float64)
+        v_lo = (lo.astype(np.uint32)).view(np.float32).astype(np.float64)
+        v_hi = (hi.astype(np.uint32)).view(np.float32).astype(np.float64)
+        d_lo, d_hi = np.abs(f64 - v_lo), np.abs(v_hi - f64)
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (((lo >> 16) & 1) == 1))
+    out = np.where(take_hi, hi, lo) >> 16
+    out = np.where(np.isnan(f), (u >> 16) | 0x40, out)
+    return out.astype(np.uint16)
+
+
+def rope_pairs(x, pos, cos_sin, pairs, dtype: str) -> np.ndarray:
+    """Rotate rows of a pair-pruned head at their positions [RAP §3].
+
+    x        [..., d] rows in storage form (bf16: uint16 words; fp32: float32);
+             kept pair e is elements e and e + d/2
+    pos      [...] position of each row
+    cos_sin  [max_pos][half][2] fp32 table of (cos, sin) per position and
+             rotary pair of the unpruned head
+    pairs    [d/2] kept pair index of each stored pair
+    Pair (x, y) becomes (x c - y s, x s + y c), (c, s) = cos_sin[pos][pairs[e]],
+    every product and the two sums rounded to fp32 on their own, the result
+    rounded to the storage type.  Returns rows in storage form.
+    """
+    x = np.asarray(x)
+    d = x.shape[-1]
+    h2 = d // 2
+    if dtype == "bf16":
+        xf = (x.astype(np.uint32) << 16).view(np.float32)
+    else:
+        xf = x.astype(np.float32)
+    a, b = xf[..., :h2], xf[..., h2:]
+    tab = np.asarray(cos_sin, np.float32)
+    pos = np.asarray(pos, np.int64)
+    pr = np.asarray(pairs, np.int64)
+    c = tab[pos[..., None], pr, 0]
+    s = tab[pos[..., None], pr, 1]
+    xc, ys, xs, yc = a * c, b * s, a * s, b * c       # float32 products, each rounded
+    out = np.concatenate([xc - ys, xs + yc], axis=-1).astype(np.float32)
+    return round_bf16(out) if dtype == "bf16" else out

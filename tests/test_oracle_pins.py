@@ -494,3 +494,107 @@ def test_attention_loss_closed_forms():
         assert abs(oracle.attention_loss(P, [0])[0] - max(0.0, 0.9 - p0)) < 1e-15
         assert oracle.attention_loss(P, [0, 1])[0] == 0.0
         assert abs(oracle.attention_loss(P, [])[0] - 0.9) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding and pair-pruned RoPE (RAP §3, Eq. 5-10)
+# ---------------------------------------------------------------------------
+
+def test_round_bf16_hand_values_and_library():
+    one = 1.0
+    cases = [(one, 0x3F80), (-2.0, 0xC000),
+             (one + 2.0 ** -8, 0x3F80),                # halfway 0x3F80 / 0x3F81: even wins
+             (one + 3 * 2.0 ** -8, 0x3F82),            # halfway 0x3F81 / 0x3F82: even wins
+             (one + 2.0 ** -8 + 2.0 ** -20, 0x3F81),   # just above halfway
+             (-(one + 2.0 ** -8), 0xBF80), (0.0, 0x0000), (-0.0, 0x8000),
+             (3.0e38, 0x7F62), (float("inf"), 0x7F80)]
+    got = oracle.round_bf16(np.array([v for v, _ in cases], np.float32))
+    assert [int(g) for g in got] == [h for _, h in cases]
+    assert (int(oracle.round_bf16(np.float32("nan"))) & 0x7FC0) == 0x7FC0
+    # torch's float -> bfloat16 conversion rounds to nearest even as well
+    import torch
+    x = np.random.default_rng(7).standard_normal(20000).astype(np.float32) * np.float32(50.0)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.round_bf16(x), ref)
+
+
+def _rope_rows(rng, shape, dtype):
+    x = rng.standard_normal(shape).astype(np.float32) * np.float32(2.0)
+    return oracle.round_bf16(x) if dtype == "bf16" else x
+
+
+def _as_f32(x, dtype):
+    return (np.asarray(x).astype(np.uint32) << 16).view(np.float32) if dtype == "bf16" else x
+
+
+def test_rope_table_is_the_rope_formula():
+    import kvsynth
+    t = kvsynth.rope_table(300, 64)
+    for pos, p in [(0, 0), (1, 0), (1, 63), (257, 5), (299, 31), (123, 40)]:
+        ang = pos * math.exp(-p / 64 * math.log(10000.0))
+        assert t[pos, p, 0] == np.float32(math.cos(ang))
+        assert t[pos, p, 1] == np.float32(math.sin(ang))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_rope_position_zero_is_identity(dtype):
+    import kvsynth
+    r = np.random.default_rng(3)
+    x = _rope_rows(r, (5, 88), dtype)
+    pairs = np.sort(r.choice(64, 44, replace=False))
+    out = oracle.rope_pairs(x, np.zeros(5, np.int64), kvsynth.rope_table(4, 64), pairs, dtype)
+    assert np.array_equal(np.asarray(out).view(np.uint8), np.asarray(x).view(np.uint8))
+
+
+def test_rope_matches_textbook_rotation():
+    """Identity pair list on a full 128-dim head equals the half-split rotation
+    by angle t * 10000^(-2p/128) computed in float64 from the formula."""
+    import kvsynth
+    r = np.random.default_rng(4)
+    x = r.standard_normal((6, 128)).astype(np.float32)
+    pos = np.array([0, 1, 17, 4095, 30000, 32767])
+    out = oracle.rope_pairs(x, pos, kvsynth.rope_table(32768, 64), np.arange(64), "fp32")
+    p = np.arange(64)
+    ang = pos[:, None] * np.power(10000.0, -2.0 * p / 128.0)[None, :]
+    a, b = x[:, :64].astype(np.float64), x[:, 64:].astype(np.float64)
+    want = np.concatenate([a * np.cos(ang) - b * np.sin(ang), a * np.sin(ang) + b * np.cos(ang)], 1)
+    assert np.max(np.abs(out - want)) <= 2e-6 * np.max(np.abs(x))
+    # the sign convention: pair 0 at a quarter turn maps (1, 0) to (0, 1)
+    quarter = np.zeros((2, 1, 2), np.float32)
+    quarter[1, 0] = (0.0, 1.0)
+    y = oracle.rope_pairs(np.array([[1.0, 0.0]], np.float32), np.array([1]), quarter, [0], "fp32")
+    assert np.array_equal(y, np.array([[0.0, 1.0]], np.float32))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_rope_commutes_with_pair_pruning(dtype):
+    """RAP's absorption identity: rotating the full head and then keeping pairs P
+    equals keeping P and rotating each kept pair with its own frequency."""
+    import kvsynth
+    r = np.random.default_rng(5)
+    x = _rope_rows(r, (7, 128), dtype)
+    pos = r.integers(0, 5000, 7)
+    tab = kvsynth.rope_table(5000, 64)
+    P = np.sort(r.choice(64, 44, replace=False))
+    full = oracle.rope_pairs(x, pos, tab, np.arange(64), dtype)
+    keep = lambda z: np.concatenate([z[:, P], z[:, P + 64]], axis=1)
+    assert np.array_equal(keep(full), oracle.rope_pairs(keep(x), pos, tab, P, dtype))
+
+
+def test_rope_preserves_pair_norms_and_relative_position():
+    import kvsynth
+    r = np.random.default_rng(6)
+    tab = kvsynth.rope_table(9000, 64)
+    P = np.sort(r.choice(64, 44, replace=False))
+    q, k = r.standard_normal((2, 88)).astype(np.float32)
+    rq = oracle.rope_pairs(q[None], np.array([700]), tab, P, "fp32")[0].astype(np.float64)
+    n0 = q[:44].astype(np.float64) ** 2 + q[44:].astype(np.float64) ** 2
+    n1 = rq[:44] ** 2 + rq[44:] ** 2
+    assert np.max(np.abs(n1 - n0) / n0) < 2e-6
+    # the attention logit depends on the positions only through their difference
+    def logit(m, j):
+        a = oracle.rope_pairs(q[None], np.array([m]), tab, P, "fp32")[0].astype(np.float64)
+        b = oracle.rope_pairs(k[None], np.array([j]), tab, P, "fp32")[0].astype(np.float64)
+        return float(a @ b)
+    for m, j, dlt in [(500, 20, 300), (4000, 3999, 4000), (100, 100, 8000)]:
+        assert abs(logit(m, j) - logit(m + dlt, j + dlt)) < 1e-4 * (np.linalg.norm(q) * np.linalg.norm(k))
