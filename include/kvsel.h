@@ -64,6 +64,37 @@ typedef enum {
 
 typedef enum { KVSEL_FP32 = 0, KVSEL_BF16 = 1 } kvsel_dtype;
 
+/* Pair-pruned rotary position embedding applied by the library (RAP page,
+ * §3, Eq. 5-10 and §6.2.3: RoPE turns 2-D pairs, so a key / query that keeps
+ * whole pairs is rotated pair by pair with each kept pair's own frequency,
+ * and pruning commutes with the rotation).  With kvsel_shape.rope set, the
+ * queries of kvsel_score, kvsel_lmba and kvsel_decode_attn and the new key of
+ * kvsel_append arrive unrotated and are rotated on their way in; cached keys
+ * are expected rotated (as kvsel_append writes them).
+ *   cos_sin  [max_pos][half][2] fp32 (device): cos and sin of the angle of
+ *            rotary pair p at position t (the unpruned model's RoPE table)
+ *   max_pos  rows of cos_sin; every position rotated must be below it
+ *   half     rotary pairs of the unpruned head (e.g. 64 for 128 dims),
+ *            half >= head_dim / 2
+ *   pairs    [hkv][head_dim / 2] int32 (device): kept pair index per KV
+ *            head, each in [0, half) (a query head uses its KV head's list)
+ *   q_pos    kvsel_decode_attn: position of the decode query
+ * Row layout: kept pair e is elements e and e + head_dim/2 of the row.  The
+ * pair (x, y) at position t becomes (x c - y s, x s + y c) with (c, s) =
+ * cos_sin[t][pairs[kvh][e]]; each product and the sum are rounded to fp32 on
+ * their own (no fused multiply-add), then to the storage type (bf16:
+ * nearest-even).  Window query i of kvsel_score / kvsel_lmba sits at
+ * q_pos0 + i; kvsel_append's key at pos.  Pair indices and positions outside
+ * the table are a documented precondition: the kernels clamp them rather
+ * than read outside it. */
+typedef struct kvsel_rope {
+  const float* cos_sin;
+  int64_t max_pos;
+  int32_t half;
+  const int32_t* pairs;
+  int64_t q_pos;
+} kvsel_rope;
+
 /* Shape of one layer's attention.
  *   batch, hq, hkv : batch size, query heads, KV heads; hq % hkv == 0;
  *                    query head h reads KV head h / G with group size
@@ -75,12 +106,15 @@ typedef enum { KVSEL_FP32 = 0, KVSEL_BF16 = 1 } kvsel_dtype;
  *                    number of chunk keys.  1 <= n < 2^31.
  *   dtype          : kvsel_dtype of q / K / V.
  *   scale          : softmax scale applied to q . k, positive and finite
- *                    (usually 1/sqrt(head dim of the unpruned model)). */
+ *                    (usually 1/sqrt(head dim of the unpruned model)).
+ *   rope           : (host pointer) NULL when queries and new keys arrive
+ *                    rotated; else the kvsel_rope that rotates them. */
 typedef struct {
   int32_t batch, hq, hkv, head_dim;
   int64_t n;
   int32_t dtype;
   float scale;
+  const kvsel_rope* rope;
 } kvsel_shape;
 
 /* ---------------------------------------------------------------- score --

@@ -28,10 +28,15 @@ class KvselError(RuntimeError):
         self.status = status
 
 
+class Rope(ctypes.Structure):
+    _fields_ = [("cos_sin", ctypes.c_void_p), ("max_pos", ctypes.c_int64), ("half", ctypes.c_int32),
+                ("pairs", ctypes.c_void_p), ("q_pos", ctypes.c_int64)]
+
+
 class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("n", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("rope", ctypes.POINTER(Rope))]
 
 
 class SelectParams(ctypes.Structure):
@@ -117,9 +122,21 @@ def _stream(stream) -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_shape(batch, hq, hkv, head_dim, n, dtype, scale) -> Shape:
+def make_rope(cos_sin, pairs, q_pos: int = 0) -> Rope:
+    """kvsel_rope over a [max_pos][half][2] fp32 cos/sin table and a
+    [hkv][head_dim/2] int32 kept-pair list (both device tensors, which the
+    caller keeps alive)."""
+    return Rope(_ptr(cos_sin), int(cos_sin.shape[0]), int(cos_sin.shape[1]), _ptr(pairs),
+                int(q_pos))
+
+
+def make_shape(batch, hq, hkv, head_dim, n, dtype, scale, rope: Rope | None = None) -> Shape:
     dt = {"fp32": KVSEL_FP32, "bf16": KVSEL_BF16}.get(dtype, dtype)
-    return Shape(int(batch), int(hq), int(hkv), int(head_dim), int(n), int(dt), float(scale))
+    sh = Shape(int(batch), int(hq), int(hkv), int(head_dim), int(n), int(dt), float(scale))
+    if rope is not None:
+        sh.rope = ctypes.pointer(rope)
+        sh._rope = rope    # the descriptor lives as long as the shape
+    return sh
 
 
 def kvsel_score_workspace(shape: Shape, w: int) -> int:

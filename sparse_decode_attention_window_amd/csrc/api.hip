@@ -63,6 +63,25 @@ kvsel_status check_shape(const kvsel_shape* s, int* S, int* G, int max_group) {
 
 int elem_size(const kvsel_shape* s) { return s->dtype == KVSEL_FP32 ? 4 : 2; }
 
+// The shape's RoPE descriptor as the kernels take it, after checking that the
+// positions pos_lo .. pos_hi the call rotates lie inside its table.  A shape
+// without one gives a null RopeDev (rows arrive rotated).
+kvsel_status rope_of(const kvsel_shape* s, int64_t pos_lo, int64_t pos_hi, RopeDev* out) {
+  *out = RopeDev{nullptr, nullptr, 0, 0};
+  const kvsel_rope* r = s->rope;
+  if (!r) return KVSEL_OK;
+  if (!r->cos_sin || !r->pairs) return fail(KVSEL_EINVAL, "rope: cos_sin and pairs must be non-NULL");
+  if (r->half < s->head_dim / 2 || r->half > (1 << 16))
+    return fail(KVSEL_EINVAL, "rope: half (%d) must be in [head_dim/2, 65536]", r->half);
+  if (r->max_pos < 1 || r->max_pos > ((int64_t)1 << 40))
+    return fail(KVSEL_EINVAL, "rope: max_pos must be in [1, 2^40]");
+  if (pos_lo < 0 || pos_hi >= r->max_pos)
+    return fail(KVSEL_EINVAL, "rope: positions %lld .. %lld outside the %lld-row table",
+                (long long)pos_lo, (long long)pos_hi, (long long)r->max_pos);
+  *out = RopeDev{r->cos_sin, r->pairs, r->max_pos, r->half};
+  return KVSEL_OK;
+}
+
 }  // namespace
 
 void set_last_error(const char* msg) { snprintf(g_err, sizeof(g_err), "%s", msg); }
@@ -125,8 +144,10 @@ kvsel_status kvsel_score(const kvsel_shape* s, int32_t w, int64_t q_pos0, const 
   const size_t need = kvsel_score_workspace(s, w);
   if (ws_bytes < need || (need && !ws))
     return fail(KVSEL_ENOSPC, "score workspace needs %zu bytes, got %zu", need, ws_bytes);
+  RopeDev rope;
+  if ((st = rope_of(s, q_pos0, q_pos0 + w - 1, &rope)) != KVSEL_OK) return st;
   return hip_status(launch_score(s->dtype, s->head_dim, s->batch, s->hq, s->hkv, w, s->n, q_pos0,
-                                 s->scale, q_win, k, scores, ws, stream),
+                                 s->scale, q_win, k, scores, ws, rope, stream),
                     "kvsel_score launch");
 }
 
@@ -173,8 +194,10 @@ kvsel_status kvsel_lmba(const kvsel_shape* s, int32_t w, int64_t q_pos0, const v
   float* probs = reinterpret_cast<float*>(base + probs_at);
   uint32_t* mask =
       reinterpret_cast<uint32_t*>(base + probs_at + align256((size_t)S * R * s->n * 4));
+  RopeDev rope;
+  if ((st = rope_of(s, q_pos0, q_pos0 + w - 1, &rope)) != KVSEL_OK) return st;
   hipError_t e = launch_probs(s->dtype, s->head_dim, s->batch, s->hq, s->hkv, w, s->n, q_pos0,
-                              s->scale, q_win, k, probs, ws, stream);
+                              s->scale, q_win, k, probs, ws, rope, stream);
   if (e == hipSuccess)
     e = launch_lmba_rows(probs, S, R, s->n, lmba, seg_off, seg_len, idx, r_cap, kept_mass, mask,
                          stream);
@@ -253,9 +276,12 @@ kvsel_status kvsel_append(const kvsel_shape* s, const void* k_new, const void* v
   if (r_cap > 0 && (!k_c || !v_c)) return fail(KVSEL_EINVAL, "k_c and v_c must be non-NULL");
   if (r_cap < 0 || r_cap > 0x7fffffffLL) return fail(KVSEL_EINVAL, "r_cap must be in [0, 2^31)");
   if (pos < 0 || pos > 0x7fffffffLL) return fail(KVSEL_EINVAL, "pos must be in [0, 2^31)");
+  RopeDev rope;
+  if ((st = rope_of(s, pos, pos, &rope)) != KVSEL_OK) return st;
   if (r_cap == 0) return KVSEL_OK;
-  return hip_status(launch_append(s->dtype, s->head_dim, S, k_new, v_new, (int32_t)pos, seg_off,
-                                  seg_cap, limit, seg_len, idx, k_c, v_c, r_cap, stream),
+  return hip_status(launch_append(s->dtype, s->head_dim, S, s->hkv, k_new, v_new, (int32_t)pos,
+                                  seg_off, seg_cap, limit, seg_len, idx, k_c, v_c, r_cap, rope,
+                                  stream),
                     "kvsel_append launch");
 }
 
@@ -278,8 +304,11 @@ kvsel_status kvsel_decode_attn(const kvsel_shape* s, const void* q, const void* 
   const size_t need = kvsel_decode_workspace(s, r_cap);
   if (ws_bytes < need || !ws)
     return fail(KVSEL_ENOSPC, "decode workspace needs %zu bytes, got %zu", need, ws_bytes);
+  RopeDev rope;
+  const int64_t q_pos = s->rope ? s->rope->q_pos : 0;
+  if ((st = rope_of(s, q_pos, q_pos, &rope)) != KVSEL_OK) return st;
   return hip_status(launch_decode(s->dtype, s->head_dim, s->batch, s->hq, s->hkv, s->scale, q, k_c,
-                                  v_c, seg_off, seg_len, r_cap, out, ws, stream),
+                                  v_c, seg_off, seg_len, r_cap, out, ws, rope, q_pos, stream),
                     "kvsel_decode_attn launch");
 }
 

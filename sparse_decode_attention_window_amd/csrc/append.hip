@@ -21,11 +21,14 @@ __device__ __forceinline__ uint64_t pack(int32_t pos, int32_t slot) {
   return ((uint64_t)(uint32_t)(pos ^ INT32_MIN) << 32) | (uint32_t)slot;
 }
 
+// T is the storage type of the rows (used only to rotate the new key).
+template <typename T>
 __global__ __launch_bounds__(kThreads) void append_kernel(
     const char* __restrict__ k_new, const char* __restrict__ v_new, int32_t pos, int row_bytes,
-    const int64_t* __restrict__ seg_off, const int64_t* __restrict__ seg_cap,
+    int hkv, const int64_t* __restrict__ seg_off, const int64_t* __restrict__ seg_cap,
     const int32_t* __restrict__ limit, int32_t* __restrict__ seg_len,
-    int32_t* __restrict__ idx, char* __restrict__ k_c, char* __restrict__ v_c, int64_t r_cap) {
+    int32_t* __restrict__ idx, char* __restrict__ k_c, char* __restrict__ v_c, int64_t r_cap,
+    RopeDev rope) {
   __shared__ uint64_t wmin[kWaves];
   const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int32_t lim = limit ? limit[s] : 0;
@@ -69,8 +72,13 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   const char* ks = k_new + (int64_t)s * row_bytes;
   const char* vs = v_new + (int64_t)s * row_bytes;
   for (int c = tid; c < row_bytes / 16; c += kThreads) {
-    store16(k_c + row * row_bytes + 16 * c, load16(ks + 16 * c));
+    if (!rope.cs) store16(k_c + row * row_bytes + 16 * c, load16(ks + 16 * c));
     store16(v_c + row * row_bytes + 16 * c, load16(vs + 16 * c));
+  }
+  if (rope.cs) {   // unrotated key: rotated at pos on its way into the cache
+    const int h2 = row_bytes / (int)sizeof(T) / 2;
+    for (int e = tid; e < h2; e += kThreads)
+      rope_pair<T>(rope, s % hkv, h2, e, pos, ks, k_c + row * row_bytes);
   }
   if (tid == 0) {
     idx[row] = pos;
@@ -80,15 +88,21 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
 
 }  // namespace
 
-hipError_t launch_append(int dtype, int head_dim, int S, const void* k_new,
+hipError_t launch_append(int dtype, int head_dim, int S, int hkv, const void* k_new,
                          const void* v_new, int32_t pos, const int64_t* seg_off,
                          const int64_t* seg_cap, const int32_t* limit, int32_t* seg_len,
-                         int32_t* idx, void* k_c, void* v_c, int64_t r_cap,
+                         int32_t* idx, void* k_c, void* v_c, int64_t r_cap, const RopeDev& rope,
                          hipStream_t stream) {
-  const int row_bytes = head_dim * (dtype == 1 ? 2 : 4);
-  append_kernel<<<dim3(S), dim3(kThreads), 0, stream>>>(
-      static_cast<const char*>(k_new), static_cast<const char*>(v_new), pos, row_bytes, seg_off, seg_cap, limit, seg_len, idx, static_cast<char*>(k_c), static_cast<char*>(v_c),
-      r_cap);
+  const auto kn = static_cast<const char*>(k_new);
+  const auto vn = static_cast<const char*>(v_new);
+  const auto kc = static_cast<char*>(k_c);
+  const auto vc = static_cast<char*>(v_c);
+  if (dtype == 1)
+    append_kernel<bf16_t><<<dim3(S), dim3(kThreads), 0, stream>>>(
+        kn, vn, pos, head_dim * 2, hkv, seg_off, seg_cap, limit, seg_len, idx, kc, vc, r_cap, rope);
+  else
+    append_kernel<float><<<dim3(S), dim3(kThreads), 0, stream>>>(
+        kn, vn, pos, head_dim * 4, hkv, seg_off, seg_cap, limit, seg_len, idx, kc, vc, r_cap, rope);
   return hipGetLastError();
 }
 

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kThreads, KVSEL_DECODE_MIN_BLOCKS) void decode_spli
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
     const int64_t* __restrict__ seg_off, const int32_t* __restrict__ seg_len, int64_t r_cap,
     int S, int hq, int hkv, int G, float c, int rpw, float2* __restrict__ part_ml,
-    float* __restrict__ part_o) {
+    float* __restrict__ part_o, RopeDev rope, int64_t q_pos) {
   using Gm = Geom<T, D>;
   __shared__ float4 sp_all[kWaves][kTile];
   __shared__ float sm_o[kWaves][HG][D];
@@ -319,11 +319,25 @@ __global__ __launch_bounds__(kThreads, KVSEL_DECODE_MIN_BLOCKS) void decode_spli
   {
     const int hl = l16 % HG;
     const char* qrow = q + ((int64_t)b * hq + (int64_t)kvh * G + hl) * Gm::RB;
+    if (rope.cs) {
+      // unrotated queries: rotate the G rows at q_pos once into LDS (sm_o is
+      // not used before the final merge; the second barrier keeps it so)
+      char* sq = reinterpret_cast<char*>(&sm_o[0][0][0]);
+      const char* qb = q + ((int64_t)b * hq + (int64_t)kvh * G) * Gm::RB;
+      constexpr int H2 = D / 2;
+      for (int i = tid; i < G * H2; i += kThreads) {
+        const int h = i / H2, e = i - h * H2;
+        rope_pair<T>(rope, kvh, H2, e, q_pos, qb + h * Gm::RB, sq + h * Gm::RB);
+      }
+      __syncthreads();
+      qrow = sq + hl * Gm::RB;
+    }
 #pragma unroll
     for (int a = 0; a < Gm::NA; ++a) {
       const int o = 64 * a + 16 * grp;
       qf[a] = (hl < G && o < Gm::RB) ? load16(qrow + o) : u32x4{0, 0, 0, 0};
     }
+    if (rope.cs) __syncthreads();
   }
 
   WaveState<T, D, HG> st;
@@ -472,7 +486,7 @@ int resident_blocks(K kernel) {
 template <typename T, int D, int HG>
 hipError_t run(int batch, int hq, int hkv, float scale, const void* q, const void* k_c,
                const void* v_c, const int64_t* seg_off, const int32_t* seg_len, int64_t r_cap,
-               float* out, void* ws, hipStream_t stream) {
+               float* out, void* ws, const RopeDev& rope, int64_t q_pos, hipStream_t stream) {
   const int S = batch * hkv, G = hq / hkv;
   const int slots = device_info().cus * resident_blocks(decode_split_kernel<T, D, HG>);
   const int rpw = rows_per_wave(r_cap, S, slots);
@@ -483,7 +497,8 @@ hipError_t run(int batch, int hq, int hkv, float scale, const void* q, const voi
   const float c = scale * kLog2e;
   decode_split_kernel<T, D, HG><<<dim3((unsigned)items), dim3(kThreads), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(k_c),
-      static_cast<const char*>(v_c), seg_off, seg_len, r_cap, S, hq, hkv, G, c, rpw, ml, po);
+      static_cast<const char*>(v_c), seg_off, seg_len, r_cap, S, hq, hkv, G, c, rpw, ml, po, rope,
+      q_pos);
   decode_combine_kernel<HG, D><<<dim3(S), dim3(kThreads), 0, stream>>>(
       ml, po, seg_off, seg_len, r_cap, hq, hkv, G, S, rpw, items, out);
   return hipGetLastError();
@@ -492,12 +507,16 @@ hipError_t run(int batch, int hq, int hkv, float scale, const void* q, const voi
 template <typename T, int D>
 hipError_t run_d(int batch, int hq, int hkv, float scale, const void* q, const void* k_c,
                  const void* v_c, const int64_t* seg_off, const int32_t* seg_len, int64_t r_cap,
-                 float* out, void* ws, hipStream_t stream) {
+                 float* out, void* ws, const RopeDev& rope, int64_t q_pos, hipStream_t stream) {
+#define KVSEL_HG(HG) \
+  return run<T, D, HG>(batch, hq, hkv, scale, q, k_c, v_c, seg_off, seg_len, r_cap, out, ws, rope, \
+                       q_pos, stream)
   switch (hg_for(hq / hkv)) {
-    case 1: return run<T, D, 1>(batch, hq, hkv, scale, q, k_c, v_c, seg_off, seg_len, r_cap, out, ws, stream);
-    case 2: return run<T, D, 2>(batch, hq, hkv, scale, q, k_c, v_c, seg_off, seg_len, r_cap, out, ws, stream);
-    default: return run<T, D, 4>(batch, hq, hkv, scale, q, k_c, v_c, seg_off, seg_len, r_cap, out, ws, stream);
+    case 1: KVSEL_HG(1);
+    case 2: KVSEL_HG(2);
+    default: KVSEL_HG(4);
   }
+#undef KVSEL_HG
 }
 
 }  // namespace
@@ -510,9 +529,11 @@ size_t decode_workspace_bytes(int S, int head_dim, int G, int64_t r_cap) {
 hipError_t launch_decode(int dtype, int head_dim, int batch, int hq, int hkv, float scale,
                          const void* q, const void* k_c, const void* v_c,
                          const int64_t* seg_off, const int32_t* seg_len, int64_t r_cap,
-                         float* out, void* ws, hipStream_t stream) {
-#define KVSEL_DEC(T, D) \
-  return run_d<T, D>(batch, hq, hkv, scale, q, k_c, v_c, seg_off, seg_len, r_cap, out, ws, stream)
+                         float* out, void* ws, const RopeDev& rope, int64_t q_pos,
+                         hipStream_t stream) {
+#define KVSEL_DEC(T, D)                                                                        \
+  return run_d<T, D>(batch, hq, hkv, scale, q, k_c, v_c, seg_off, seg_len, r_cap, out, ws, rope, \
+                     q_pos, stream)
   if (dtype == 1) {
     if (head_dim == 64) KVSEL_DEC(bf16_t, 64);
     if (head_dim == 88) KVSEL_DEC(bf16_t, 88);

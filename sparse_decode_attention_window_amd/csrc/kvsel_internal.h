@@ -52,6 +52,70 @@ __device__ __forceinline__ void store16(void* p, const u32x4& v) {
 }
 
 // ---------------------------------------------------------------------------
+// Pair-pruned rotary position embedding (RAP page, §3 and Eq. 5-10: RoPE
+// turns 2-D pairs, so a head that keeps whole pairs is rotated pair by pair
+// with each kept pair's own frequency).  A row of head_dim elements stores
+// kept pair e as elements e and e + head_dim/2; its angle at position t has
+// (cos, sin) = cs[t][pairs[kvh][e]].
+// ---------------------------------------------------------------------------
+struct RopeDev {
+  const float* cs;       // [max_pos][half][2] (cos, sin); null: rows arrive rotated
+  const int32_t* pairs;  // [hkv][head_dim / 2] kept pair index, in [0, half)
+  int64_t max_pos;
+  int32_t half;
+};
+
+// (x, y) turned by the angle with cosine c and sine s.  Each product and the
+// sum are rounded to fp32 on their own (no fused multiply-add), so any IEEE
+// fp32 implementation reproduces the result bit for bit.
+__device__ __forceinline__ void rope_turn(float x, float y, float c, float s, float& xo,
+                                          float& yo) {
+#pragma clang fp contract(off)
+  const float xc = x * c, ys = y * s, xs = x * s, yc = y * c;
+  xo = xc - ys;
+  yo = xs + yc;
+}
+
+// fp32 -> bf16, round to nearest even (a NaN stays a quiet NaN)
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float elem_get(const char* row, int e);
+template <> __device__ __forceinline__ float elem_get<float>(const char* row, int e) {
+  return reinterpret_cast<const float*>(row)[e];
+}
+template <> __device__ __forceinline__ float elem_get<bf16_t>(const char* row, int e) {
+  return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[e] << 16);
+}
+template <typename T> __device__ __forceinline__ void elem_put(char* row, int e, float v);
+template <> __device__ __forceinline__ void elem_put<float>(char* row, int e, float v) {
+  reinterpret_cast<float*>(row)[e] = v;
+}
+template <> __device__ __forceinline__ void elem_put<bf16_t>(char* row, int e, float v) {
+  reinterpret_cast<uint16_t*>(row)[e] = bf16_rne(v);
+}
+
+// Rotate kept pair e (elements e and e + h2 of a row of 2*h2 elements of T)
+// of KV head kvh at position pos, reading src and writing dst (may alias).
+// Pair index and position are clamped into the table, so a bad pair list
+// or position never reads outside it.
+template <typename T>
+__device__ __forceinline__ void rope_pair(const RopeDev& r, int kvh, int h2, int e, int64_t pos,
+                                          const char* src, char* dst) {
+  int p = r.pairs[(int64_t)kvh * h2 + e];
+  p = p < 0 ? 0 : (p >= r.half ? r.half - 1 : p);
+  pos = pos < 0 ? 0 : (pos >= r.max_pos ? r.max_pos - 1 : pos);
+  const float2 cs = reinterpret_cast<const float2*>(r.cs)[pos * r.half + p];
+  float xo, yo;
+  rope_turn(elem_get<T>(src, e), elem_get<T>(src, e + h2), cs.x, cs.y, xo, yo);
+  elem_put<T>(dst, e, xo);
+  elem_put<T>(dst, e + h2, yo);
+}
+
+// ---------------------------------------------------------------------------
 // segment table: clipped offsets / lengths and an exclusive prefix of work
 // units per segment, built by every workgroup of a launch in LDS.
 //   off[s], len[s]  clipped so that [off, off + len) lies inside [0, r_cap)
@@ -245,23 +309,26 @@ size_t decode_workspace_bytes(int S, int head_dim, int G, int64_t r_cap);
 hipError_t launch_decode(int dtype, int head_dim, int batch, int hq, int hkv, float scale,
                          const void* q, const void* k_c, const void* v_c,
                          const int64_t* seg_off, const int32_t* seg_len, int64_t r_cap,
-                         float* out, void* ws, hipStream_t stream);
+                         float* out, void* ws, const RopeDev& rope, int64_t q_pos,
+                         hipStream_t stream);
 
-hipError_t launch_append(int dtype, int head_dim, int S, const void* k_new, const void* v_new,
-                         int32_t pos, const int64_t* seg_off, const int64_t* seg_cap,
-                         const int32_t* limit, int32_t* seg_len, int32_t* idx, void* k_c,
-                         void* v_c, int64_t r_cap, hipStream_t stream);
+hipError_t launch_append(int dtype, int head_dim, int S, int hkv, const void* k_new,
+                         const void* v_new, int32_t pos, const int64_t* seg_off,
+                         const int64_t* seg_cap, const int32_t* limit, int32_t* seg_len,
+                         int32_t* idx, void* k_c, void* v_c, int64_t r_cap, const RopeDev& rope,
+                         hipStream_t stream);
 
 size_t score_workspace_bytes(int S, int64_t n, int rows);
 hipError_t launch_score(int dtype, int head_dim, int batch, int hq, int hkv, int w,
                         int64_t n, int64_t q_pos0, float scale, const void* q_win,
-                        const void* k, float* scores, void* ws, hipStream_t stream);
+                        const void* k, float* scores, void* ws, const RopeDev& rope,
+                        hipStream_t stream);
 
 // Attention rows of the window queries, probs [S][G*w][n] fp32 (same passes as
 // launch_score; the score workspace holds the row statistics).
 hipError_t launch_probs(int dtype, int head_dim, int batch, int hq, int hkv, int w, int64_t n,
                         int64_t q_pos0, float scale, const void* q_win, const void* k,
-                        float* probs, void* ws, hipStream_t stream);
+                        float* probs, void* ws, const RopeDev& rope, hipStream_t stream);
 
 // Per attention row: the 90 %-mass minimum token count, and optionally the
 // mass on a selection (seg_off / seg_len / idx) of the row's segment.

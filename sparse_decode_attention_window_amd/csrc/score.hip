@@ -63,9 +63,11 @@ __device__ __forceinline__ int acc_row(int j, int lane) {
 }
 
 // Stage the R query rows of segment (b, kvh) into LDS (rows >= R zero-filled).
+// With rope.cs set the rows arrive unrotated and are rotated here, row r at
+// position q_pos0 + r % w (the caller's next barrier publishes them).
 template <typename T, int D>
 __device__ void stage_q(const char* __restrict__ qw, int b, int kvh, int hq, int G, int w, int R,
-                        int RP, char* sq) {
+                        int RP, char* sq, const RopeDev& rope, int64_t q_pos0) {
   using Gm = SGeom<T, D>;
   const char* src = qw + ((int64_t)b * hq + (int64_t)kvh * G) * w * Gm::RB;
   constexpr int CH = Gm::RB / 16;
@@ -77,6 +79,15 @@ __device__ void stage_q(const char* __restrict__ qw, int b, int kvh, int hq, int
   // zero the pad step beyond the row (NA * 32 may exceed RB)
   for (int i = threadIdx.x; i < RP; i += kThreads)
     if (Gm::NA * 32 > Gm::RB) store16(sq + i * Gm::PITCH + Gm::RB, u32x4{0, 0, 0, 0});
+  if (rope.cs) {
+    __syncthreads();
+    constexpr int H2 = D / 2;
+    for (int i = threadIdx.x; i < R * H2; i += kThreads) {
+      const int r = i / H2, e = i - r * H2;
+      char* row = sq + r * Gm::PITCH;
+      rope_pair<T>(rope, kvh, H2, e, q_pos0 + (r % w), row, row);
+    }
+  }
 }
 
 // Branch-free K fragment load of one key row (the caller clamps `key` into
@@ -133,7 +144,7 @@ __device__ __forceinline__ void for_each_key_block(const char* __restrict__ kseg
 template <typename T, int D, int RBN>
 __global__ __launch_bounds__(kThreads) void score_stats_kernel(
     const char* __restrict__ qw, const char* __restrict__ k, int64_t n, int hq, int hkv, int G,
-    int w, int R, int64_t q_pos0, float c, float2* __restrict__ stats, int tiles) {
+    int w, int R, int64_t q_pos0, float c, float2* __restrict__ stats, int tiles, RopeDev rope) {
   using Gm = SGeom<T, D>;
   extern __shared__ char lds_raw[];
   char* sq = lds_raw;                                   // RP * PITCH
@@ -144,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(
   const int b = s / hkv, kvh = s % hkv;
   constexpr int RP = RBN * 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, half = lane >> 5;
-  stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq);
+  stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq, rope, q_pos0);
   for (int r = tid; r < RP; r += kThreads) {
     const int64_t p = q_pos0 + (r % w);
     lim[r] = r < R ? (int)(p < n - 1 ? p : n - 1) : -1;   // row r sees keys <= lim[r]
@@ -254,7 +265,7 @@ template <typename T, int D, int RBN, bool PROBS = false>
 __global__ __launch_bounds__(kThreads) void score_final_kernel(
     const char* __restrict__ qw, const char* __restrict__ k, int64_t n, int hq, int hkv, int G,
     int w, int R, int64_t q_pos0, float c, const float* __restrict__ rowc,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, RopeDev rope) {
   using Gm = SGeom<T, D>;
   extern __shared__ char lds_raw[];
   char* sq = lds_raw;
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
   const int b = s / hkv, kvh = s % hkv;
   constexpr int RP = RBN * 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, half = lane >> 5;
-  stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq);
+  stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq, rope, q_pos0);
   for (int r = tid; r < RP; r += kThreads) {
     krow[r] = rowc[(int64_t)s * RP + r];
     const int64_t p = q_pos0 + (r % w);
@@ -318,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
 template <typename T, int D, int RBN, bool PROBS = false>
 hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int64_t q_pos0,
                     float c, const char* qp, const char* kp, float* scores, float2* stats,
-                    float* rowc, int tiles, hipStream_t stream) {
+                    float* rowc, int tiles, const RopeDev& rope, hipStream_t stream) {
   using Gm = SGeom<T, D>;
   const size_t lds = (size_t)RBN * 32 * Gm::PITCH;
   if (lds > 65536) {
@@ -331,16 +342,17 @@ hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int6
   }
   const dim3 grid(tiles, S);
   score_stats_kernel<T, D, RBN><<<grid, dim3(kThreads), lds, stream>>>(
-      qp, kp, n, hq, hkv, G, w, R, q_pos0, c, stats, tiles);
+      qp, kp, n, hq, hkv, G, w, R, q_pos0, c, stats, tiles, rope);
   score_reduce_kernel<<<dim3(S), dim3(kReduceThreads), 0, stream>>>(stats, tiles, R, rowc);
   score_final_kernel<T, D, RBN, PROBS><<<grid, dim3(kThreads), lds, stream>>>(
-      qp, kp, n, hq, hkv, G, w, R, q_pos0, c, rowc, scores);
+      qp, kp, n, hq, hkv, G, w, R, q_pos0, c, rowc, scores, rope);
   return hipGetLastError();
 }
 
 template <typename T, int D, bool PROBS = false>
 hipError_t run(int batch, int hq, int hkv, int w, int64_t n, int64_t q_pos0, float scale,
-               const void* q_win, const void* k, float* scores, void* ws, hipStream_t stream) {
+               const void* q_win, const void* k, float* scores, void* ws, const RopeDev& rope,
+               hipStream_t stream) {
   const int S = batch * hkv, G = hq / hkv, R = G * w;
   const int RP = padded_rows(R);
   const int tiles = (int)((n + kTileKeys - 1) / kTileKeys);
@@ -351,7 +363,7 @@ hipError_t run(int batch, int hq, int hkv, int w, int64_t n, int64_t q_pos0, flo
   auto kp = static_cast<const char*>(k);
 #define KVSEL_ROWS(RBN) \
   return run_rows<T, D, RBN, PROBS>(S, hq, hkv, G, w, R, n, q_pos0, c, qp, kp, scores, stats, \
-                                    rowc, tiles, stream)
+                                    rowc, tiles, rope, stream)
   switch (RP / 32) {
     case 1: KVSEL_ROWS(1);
     case 2: KVSEL_ROWS(2);
@@ -371,9 +383,9 @@ size_t score_workspace_bytes(int S, int64_t n, int rows) {
 
 hipError_t launch_probs(int dtype, int head_dim, int batch, int hq, int hkv, int w, int64_t n,
                         int64_t q_pos0, float scale, const void* q_win, const void* k,
-                        float* probs, void* ws, hipStream_t stream) {
+                        float* probs, void* ws, const RopeDev& rope, hipStream_t stream) {
 #define KVSEL_PR(T, D) \
-  return run<T, D, true>(batch, hq, hkv, w, n, q_pos0, scale, q_win, k, probs, ws, stream)
+  return run<T, D, true>(batch, hq, hkv, w, n, q_pos0, scale, q_win, k, probs, ws, rope, stream)
   if (dtype == 1) {
     if (head_dim == 64) KVSEL_PR(bf16_t, 64);
     if (head_dim == 88) KVSEL_PR(bf16_t, 88);
@@ -389,8 +401,9 @@ hipError_t launch_probs(int dtype, int head_dim, int batch, int hq, int hkv, int
 
 hipError_t launch_score(int dtype, int head_dim, int batch, int hq, int hkv, int w, int64_t n,
                         int64_t q_pos0, float scale, const void* q_win, const void* k,
-                        float* scores, void* ws, hipStream_t stream) {
-#define KVSEL_SC(T, D) return run<T, D>(batch, hq, hkv, w, n, q_pos0, scale, q_win, k, scores, ws, stream)
+                        float* scores, void* ws, const RopeDev& rope, hipStream_t stream) {
+#define KVSEL_SC(T, D) \
+  return run<T, D>(batch, hq, hkv, w, n, q_pos0, scale, q_win, k, scores, ws, rope, stream)
   if (dtype == 1) {
     if (head_dim == 64) KVSEL_SC(bf16_t, 64);
     if (head_dim == 88) KVSEL_SC(bf16_t, 88);

@@ -33,6 +33,37 @@ def test_header_symbols_exported():
     assert set(names) == set(_lib.EXPORTED)
 
 
+def test_struct_layouts_match_header(tmp_path):
+    """The ctypes mirrors of kvsel_shape, kvsel_rope and kvsel_select_params
+    have the sizes and field offsets the C compiler gives the header's structs."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = {"kvsel_shape": [f for f, _ in _lib.Shape._fields_],
+              "kvsel_rope": [f for f, _ in _lib.Rope._fields_],
+              "kvsel_select_params": [f for f, _ in _lib.SelectParams._fields_]}
+    lines = []
+    for st, fs in fields.items():
+        lines.append(f'printf("{st} %zu\\n", sizeof({st}));')
+        lines += [f'printf("{st}.{f} %zu\\n", offsetof({st}, {f}));' for f in fs]
+    src = tmp_path / "probe.c"
+    src.write_text('#include "kvsel.h"\n#include <stdio.h>\n#include <stddef.h>\n'
+                   "int main(void) {\n" + "\n".join(lines) + "\nreturn 0;\n}\n")
+    exe = tmp_path / "probe"
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    subprocess.run([cc, "-D__HIP_PLATFORM_AMD__", "-I" + os.path.dirname(HEADER),
+                    "-I" + os.path.join(rocm, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                       text=True).stdout.splitlines())
+    for st, cls in (("kvsel_shape", _lib.Shape), ("kvsel_rope", _lib.Rope),
+                    ("kvsel_select_params", _lib.SelectParams)):
+        assert int(got[st]) == ctypes.sizeof(cls), st
+        for f in fields[st]:
+            assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
+
+
 def test_version():
     assert "gfx950" in kvsel.kvsel_version()
 
@@ -139,6 +170,35 @@ def test_append_rejects_bad_args():
     assert app(r_cap=0) == _lib.KVSEL_OK          # an empty cache: nothing to do, nothing launched
     assert lib.kvsel_append(ctypes.byref(shape(head_dim=96)), FAKE, FAKE, 1, FAKE, FAKE, None,
                             FAKE, FAKE, FAKE, FAKE, 16, None) == _lib.KVSEL_EUNSUPPORTED
+
+
+def test_rope_rejects_bad_descriptors():
+    """RoPE descriptor checks run before any launch: missing table or pair list,
+    half below head_dim/2, and positions outside the table."""
+    lib = kvsel.lib()
+
+    def rope(**kw):
+        base = dict(cos_sin=FAKE, max_pos=1024, half=32, pairs=FAKE, q_pos=10)
+        base.update(kw)
+        return _lib.Rope(**base)
+
+    def score(r, w=8, q_pos0=0):
+        sh = shape(rope=r)
+        return lib.kvsel_score(ctypes.byref(sh), w, q_pos0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert score(rope(cos_sin=None)) == _lib.KVSEL_EINVAL
+    assert score(rope(pairs=None)) == _lib.KVSEL_EINVAL
+    assert score(rope(half=31)) == _lib.KVSEL_EINVAL            # head_dim 64 keeps 32 pairs
+    assert score(rope(max_pos=0)) == _lib.KVSEL_EINVAL
+    assert score(rope(), q_pos0=1017) == _lib.KVSEL_EINVAL      # rows reach position 1024
+    sh = shape(rope=rope(q_pos=1024))
+    assert lib.kvsel_decode_attn(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE,
+                                 1 << 30, None) == _lib.KVSEL_EINVAL
+    sh = shape(rope=rope())
+    assert lib.kvsel_append(ctypes.byref(sh), FAKE, FAKE, 1024, FAKE, FAKE, None, FAKE, FAKE,
+                            FAKE, FAKE, 16, None) == _lib.KVSEL_EINVAL
+    sh = shape(rope=rope(q_pos=-1))
+    assert lib.kvsel_decode_attn(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE,
+                                 1 << 30, None) == _lib.KVSEL_EINVAL
 
 
 # ---------------------------------------------------------------------------

@@ -633,3 +633,148 @@ def test_lmba_and_kept_mass_match_oracle(kv, cid):
         assert np.all(np.minimum(got_m[s], 0.9) <= want + 1e-5)
     print(f"  {cfg.name}: layer LMBA {got_k.mean():.1f} of n={cfg.n}, kept-mass err {worst:.1e}, "
           f"mean attention loss {np.maximum(0, 0.9 - got_m).mean():.4f}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# fused pair-pruned RoPE (RAP §3, Eq. 5-10): rows arrive unrotated and are
+# rotated inside the kernels; the rotation is fixed fp32 arithmetic, so the
+# fused path must equal the same kernels fed the oracle's rotated rows bit for
+# bit, and the oracle within the usual bars.
+# ---------------------------------------------------------------------------
+
+def _rope_setup(kv, dtype, d, half, hkv, max_pos, seed):
+    kvsel, pipeline, torch = kv
+    r = np.random.default_rng(seed)
+    if d // 2 == half:
+        pairs = np.tile(np.arange(half, dtype=np.int32), (hkv, 1))
+    else:
+        pairs = np.stack([np.sort(r.choice(half, d // 2, replace=False))
+                          for _ in range(hkv)]).astype(np.int32)
+    tab = kvsynth.rope_table(max_pos, half)
+    store = (lambda x: kvsynth.f32_to_bf16_bits(x)) if dtype == "bf16" else (lambda x: x)
+    dev = (pipeline.device_tensor(tab), pipeline.device_tensor(pairs))
+    return r, pairs, tab, store, dev
+
+
+@pytest.mark.parametrize("dtype,d,half,G,w,n", [("bf16", 128, 64, 4, 32, 3000),
+                                               ("bf16", 88, 64, 4, 8, 1500),
+                                               ("fp32", 64, 64, 2, 8, 777),
+                                               ("fp32", 88, 64, 1, 3, 300)])
+def test_rope_score_and_lmba_fused(kv, dtype, d, half, G, w, n):
+    kvsel, pipeline, torch = kv
+    _say("rope score", dtype, d, half, G, w, n)
+    B, hkv = 2, 2
+    q_pos0 = n - w
+    r, pairs, tab, store, (tab_d, pairs_d) = _rope_setup(kv, dtype, d, half, hkv, n + 5, n * 7 + d)
+    q = store((r.standard_normal((B, hkv * G, w, d)) * 1.5).astype(np.float32))
+    K = store(r.standard_normal((B, hkv, n, d)).astype(np.float32))
+    q_rot = np.empty_like(q)
+    for b in range(B):
+        for h in range(hkv * G):
+            q_rot[b, h] = oracle.rope_pairs(q[b, h], q_pos0 + np.arange(w), tab, pairs[h // G], dtype)
+    plain = kvsel.make_shape(B, hkv * G, hkv, d, n, dtype, 1 / math.sqrt(d))
+    fused = kvsel.make_shape(B, hkv * G, hkv, d, n, dtype, 1 / math.sqrt(d),
+                             rope=kvsel.make_rope(tab_d, pairs_d))
+    Kd = pipeline.device_tensor(K)
+    ws = torch.empty(kvsel.kvsel_score_workspace(plain, w), dtype=torch.uint8, device="cuda")
+    s1 = torch.empty(B * hkv * n, dtype=torch.float32, device="cuda")
+    s2 = torch.empty_like(s1)
+    kvsel.kvsel_score(fused, w, q_pos0, pipeline.device_tensor(q), Kd, s1, ws)
+    kvsel.kvsel_score(plain, w, q_pos0, pipeline.device_tensor(q_rot), Kd, s2, ws)
+    lws = torch.empty(kvsel.kvsel_lmba_workspace(plain, w), dtype=torch.uint8, device="cuda")
+    l1 = torch.empty(B * hkv * G * w, dtype=torch.int32, device="cuda")
+    l2 = torch.empty_like(l1)
+    kvsel.kvsel_lmba(fused, w, q_pos0, pipeline.device_tensor(q), Kd, l1, lws)
+    kvsel.kvsel_lmba(plain, w, q_pos0, pipeline.device_tensor(q_rot), Kd, l2, lws)
+    torch.cuda.synchronize()
+    a, b_ = pu.to_host(s1), pu.to_host(s2)
+    assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), "fused RoPE score differs"
+    assert np.array_equal(pu.to_host(l1), pu.to_host(l2)), "fused RoPE LMBA differs"
+    a = a.reshape(B * hkv, n)
+    for s in range(B * hkv):
+        bb, kh = divmod(s, hkv)
+        ref = oracle.window_scores(oracle.to_f64(q_rot[bb, kh * G:(kh + 1) * G]),
+                                   oracle.to_f64(K[bb, kh]), 1 / math.sqrt(d), q_pos0)
+        pu.check_scores(a[s], ref, G * w, f"rope score seg {s}")
+
+
+@pytest.mark.parametrize("dtype,d,half,G", [("bf16", 88, 64, 4), ("bf16", 128, 64, 4),
+                                           ("fp32", 88, 64, 2), ("bf16", 64, 64, 1)])
+def test_rope_decode_fused(kv, dtype, d, half, G):
+    kvsel, pipeline, torch = kv
+    _say("rope decode", dtype, d, half, G)
+    B, hkv = 2, 2
+    S = B * hkv
+    q_pos = 40000
+    r, pairs, tab, store, (tab_d, pairs_d) = _rope_setup(kv, dtype, d, half, hkv, q_pos + 1, d + G)
+    lens = np.array([0, 3, 700, 2500], np.int32)
+    off, r_cap = pipeline.offsets(lens.astype(np.int64))
+    Kc = store(r.standard_normal((r_cap, d)).astype(np.float32))
+    Vc = store(r.standard_normal((r_cap, d)).astype(np.float32))
+    q = store((2 * r.standard_normal((B, hkv * G, d))).astype(np.float32))
+    q_rot = np.empty_like(q)
+    for b in range(B):
+        for h in range(hkv * G):
+            q_rot[b, h] = oracle.rope_pairs(q[b, h][None], np.array([q_pos]), tab, pairs[h // G],
+                                            dtype)[0]
+    plain = kvsel.make_shape(B, hkv * G, hkv, d, 2500, dtype, 1 / math.sqrt(128))
+    fused = kvsel.make_shape(B, hkv * G, hkv, d, 2500, dtype, 1 / math.sqrt(128),
+                             rope=kvsel.make_rope(tab_d, pairs_d, q_pos=q_pos))
+    ws = torch.empty(kvsel.kvsel_decode_workspace(plain, r_cap), dtype=torch.uint8, device="cuda")
+    o1 = torch.empty((B, hkv * G, d), dtype=torch.float32, device="cuda")
+    o2 = torch.empty_like(o1)
+    args = (pipeline.device_tensor(Kc), pipeline.device_tensor(Vc), pipeline.device_tensor(off),
+            pipeline.device_tensor(lens), r_cap)
+    kvsel.kvsel_decode_attn(fused, pipeline.device_tensor(q), *args, o1, ws)
+    kvsel.kvsel_decode_attn(plain, pipeline.device_tensor(q_rot), *args, o2, ws)
+    torch.cuda.synchronize()
+    a = pu.to_host(o1)
+    assert np.array_equal(a.view(np.uint32), pu.to_host(o2).view(np.uint32)), "fused RoPE decode differs"
+    for s in range(S):
+        b, h = divmod(s, hkv)
+        rows = np.arange(off[s], off[s] + lens[s])
+        pu.check_decode(a[b, h * G:(h + 1) * G], q_rot[b, h * G:(h + 1) * G], Kc, Vc, rows,
+                        1 / math.sqrt(128), dtype, f"rope decode seg {s}")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 88), ("fp32", 128)])
+def test_rope_append_rotates_new_key(kv, dtype, d):
+    """The appended key is the oracle's rotation of the new key at pos, bit for
+    bit; the value row is copied unchanged."""
+    kvsel, pipeline, torch = kv
+    _say("rope append", dtype, d)
+    B, hkv, G = 2, 2, 2
+    S = B * hkv
+    pos = 9000
+    r, pairs, tab, store, (tab_d, pairs_d) = _rope_setup(kv, dtype, d, 64, hkv, pos + 1, 11 + d)
+    cap = np.array([4, 4, 4, 4], np.int64)
+    lens = np.array([0, 2, 4, 4], np.int32)
+    limit = np.array([0, 0, 3, -1], np.int32)
+    off, r_cap = pipeline.offsets(cap)
+    Kc = store(r.standard_normal((r_cap, d)).astype(np.float32))
+    Vc = store(r.standard_normal((r_cap, d)).astype(np.float32))
+    idx = np.arange(r_cap, dtype=np.int32) * 7
+    k_new = store(r.standard_normal((B, hkv, d)).astype(np.float32))
+    v_new = store(r.standard_normal((B, hkv, d)).astype(np.float32))
+    fused = kvsel.make_shape(B, hkv * G, hkv, d, 5000, dtype, 0.1,
+                             rope=kvsel.make_rope(tab_d, pairs_d))
+    kc_d, vc_d, idx_d = (pipeline.device_tensor(Kc), pipeline.device_tensor(Vc),
+                         pipeline.device_tensor(idx))
+    len_d = pipeline.device_tensor(lens)
+    kvsel.kvsel_append(fused, pipeline.device_tensor(k_new), pipeline.device_tensor(v_new), pos,
+                       pipeline.device_tensor(off), pipeline.device_tensor(cap),
+                       pipeline.device_tensor(limit), len_d, idx_d, kc_d, vc_d, r_cap)
+    torch.cuda.synchronize()
+    kg, vg, ig = pu.to_host(kc_d), pu.to_host(vc_d), pu.to_host(idx_d)
+    Kw, Vw, Iw = Kc.copy(), Vc.copy(), idx.copy()
+    for s in range(S):
+        b, h = divmod(s, hkv)
+        o = int(off[s])
+        rows = slice(o, o + int(lens[s]))
+        k_rot = oracle.rope_pairs(k_new[b, h][None], np.array([pos]), tab, pairs[h], dtype)[0]
+        i2, k2, v2 = oracle.append_token(idx[rows], Kc[rows], Vc[rows], pos, k_rot, v_new[b, h],
+                                         int(cap[s]), int(limit[s]))
+        Iw[o:o + len(i2)], Kw[o:o + len(i2)], Vw[o:o + len(i2)] = i2, k2, v2
+    assert np.array_equal(ig, Iw)
+    assert np.array_equal(kg.view(np.uint8), Kw.view(np.uint8)), "rotated key rows differ"
+    assert np.array_equal(vg.view(np.uint8), Vw.view(np.uint8))
