@@ -118,9 +118,15 @@ const char* kvsel_last_error(void) { return g_err; }
 
 const char* kvsel_version(void) { return "kvsel 0.1.0 gfx950"; }
 
+// Score workspace of a valid shape (unrotated queries add their rotated copy).
+static size_t score_ws(const kvsel_shape* s, int32_t w) {
+  const size_t rope = s->rope ? (size_t)s->batch * s->hq * w * s->head_dim * elem_size(s) : 0;
+  return score_workspace_bytes(s->batch * s->hkv, s->n, (s->hq / s->hkv) * w, rope);
+}
+
 size_t kvsel_score_workspace(const kvsel_shape* s, int32_t w) {
   if (!s || w < 1 || s->batch < 1 || s->hkv < 1 || s->hq < s->hkv || s->n < 1) return 0;
-  return score_workspace_bytes(s->batch * s->hkv, s->n, (s->hq / s->hkv) * w);
+  return score_ws(s, w);
 }
 
 kvsel_status kvsel_score(const kvsel_shape* s, int32_t w, int64_t q_pos0, const void* q_win,
@@ -156,7 +162,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t kvsel_lmba_workspace(const kvsel_shape* s, int32_t w) {
   if (!s || w < 1 || s->batch < 1 || s->hkv < 1 || s->hq < s->hkv || s->n < 1) return 0;
   const size_t S = (size_t)s->batch * s->hkv, R = (size_t)(s->hq / s->hkv) * w;
-  return align256(score_workspace_bytes((int)S, s->n, (int)R)) +
+  return align256(score_ws(s, w)) +
          align256(S * R * (size_t)s->n * 4) + lmba_mask_bytes((int)S, s->n);
 }
 
@@ -190,7 +196,7 @@ kvsel_status kvsel_lmba(const kvsel_shape* s, int32_t w, int64_t q_pos0, const v
     return fail(KVSEL_ENOSPC, "lmba workspace needs %zu bytes, got %zu", need, ws_bytes);
   const int R = G * w;
   char* base = static_cast<char*>(ws);
-  const size_t probs_at = align256(score_workspace_bytes(S, s->n, R));
+  const size_t probs_at = align256(score_ws(s, w));
   float* probs = reinterpret_cast<float*>(base + probs_at);
   uint32_t* mask =
       reinterpret_cast<uint32_t*>(base + probs_at + align256((size_t)S * R * s->n * 4));

@@ -318,7 +318,11 @@ hipError_t launch_append(int dtype, int head_dim, int S, int hkv, const void* k_
                          int32_t* idx, void* k_c, void* v_c, int64_t r_cap, const RopeDev& rope,
                          hipStream_t stream);
 
-size_t score_workspace_bytes(int S, int64_t n, int rows);
+// Score workspace: per-tile row statistics and row constants, then (when the
+// queries arrive unrotated, rope_bytes = their size) a rotated copy of them at
+// score_rope_offset.
+size_t score_workspace_bytes(int S, int64_t n, int rows, size_t rope_bytes = 0);
+size_t score_rope_offset(int S, int64_t n, int rows);
 hipError_t launch_score(int dtype, int head_dim, int batch, int hq, int hkv, int w,
                         int64_t n, int64_t q_pos0, float scale, const void* q_win,
                         const void* k, float* scores, void* ws, const RopeDev& rope,

@@ -63,11 +63,9 @@ __device__ __forceinline__ int acc_row(int j, int lane) {
 }
 
 // Stage the R query rows of segment (b, kvh) into LDS (rows >= R zero-filled).
-// With rope.cs set the rows arrive unrotated and are rotated here, row r at
-// position q_pos0 + r % w (the caller's next barrier publishes them).
 template <typename T, int D>
 __device__ void stage_q(const char* __restrict__ qw, int b, int kvh, int hq, int G, int w, int R,
-                        int RP, char* sq, const RopeDev& rope, int64_t q_pos0) {
+                        int RP, char* sq) {
   using Gm = SGeom<T, D>;
   const char* src = qw + ((int64_t)b * hq + (int64_t)kvh * G) * w * Gm::RB;
   constexpr int CH = Gm::RB / 16;
@@ -79,15 +77,26 @@ __device__ void stage_q(const char* __restrict__ qw, int b, int kvh, int hq, int
   // zero the pad step beyond the row (NA * 32 may exceed RB)
   for (int i = threadIdx.x; i < RP; i += kThreads)
     if (Gm::NA * 32 > Gm::RB) store16(sq + i * Gm::PITCH + Gm::RB, u32x4{0, 0, 0, 0});
-  if (rope.cs) {
-    __syncthreads();
-    constexpr int H2 = D / 2;
-    for (int i = threadIdx.x; i < R * H2; i += kThreads) {
-      const int r = i / H2, e = i - r * H2;
-      char* row = sq + r * Gm::PITCH;
-      rope_pair<T>(rope, kvh, H2, e, q_pos0 + (r % w), row, row);
-    }
-  }
+}
+
+// Unrotated window queries: a rotated copy, made once per call (every score
+// workgroup of a segment stages the same rows).  Row ((b*hq + h)*w + i) is
+// window query i of head h at position q_pos0 + i and uses the kept pairs of
+// KV head h / G; one pair per thread.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void rope_rows_kernel(const char* __restrict__ q,
+                                                             char* __restrict__ out, int64_t rows,
+                                                             int w, int hq, int G, int64_t q_pos0,
+                                                             RopeDev rope) {
+  constexpr int H2 = D / 2;
+  constexpr int RB = D * (int)sizeof(T);
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= rows * H2) return;
+  const int64_t row = i / H2;
+  const int e = (int)(i - row * H2);
+  const int t = (int)(row % w);
+  const int h = (int)((row / w) % hq);
+  rope_pair<T>(rope, h / G, H2, e, q_pos0 + t, q + row * RB, out + row * RB);
 }
 
 // Branch-free K fragment load of one key row (the caller clamps `key` into
@@ -144,7 +153,7 @@ __device__ __forceinline__ void for_each_key_block(const char* __restrict__ kseg
 template <typename T, int D, int RBN>
 __global__ __launch_bounds__(kThreads) void score_stats_kernel(
     const char* __restrict__ qw, const char* __restrict__ k, int64_t n, int hq, int hkv, int G,
-    int w, int R, int64_t q_pos0, float c, float2* __restrict__ stats, int tiles, RopeDev rope) {
+    int w, int R, int64_t q_pos0, float c, float2* __restrict__ stats, int tiles) {
   using Gm = SGeom<T, D>;
   extern __shared__ char lds_raw[];
   char* sq = lds_raw;                                   // RP * PITCH
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(
   const int b = s / hkv, kvh = s % hkv;
   constexpr int RP = RBN * 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, half = lane >> 5;
-  stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq, rope, q_pos0);
+  stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq);
   for (int r = tid; r < RP; r += kThreads) {
     const int64_t p = q_pos0 + (r % w);
     lim[r] = r < R ? (int)(p < n - 1 ? p : n - 1) : -1;   // row r sees keys <= lim[r]
@@ -265,7 +274,7 @@ template <typename T, int D, int RBN, bool PROBS = false>
 __global__ __launch_bounds__(kThreads) void score_final_kernel(
     const char* __restrict__ qw, const char* __restrict__ k, int64_t n, int hq, int hkv, int G,
     int w, int R, int64_t q_pos0, float c, const float* __restrict__ rowc,
-    float* __restrict__ scores, RopeDev rope) {
+    float* __restrict__ scores) {
   using Gm = SGeom<T, D>;
   extern __shared__ char lds_raw[];
   char* sq = lds_raw;
@@ -276,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
   const int b = s / hkv, kvh = s % hkv;
   constexpr int RP = RBN * 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, half = lane >> 5;
-  stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq, rope, q_pos0);
+  stage_q<T, D>(qw, b, kvh, hq, G, w, R, RP, sq);
   for (int r = tid; r < RP; r += kThreads) {
     krow[r] = rowc[(int64_t)s * RP + r];
     const int64_t p = q_pos0 + (r % w);
@@ -329,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
 template <typename T, int D, int RBN, bool PROBS = false>
 hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int64_t q_pos0,
                     float c, const char* qp, const char* kp, float* scores, float2* stats,
-                    float* rowc, int tiles, const RopeDev& rope, hipStream_t stream) {
+                    float* rowc, int tiles, hipStream_t stream) {
   using Gm = SGeom<T, D>;
   const size_t lds = (size_t)RBN * 32 * Gm::PITCH;
   if (lds > 65536) {
@@ -342,10 +351,10 @@ hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int6
   }
   const dim3 grid(tiles, S);
   score_stats_kernel<T, D, RBN><<<grid, dim3(kThreads), lds, stream>>>(
-      qp, kp, n, hq, hkv, G, w, R, q_pos0, c, stats, tiles, rope);
+      qp, kp, n, hq, hkv, G, w, R, q_pos0, c, stats, tiles);
   score_reduce_kernel<<<dim3(S), dim3(kReduceThreads), 0, stream>>>(stats, tiles, R, rowc);
   score_final_kernel<T, D, RBN, PROBS><<<grid, dim3(kThreads), lds, stream>>>(
-      qp, kp, n, hq, hkv, G, w, R, q_pos0, c, rowc, scores, rope);
+      qp, kp, n, hq, hkv, G, w, R, q_pos0, c, rowc, scores);
   return hipGetLastError();
 }
 
@@ -361,9 +370,17 @@ hipError_t run(int batch, int hq, int hkv, int w, int64_t n, int64_t q_pos0, flo
   const float c = scale * kLog2e;
   auto qp = static_cast<const char*>(q_win);
   auto kp = static_cast<const char*>(k);
+  if (rope.cs) {   // rotated copy of the queries after the statistics in the workspace
+    char* qr = static_cast<char*>(ws) + score_rope_offset(S, n, R);
+    const int64_t rows = (int64_t)batch * hq * w;
+    const int64_t blocks = (rows * (D / 2) + kThreads - 1) / kThreads;
+    rope_rows_kernel<T, D><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(
+        qp, qr, rows, w, hq, hq / hkv, q_pos0, rope);
+    qp = qr;
+  }
 #define KVSEL_ROWS(RBN) \
   return run_rows<T, D, RBN, PROBS>(S, hq, hkv, G, w, R, n, q_pos0, c, qp, kp, scores, stats, \
-                                    rowc, tiles, rope, stream)
+                                    rowc, tiles, stream)
   switch (RP / 32) {
     case 1: KVSEL_ROWS(1);
     case 2: KVSEL_ROWS(2);
@@ -375,10 +392,20 @@ hipError_t run(int batch, int hq, int hkv, int w, int64_t n, int64_t q_pos0, flo
 
 }  // namespace
 
-size_t score_workspace_bytes(int S, int64_t n, int rows) {
+size_t score_rope_offset(int S, int64_t n, int rows) {
   const int RP = padded_rows(rows);
   const int64_t tiles = (n + kTileKeys - 1) / kTileKeys;
-  return (size_t)S * tiles * RP * sizeof(float2) + (size_t)S * RP * sizeof(float);
+  const size_t stats = (size_t)S * tiles * RP * sizeof(float2) + (size_t)S * RP * sizeof(float);
+  return (stats + 255) & ~(size_t)255;
+}
+
+size_t score_workspace_bytes(int S, int64_t n, int rows, size_t rope_bytes) {
+  if (!rope_bytes) {
+    const int RP = padded_rows(rows);
+    const int64_t tiles = (n + kTileKeys - 1) / kTileKeys;
+    return (size_t)S * tiles * RP * sizeof(float2) + (size_t)S * RP * sizeof(float);
+  }
+  return score_rope_offset(S, n, rows) + rope_bytes;
 }
 
 hipError_t launch_probs(int dtype, int head_dim, int batch, int hq, int hkv, int w, int64_t n,

@@ -676,12 +676,14 @@ def test_rope_score_and_lmba_fused(kv, dtype, d, half, G, w, n):
     fused = kvsel.make_shape(B, hkv * G, hkv, d, n, dtype, 1 / math.sqrt(d),
                              rope=kvsel.make_rope(tab_d, pairs_d))
     Kd = pipeline.device_tensor(K)
-    ws = torch.empty(kvsel.kvsel_score_workspace(plain, w), dtype=torch.uint8, device="cuda")
+    # unrotated queries need room for their rotated copy: the fused shape's size serves both
+    assert kvsel.kvsel_score_workspace(fused, w) > kvsel.kvsel_score_workspace(plain, w)
+    ws = torch.empty(kvsel.kvsel_score_workspace(fused, w), dtype=torch.uint8, device="cuda")
     s1 = torch.empty(B * hkv * n, dtype=torch.float32, device="cuda")
     s2 = torch.empty_like(s1)
     kvsel.kvsel_score(fused, w, q_pos0, pipeline.device_tensor(q), Kd, s1, ws)
     kvsel.kvsel_score(plain, w, q_pos0, pipeline.device_tensor(q_rot), Kd, s2, ws)
-    lws = torch.empty(kvsel.kvsel_lmba_workspace(plain, w), dtype=torch.uint8, device="cuda")
+    lws = torch.empty(kvsel.kvsel_lmba_workspace(fused, w), dtype=torch.uint8, device="cuda")
     l1 = torch.empty(B * hkv * G * w, dtype=torch.int32, device="cuda")
     l2 = torch.empty_like(l1)
     kvsel.kvsel_lmba(fused, w, q_pos0, pipeline.device_tensor(q), Kd, l1, lws)
