@@ -492,15 +492,23 @@ def test_append_steps_match_oracle(kv, dtype, d):
         assert np.all(g_idx[~used] == -7), f"append step {t}: rows outside segments written"
 
 
-def test_c3_decode_loop_with_append(kv):
+@pytest.mark.parametrize("fused", [False, True])
+def test_c3_decode_loop_with_append(kv, fused):
     """FastGen serving loop on a reduced C3 layer: policy select, compact, then
     three decode steps; before each step the new token joins the cache under
     its head rule (local: sliding window, special: not added, global: grows),
-    and the step's decode output is checked against the oracle."""
+    and the step's decode output is checked against the oracle.  fused: the
+    new key and the queries arrive unrotated and the library rotates them with
+    the segment's kept RoPE pairs (RAP §3); the oracle rotates them itself."""
     kvsel, pipeline, torch = kv
     steps = 3
     cfg = kvsynth.get_config(3, batch=2, n=3000 + 5)
-    _say(cfg.name, "decode loop with append, n", cfg.n)
+    _say(cfg.name, "decode loop with append, n", cfg.n, "fused RoPE" if fused else "")
+    if fused:
+        pairs = np.stack([kvsynth.kept_pairs(cfg, 0, kvh)
+                          for kvh in range(cfg.hkv)]).astype(np.int32)
+        tab = kvsynth.rope_table(cfg.n + steps, cfg.d_rope // 2)
+        tab_d, pairs_d = pipeline.device_tensor(tab), pipeline.device_tensor(pairs)
     inputs = kvsynth.layer_inputs(cfg, 0)
     run = pipeline.build_layer(cfg, inputs, slack=steps)
     run.select()
@@ -523,23 +531,33 @@ def test_c3_decode_loop_with_append(kv):
         segs.append([idx, Kc, Vc])
     worst = 0.0
     for t in range(steps):
-        st = kvsynth.step_inputs(cfg, 0, t)
-        run.append(pipeline.device_tensor(st["k_new"]), pipeline.device_tensor(st["v_new"]),
-                   st["pos"], t_lim)
+        st = kvsynth.step_inputs(cfg, 0, t, rotated=not fused)
+        pos = st["pos"]
+        shape = run.shape
+        if fused:
+            sh = run.shape
+            shape = kvsel.make_shape(sh.batch, sh.hq, sh.hkv, sh.head_dim, sh.n, sh.dtype, sh.scale,
+                                     rope=kvsel.make_rope(tab_d, pairs_d, q_pos=pos))
+        kvsel.kvsel_append(shape, pipeline.device_tensor(st["k_new"]),
+                           pipeline.device_tensor(st["v_new"]), pos, run.seg_off, run.seg_cap,
+                           t_lim, run.seg_len, run.idx, run.k_c, run.v_c, run.r_cap)
         q = pipeline.device_tensor(st["q"])
-        kvsel.kvsel_decode_attn(run.shape, q, run.k_c, run.v_c, run.seg_off, run.seg_len,
+        kvsel.kvsel_decode_attn(shape, q, run.k_c, run.v_c, run.seg_off, run.seg_len,
                                 run.r_cap, run.out, run.ws_dec)
         torch.cuda.synchronize()
         out = pu.to_host(run.out)
+        rot = (lambda x, kvh: oracle.rope_pairs(x[None], np.array([pos]), tab, pairs[kvh],
+                                                cfg.dtype)[0]) if fused else (lambda x, kvh: x)
         for s in range(S):
             b, kvh = divmod(s, cfg.hkv)
-            segs[s] = list(oracle.append_token(segs[s][0], segs[s][1], segs[s][2], st["pos"],
-                                               st["k_new"][b, kvh], st["v_new"][b, kvh],
+            segs[s] = list(oracle.append_token(segs[s][0], segs[s][1], segs[s][2], pos,
+                                               rot(st["k_new"][b, kvh], kvh), st["v_new"][b, kvh],
                                                int(caps[s]), int(limits[s])))
             Kc, Vc = oracle.to_f64(segs[s][1]), oracle.to_f64(segs[s][2])
             for g in range(cfg.G):
                 h_ = kvh * cfg.G + g
-                want = oracle.decode_attention(oracle.to_f64(st["q"][b, h_]), Kc, Vc, cfg.scale)
+                want = oracle.decode_attention(oracle.to_f64(rot(st["q"][b, h_], kvh)), Kc, Vc,
+                                               cfg.scale)
                 err = float(np.max(np.abs(out[b, h_] - want)))
                 worst = max(worst, err)
                 assert err <= pu.OUT_ATOL[cfg.dtype], f"step {t} seg {s} head {g}: err {err}"
