@@ -190,3 +190,89 @@ def build_layer(cfg, inputs: dict, *, budget=None, slack: int = 0, local_chunks:
     run.r_cap = r_cap
     run.keep = keep
     return run.allocate()
+
+
+@dataclass
+class ServingLoop:
+    """Decode-time maintenance of one layer's selection (ZigZagkv: the token
+    score is the attention of the last w queries, Eq. 7; FastGen: the per-head
+    rule keeps holding while generating).  The full cache stays resident in
+    HBM; every step the new token joins it and the compacted cache, and the
+    decode reads the compacted cache; every `period` steps the score is taken
+    again from the last w decode queries over the full cache and the
+    selection and compaction are redone from it.  `period` == w, so the
+    window buffer holds exactly the queries of the last period, in order.
+
+    All arithmetic runs in the library's kernels (append, decode, score,
+    select, compact); this class only owns buffers and orders the calls.
+    """
+    run: LayerRun            # the compacted cache (TOPB), slack >= period
+    n0: int                  # tokens before the first decode step
+    k_full: object = None    # [b][hkv][n_cap][d], rows >= current length zero
+    v_full: object = None
+    full_shape: K.Shape | None = None
+    full_off: object = None
+    full_cap: object = None
+    full_len: object = None
+    full_idx: object = None
+    q_buf: object = None     # [b][hq][w][d]: the last w decode queries
+    period: int = 0
+    t: int = 0
+    reselections: int = 0
+
+    @staticmethod
+    def start(run: LayerRun, k, v, n0: int, steps: int) -> "ServingLoop":
+        """Full cache of n0 tokens (k, v: [b][hkv][n0][d] device tensors) with
+        room for `steps` more; the compacted run must already hold a selection."""
+        import torch
+        sh = run.shape
+        B, hkv, d, w = sh.batch, sh.hkv, sh.head_dim, run.w
+        assert run.mode == K.KVSEL_SEL_TOPB and w >= 1 and run.q_win is not None
+        assert not sh.rope, "the loop takes rotated queries and keys"
+        n_cap = n0 + steps
+        S = B * hkv
+        kf = torch.zeros((B, hkv, n_cap, d), dtype=k.dtype, device=k.device)
+        vf = torch.zeros_like(kf)
+        kf[:, :, :n0] = k.view(B, hkv, n0, d)
+        vf[:, :, :n0] = v.view(B, hkv, n0, d)
+        full_shape = K.make_shape(B, sh.hq, hkv, d, n_cap, sh.dtype, sh.scale)
+        off = device_tensor(np.arange(S, dtype=np.int64) * n_cap, k.device)
+        cap = device_tensor(np.full(S, n_cap, np.int64), k.device)
+        ln = device_tensor(np.full(S, n0, np.int32), k.device)
+        idx = device_tensor(np.tile(np.arange(n_cap, dtype=np.int32), S), k.device)
+        loop = ServingLoop(run, n0, kf, vf, full_shape, off, cap, ln, idx, period=w)
+        loop.q_buf = torch.zeros((B, sh.hq, w, d), dtype=k.dtype, device=k.device)
+        # scores and score workspace sized for the full cache
+        run.scores = torch.empty(S * n_cap, dtype=torch.float32, device=k.device)
+        run.ws_score = torch.empty(max(K.kvsel_score_workspace(full_shape, w), 1),
+                                   dtype=torch.uint8, device=k.device)
+        return loop
+
+    def step(self, k_new, v_new, q, stream=None):
+        """Decode step at position n0 + t: k_new, v_new [b][hkv][d], q [b][hq][d].
+        Returns True when the selection was redone after this step's decode."""
+        run = self.run
+        sh = run.shape
+        pos = self.n0 + self.t
+        full = self.full_shape
+        K.kvsel_append(full, k_new, v_new, pos, self.full_off, self.full_cap, None,
+                       self.full_len, self.full_idx, self.k_full.view(-1, sh.head_dim),
+                       self.v_full.view(-1, sh.head_dim), self.full_len.numel() * full.n, stream)
+        K.kvsel_append(sh, k_new, v_new, pos, run.seg_off, run.seg_cap, None, run.seg_len,
+                       run.idx, run.k_c, run.v_c, run.r_cap, stream)
+        self.q_buf[:, :, self.t % self.period].copy_(q.view(sh.batch, sh.hq, sh.head_dim))
+        K.kvsel_decode_attn(sh, q, run.k_c, run.v_c, run.seg_off, run.seg_len, run.r_cap,
+                            run.out, run.ws_dec, stream)
+        self.t += 1
+        if self.t % self.period:
+            return False
+        # re-score from the last w queries (positions pos-w+1 .. pos) over the full cache;
+        # keys past pos are masked by the causal window and score 0
+        K.kvsel_score(self.full_shape, run.w, pos - run.w + 1, self.q_buf, self.k_full,
+                      run.scores, run.ws_score, stream)
+        K.kvsel_select(self.full_shape, run.params, run.scores, run.seg_off, run.seg_len,
+                       run.idx, run.r_cap, stream)
+        K.kvsel_compact(self.full_shape, self.k_full, self.v_full, run.seg_off, run.seg_len,
+                        run.idx, run.k_c, run.v_c, run.r_cap, stream)
+        self.reselections += 1
+        return True

@@ -798,3 +798,78 @@ def test_rope_append_rotates_new_key(kv, dtype, d):
     assert np.array_equal(ig, Iw)
     assert np.array_equal(kg.view(np.uint8), Kw.view(np.uint8)), "rotated key rows differ"
     assert np.array_equal(vg.view(np.uint8), Vw.view(np.uint8))
+
+
+# ---------------------------------------------------------------------------
+# serving loop: periodic re-scoring and re-selection over the resident full cache
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid,over,steps", [(0, {}, 20),
+                                            (1, dict(n=3000, budget=400, w=16, batch=2), 33)])
+def test_serving_loop_periodic_reselection(kv, cid, over, steps):
+    """Each step the new token joins the full and the compacted cache and the
+    decode reads the compacted cache (checked against the oracle over the
+    GPU's kept rows); every w steps the score of the last w decode queries over
+    the full cache is taken again (oracle within the score bar, keys not yet
+    generated score 0) and the top-B selection (tie band) and compaction
+    (bit-exact) are redone."""
+    kvsel, pipeline, torch = kv
+    cfg = kvsynth.get_config(cid, **over)
+    _say(cfg.name, "serving loop, n", cfg.n, "w", cfg.w, "steps", steps)
+    inputs = kvsynth.layer_inputs(cfg, 0)
+    run = pipeline.build_layer(cfg, inputs, slack=cfg.w)
+    run.score(); run.select(); run.compact()
+    loop = pipeline.ServingLoop.start(run, run.k, run.v, cfg.n, steps)
+    torch.cuda.synchronize()
+    S, G, w, B = cfg.batch * cfg.hkv, cfg.G, cfg.w, cfg.budget
+    Kf = [[inputs["K"][b, h] for h in range(cfg.hkv)] for b in range(cfg.batch)]
+    Vf = [[inputs["V"][b, h] for h in range(cfg.hkv)] for b in range(cfg.batch)]
+    h0 = _host(run)
+    sel = {s: h0["idx"][int(h0["seg_off"][s]):int(h0["seg_off"][s]) + int(h0["seg_len"][s])]
+           .astype(np.int64) for s in range(S)}
+    since = cfg.n          # first position appended after the current selection
+    qs = []
+    worst = 0.0
+    for t in range(steps):
+        st = kvsynth.step_inputs(cfg, 0, t)
+        pos = st["pos"]
+        redone = loop.step(pipeline.device_tensor(st["k_new"]), pipeline.device_tensor(st["v_new"]),
+                           pipeline.device_tensor(st["q"]))
+        torch.cuda.synchronize()
+        qs.append(st["q"])
+        h = _host(run)
+        for s in range(S):
+            b, kvh = divmod(s, cfg.hkv)
+            Kf[b][kvh] = np.concatenate([Kf[b][kvh], st["k_new"][b, kvh][None]])
+            Vf[b][kvh] = np.concatenate([Vf[b][kvh], st["v_new"][b, kvh][None]])
+            # this step's decode read the selection plus every token appended since
+            idx = np.concatenate([sel[s], np.arange(since, pos + 1)])
+            if not redone:
+                o, ln = int(h["seg_off"][s]), int(h["seg_len"][s])
+                assert np.array_equal(h["idx"][o:o + ln], idx), f"t={t} seg {s}: kept rows"
+                pu.check_compact(h["k_c"][o:o + ln], h["v_c"][o:o + ln], Kf[b][kvh], Vf[b][kvh],
+                                 idx, f"t={t} seg {s}")
+            err = pu.check_decode(h["out"][b, kvh * G:(kvh + 1) * G],
+                                  st["q"][b, kvh * G:(kvh + 1) * G], Kf[b][kvh], Vf[b][kvh], idx,
+                                  cfg.scale, cfg.dtype, f"t={t} seg {s}")
+            worst = max(worst, err)
+        if redone:
+            assert t % w == w - 1
+            sc = h["scores"].reshape(S, -1)
+            win = np.stack(qs[-w:], axis=2)           # [b][hq][w][d], positions pos-w+1 .. pos
+            for s in range(S):
+                b, kvh = divmod(s, cfg.hkv)
+                o, ln = int(h["seg_off"][s]), int(h["seg_len"][s])
+                idx = h["idx"][o:o + ln].astype(np.int64)
+                ref = oracle.window_scores(oracle.to_f64(win[b, kvh * G:(kvh + 1) * G]),
+                                           oracle.to_f64(Kf[b][kvh]), cfg.scale, pos - w + 1)
+                assert not sc[s, pos + 1:].any(), "keys not yet generated must score 0"
+                pu.check_scores(sc[s, :pos + 1], ref, G * w, f"t={t} seg {s}")
+                pu.check_topb_selection(idx, sc[s, :pos + 1], ref, B, f"t={t} seg {s}")
+                pu.check_compact(h["k_c"][o:o + ln], h["v_c"][o:o + ln], Kf[b][kvh], Vf[b][kvh],
+                                 idx, f"t={t} seg {s}")
+                sel[s] = idx
+            since = pos + 1
+    assert loop.reselections == steps // w
+    print(f"  {cfg.name}: {loop.reselections} re-selections, decode max abs err {worst:.2e}",
+          flush=True)
