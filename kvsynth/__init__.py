@@ -19,6 +19,7 @@ from .gen import (
     chunk_ends,
     step_token,
     step_inputs,
+    chunk_step_inputs,
     kept_pairs,
     rope_table,
     HEAD_GLOBAL,
@@ -29,5 +30,5 @@ from .gen import (
 __all__ = [
     "CONFIGS", "Config", "get_config", "bf16_bits_to_f32", "f32_to_bf16_bits",
     "layer_inputs", "segment_inputs", "zigzag_profile", "head_kinds",
-    "special_positions", "chunk_ends", "step_token", "step_inputs", "kept_pairs", "rope_table", "HEAD_GLOBAL", "HEAD_LOCAL", "HEAD_SPECIAL",
+    "special_positions", "chunk_ends", "step_token", "step_inputs", "chunk_step_inputs", "kept_pairs", "rope_table", "HEAD_GLOBAL", "HEAD_LOCAL", "HEAD_SPECIAL",
 ]

@@ -33,6 +33,7 @@ SEED_ROOT = 20261203
 T_U, T_K, T_V, T_QWIN, T_QDEC, T_HH, T_PROFILE, T_HHFRAC, T_HEADKIND, T_SPECIAL, \
     T_PAIRS, T_CHUNKS, T_PROJ = range(13)
 T_STEP = 13   # decode step t draws tensor ids T_STEP + 3t (key), + 1 (value), + 2 (queries)
+T_CSTEP = 1 << 20   # C4 decode step t: tensor id T_CSTEP + t draws the chunk-boundary flag
 
 HEAD_GLOBAL, HEAD_LOCAL, HEAD_SPECIAL = 0, 1, 2
 
@@ -254,6 +255,21 @@ def step_inputs(cfg: Config, layer: int, t: int, rotated: bool = True) -> dict:
             kn[b, kvh], vn[b, kvh], q[b, kvh * G:(kvh + 1) * G] = step_token(cfg, layer, b, kvh, t,
                                                                               rotated)
     return {"k_new": kn, "v_new": vn, "q": q, "pos": cfg.n + t}
+
+
+def chunk_step_inputs(cfg: Config, layer: int, t: int) -> dict:
+    """C4 decode step t: step_inputs plus whether token n + t closes a chunk
+    (Bernoulli(1 / chunk_mean): the Geometric chunk lengths continued past n,
+    one draw per layer shared by the batch), the chunk key that token gives
+    (its key times the projection) [b][hkv][chunk_dim] and each query head's
+    chunk query (its decode query times the projection) [b][hq][1][chunk_dim]."""
+    st = step_inputs(cfg, layer, t)
+    P = chunk_projection(cfg, layer)
+    boundary = bool(_rng(cfg, layer, 0, 0, T_CSTEP + t).random() < 1.0 / cfg.chunk_mean)
+    ck = (stored_to_f32(cfg, st["k_new"]).astype(np.float64) @ P).astype(np.float32)
+    cq = (stored_to_f32(cfg, st["q"]).astype(np.float64) @ P).astype(np.float32)
+    st.update(boundary=boundary, chunk_key=_store(cfg, ck), chunk_q=_store(cfg, cq[:, :, None, :]))
+    return st
 
 
 def segment_chunk_inputs(cfg: Config, K_seg: np.ndarray, qdec_seg: np.ndarray,

@@ -276,3 +276,117 @@ class ServingLoop:
                         run.idx, run.k_c, run.v_c, run.r_cap, stream)
         self.reselections += 1
         return True
+
+
+@dataclass
+class ChunkServingLoop:
+    """ChunkLLM decode loop (ChunkLLM page, §2.3: by intra-chunk attention
+    consistency the chunk selection is redone only when the current token
+    closes a chunk).  The full cache stays resident; every step the new token
+    joins it and the compacted cache and the decode reads the compacted
+    cache.  When the token closes a chunk, its chunk key joins the chunk keys,
+    the chunks are scored with this step's chunk query, the `local` last
+    chunks plus the `top` best others are selected, and the compacted cache is
+    rebuilt from the full cache.  All arithmetic runs in the library's
+    kernels; this class owns buffers and orders the calls (the torch copies
+    below only move data into the layouts the calls take)."""
+    run: LayerRun                 # chunk mode, count form (top_chunks > 0)
+    n0: int
+    local: int
+    top: int
+    k_full: object = None
+    v_full: object = None
+    full_shape: K.Shape | None = None
+    full_off: object = None
+    full_cap: object = None
+    full_len: object = None
+    full_idx: object = None
+    ck: object = None             # chunk keys [b][hkv][nc_cap][chunk_dim]
+    ends: object = None           # chunk ends [b][nc_cap] int64
+    ck_shape: K.Shape | None = None
+    sc: object = None             # chunk scores [b*hkv][nc_cap]
+    sc_c: object = None           # the same, [b*hkv][nc] contiguous for select
+    ends_c: object = None
+    ws: object = None
+    nc: int = 0
+    t: int = 0
+    reselections: int = 0
+
+    @staticmethod
+    def start(run: LayerRun, k, v, n0: int, steps: int, chunk_keys, ends: np.ndarray,
+              local: int, top: int) -> "ChunkServingLoop":
+        """k, v [b][hkv][n0][d] and chunk_keys [b][hkv][nc0][chunk_dim] device
+        tensors, ends [b][nc0] host int64 (last == n0); the run must hold the
+        selection over them; `steps` bounds the tokens and chunks to come."""
+        import torch
+        sh, ss = run.shape, run.score_shape
+        B, hkv, d = sh.batch, sh.hkv, sh.head_dim
+        assert run.mode == K.KVSEL_SEL_CHUNK and top > 0 and not sh.rope
+        S = B * hkv
+        n_cap, nc0 = n0 + steps, ends.shape[1]
+        nc_cap = nc0 + steps
+        kf = torch.zeros((B, hkv, n_cap, d), dtype=k.dtype, device=k.device)
+        vf = torch.zeros_like(kf)
+        kf[:, :, :n0] = k.view(B, hkv, n0, d)
+        vf[:, :, :n0] = v.view(B, hkv, n0, d)
+        lp = ChunkServingLoop(run, n0, local, top, kf, vf,
+                              K.make_shape(B, sh.hq, hkv, d, n_cap, sh.dtype, sh.scale),
+                              device_tensor(np.arange(S, dtype=np.int64) * n_cap, k.device),
+                              device_tensor(np.full(S, n_cap, np.int64), k.device),
+                              device_tensor(np.full(S, n0, np.int32), k.device),
+                              device_tensor(np.tile(np.arange(n_cap, dtype=np.int32), S),
+                                            k.device))
+        cd = ss.head_dim
+        lp.ck = torch.zeros((B, hkv, nc_cap, cd), dtype=k.dtype, device=k.device)
+        lp.ck[:, :, :nc0] = chunk_keys.view(B, hkv, nc0, cd)
+        e = np.zeros((B, nc_cap), np.int64)
+        e[:, :nc0] = ends
+        lp.ends = device_tensor(e, k.device)
+        lp.ck_shape = K.make_shape(B, ss.hq, hkv, cd, nc_cap, ss.dtype, ss.scale)
+        lp.sc = torch.empty(S * nc_cap, dtype=torch.float32, device=k.device)
+        lp.sc_c = torch.empty_like(lp.sc)
+        lp.ends_c = torch.empty_like(lp.ends).view(-1)
+        lp.ws = torch.empty(max(K.kvsel_score_workspace(lp.ck_shape, 1), 1), dtype=torch.uint8,
+                            device=k.device)
+        lp.nc = nc0
+        return lp
+
+    def step(self, k_new, v_new, q, boundary: bool, chunk_key=None, chunk_q=None,
+             stream=None) -> bool:
+        """Decode step at position n0 + t.  When `boundary`, chunk_key
+        [b][hkv][chunk_dim] and chunk_q [b][hq][1][chunk_dim] are the closing
+        token's chunk key and chunk query.  Returns True when the selection was
+        redone (after this step's decode)."""
+        run, sh = self.run, self.run.shape
+        pos = self.n0 + self.t
+        B, hkv = sh.batch, sh.hkv
+        S = B * hkv
+        K.kvsel_append(self.full_shape, k_new, v_new, pos, self.full_off, self.full_cap, None,
+                       self.full_len, self.full_idx, self.k_full.view(-1, sh.head_dim),
+                       self.v_full.view(-1, sh.head_dim), S * self.full_shape.n, stream)
+        K.kvsel_append(sh, k_new, v_new, pos, run.seg_off, run.seg_cap, None, run.seg_len,
+                       run.idx, run.k_c, run.v_c, run.r_cap, stream)
+        K.kvsel_decode_attn(sh, q, run.k_c, run.v_c, run.seg_off, run.seg_len, run.r_cap,
+                            run.out, run.ws_dec, stream)
+        self.t += 1
+        if not boundary:
+            return False
+        nc_cap = self.ends.shape[1]
+        assert self.nc < nc_cap
+        self.ends[:, self.nc] = pos + 1
+        self.ck[:, :, self.nc].copy_(chunk_key.view(B, hkv, -1))
+        self.nc += 1
+        nc = self.nc
+        # chunk attention of this step's chunk query over the nc chunk keys (the
+        # causal window masks the free key slots)
+        K.kvsel_score(self.ck_shape, 1, nc - 1, chunk_q, self.ck, self.sc, self.ws, stream)
+        self.sc_c[:S * nc].view(S, nc).copy_(self.sc.view(S, nc_cap)[:, :nc])
+        self.ends_c[:B * nc].view(B, nc).copy_(self.ends[:, :nc])
+        params = K.select_params(K.KVSEL_SEL_CHUNK, n_chunks=nc, chunk_end=self.ends_c,
+                                 local_chunks=self.local, top_chunks=self.top)
+        K.kvsel_select(self.full_shape, params, self.sc_c, run.seg_off, run.seg_len, run.idx,
+                       run.r_cap, stream)
+        K.kvsel_compact(self.full_shape, self.k_full, self.v_full, run.seg_off, run.seg_len,
+                        run.idx, run.k_c, run.v_c, run.r_cap, stream)
+        self.reselections += 1
+        return True

@@ -873,3 +873,81 @@ def test_serving_loop_periodic_reselection(kv, cid, over, steps):
     assert loop.reselections == steps // w
     print(f"  {cfg.name}: {loop.reselections} re-selections, decode max abs err {worst:.2e}",
           flush=True)
+
+
+def test_chunk_serving_loop_reselects_at_boundaries(kv):
+    """ChunkLLM decode loop on a reduced C4 layer (§2.3, ICAC): 4 local chunks
+    + the 16 best others; the selection is redone only at the steps whose token
+    closes a chunk.  At those steps the chunk scores (oracle within the score
+    bar), the chunk selection (tie band) and the compaction (bit-exact) are
+    checked; every step's decode is checked against the oracle over the rows
+    the GPU kept (the selection plus the tokens appended since)."""
+    kvsel, pipeline, torch = kv
+    local, top, steps = 4, 16, 100
+    cfg = kvsynth.get_config(4, n=3000)
+    _say(cfg.name, "chunk serving loop, n", cfg.n, "steps", steps)
+    inputs = kvsynth.layer_inputs(cfg, 0)
+    run = pipeline.build_layer(cfg, inputs, local_chunks=local, top_chunks=top,
+                               slack=(local + top + 1) * steps)
+    run.run()
+    loop = pipeline.ChunkServingLoop.start(run, run.k, run.v, cfg.n, steps, run.score_keys,
+                                           np.asarray(inputs["chunk_end"], np.int64), local, top)
+    torch.cuda.synchronize()
+    S, G, hkv = cfg.batch * cfg.hkv, cfg.G, cfg.hkv
+    Kf = [[inputs["K"][b, h] for h in range(hkv)] for b in range(cfg.batch)]
+    Vf = [[inputs["V"][b, h] for h in range(hkv)] for b in range(cfg.batch)]
+    CK = [[inputs["chunk_keys"][b, h] for h in range(hkv)] for b in range(cfg.batch)]
+    ends = [np.asarray(inputs["chunk_end"][b], np.int64) for b in range(cfg.batch)]
+    h0 = _host(run)
+    sel = {s: h0["idx"][int(h0["seg_off"][s]):int(h0["seg_off"][s]) + int(h0["seg_len"][s])]
+           .astype(np.int64) for s in range(S)}
+    since = cfg.n
+    worst, nb = 0.0, 0
+    for t in range(steps):
+        st = kvsynth.chunk_step_inputs(cfg, 0, t)
+        pos = st["pos"]
+        redone = loop.step(pipeline.device_tensor(st["k_new"]), pipeline.device_tensor(st["v_new"]),
+                           pipeline.device_tensor(st["q"]), st["boundary"],
+                           pipeline.device_tensor(st["chunk_key"]),
+                           pipeline.device_tensor(st["chunk_q"]))
+        torch.cuda.synchronize()
+        assert redone == st["boundary"]
+        h = _host(run)
+        for s in range(S):
+            b, kvh = divmod(s, hkv)
+            Kf[b][kvh] = np.concatenate([Kf[b][kvh], st["k_new"][b, kvh][None]])
+            Vf[b][kvh] = np.concatenate([Vf[b][kvh], st["v_new"][b, kvh][None]])
+            idx = np.concatenate([sel[s], np.arange(since, pos + 1)])
+            if not redone:
+                o, ln = int(h["seg_off"][s]), int(h["seg_len"][s])
+                assert np.array_equal(h["idx"][o:o + ln], idx), f"t={t} seg {s}: kept rows"
+            err = pu.check_decode(h["out"][b, kvh * G:(kvh + 1) * G],
+                                  st["q"][b, kvh * G:(kvh + 1) * G], Kf[b][kvh], Vf[b][kvh], idx,
+                                  cfg.scale, cfg.dtype, f"t={t} seg {s}")
+            worst = max(worst, err)
+        if not redone:
+            continue
+        nb += 1
+        nc = loop.nc
+        sc = pu.to_host(loop.sc).reshape(S, -1)
+        for b in range(cfg.batch):
+            ends[b] = np.append(ends[b], pos + 1)
+            assert len(ends[b]) == nc
+        for s in range(S):
+            b, kvh = divmod(s, hkv)
+            CK[b][kvh] = np.concatenate([CK[b][kvh], st["chunk_key"][b, kvh][None]])
+            o, ln = int(h["seg_off"][s]), int(h["seg_len"][s])
+            idx = h["idx"][o:o + ln].astype(np.int64)
+            ref = oracle.window_scores(oracle.to_f64(st["chunk_q"][b, kvh * G:(kvh + 1) * G]),
+                                       oracle.to_f64(CK[b][kvh]), cfg.scale, nc - 1)
+            assert not sc[s, nc:].any()
+            pu.check_scores(sc[s, :nc], ref, G, f"t={t} seg {s} chunk scores")
+            pu.check_chunk_selection(idx, sc[s, :nc], ref, ends[b], 0, f"t={t} seg {s}",
+                                     local=local, top=top)
+            pu.check_compact(h["k_c"][o:o + ln], h["v_c"][o:o + ln], Kf[b][kvh], Vf[b][kvh], idx,
+                             f"t={t} seg {s}")
+            sel[s] = idx
+        since = pos + 1
+    assert nb >= 2 and loop.reselections == nb
+    print(f"  {cfg.name}: {nb} boundary re-selections in {steps} steps, decode max abs err "
+          f"{worst:.2e}", flush=True)
