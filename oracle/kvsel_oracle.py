@@ -47,7 +47,7 @@ __all__ = [
     "zigzag_budgets", "score_order", "select_topb", "select_chunks",
     "select_policy", "compact", "decode_attention", "decode_partial",
     "combine_partials", "append_token", "window_probabilities", "attention_loss",
-    "round_bf16", "rope_pairs",
+    "round_bf16", "rope_pairs", "vote_key",
     "HEAD_GLOBAL", "HEAD_LOCAL", "HEAD_SPECIAL",
 ]
 
@@ -287,6 +287,32 @@ def select_chunks(chunk_scores: np.ndarray, chunk_end: np.ndarray, keep_tokens: 
     if not chosen:
         return np.zeros(0, np.int64)
     return np.concatenate([np.arange(starts[c], ends[c]) for c in chosen]).astype(np.int64)
+
+
+def vote_key(layer_scores, top_k: int, group: int) -> np.ndarray:
+    """Layer-wise chunk voting [CK §2.3, where the rule is given only in words;
+    the reading taken]: each of the L layers votes for its own top_k chunks
+    (select_topb on that layer's chunk scores); the shared set is then the
+    chunks with the most votes, ties to the larger chunk attention summed over
+    the layers, then to the lower index.  Expressed as one key per chunk,
+
+        key = votes + 0.5 * (sum_l s_l / (L * group))      (every step fp32,
+                                                           layers summed in order)
+
+    where each s_l <= group (a chunk's attention summed over the group's query
+    heads), so the fraction stays below the next vote count.  Keeping the
+    local chunks plus the top_k best keys is select_chunks(key, ends, 0, local,
+    top_k).  layer_scores [L][nc] are taken as fp32; returns float32 keys."""
+    S = np.asarray(layer_scores, np.float32)
+    L, nc = S.shape
+    votes = np.zeros(nc, np.int64)
+    for layer in range(L):
+        votes[select_topb(S[layer].astype(np.float64), top_k)] += 1
+    acc = np.zeros(nc, np.float32)
+    for layer in range(L):
+        acc = (acc + S[layer]).astype(np.float32)
+    frac = (acc / np.float32(L * group)).astype(np.float32)
+    return (votes.astype(np.float32) + np.float32(0.5) * frac).astype(np.float32)
 
 
 def select_policy(kind: int, n: int, local_window: int, special_pos) -> np.ndarray:

@@ -598,3 +598,67 @@ def test_rope_preserves_pair_norms_and_relative_position():
         return float(a @ b)
     for m, j, dlt in [(500, 20, 300), (4000, 3999, 4000), (100, 100, 8000)]:
         assert abs(logit(m, j) - logit(m + dlt, j + dlt)) < 1e-4 * (np.linalg.norm(q) * np.linalg.norm(k))
+
+
+# ---------------------------------------------------------------------------
+# ChunkLLM layer-wise voting (CK §2.3; the rule is only described in words)
+# ---------------------------------------------------------------------------
+
+def _voted_chunks(layer_scores, k, local, ends):
+    key = oracle.vote_key(layer_scores, k, group=1)
+    toks = oracle.select_chunks(key, ends, 0, local, k)
+    return sorted(set(np.searchsorted(ends, toks, side="right").tolist()))
+
+
+def test_vote_hand_worked():
+    # three layers, six one-token chunks, top-2 per layer:
+    #   layer 0 votes {3, 1}, layer 1 {2, 3}, layer 2 {3, 0}: chunk 3 has 3 votes,
+    #   chunks 0, 1, 2 one each; summed attention 1.0, 0.8, 1.1 -> chunk 2 joins
+    s = [[0.1, 0.5, 0.2, 0.9, 0.0, 0.0],
+         [0.3, 0.1, 0.8, 0.7, 0.0, 0.1],
+         [0.6, 0.2, 0.1, 0.65, 0.05, 0.0]]
+    ends = np.arange(1, 7)
+    assert _voted_chunks(s, 2, 0, ends) == [2, 3]
+    assert _voted_chunks(s, 2, 1, ends) == [2, 3, 5]          # chunk 5 forced (local)
+    assert _voted_chunks(s, 1, 0, ends) == [3]
+
+
+def test_vote_counts_beat_summed_attention():
+    # top-1 per layer: layer 0 votes chunk 1 (0.95), layers 1 and 2 vote chunk 0
+    # (0.30 against 0.29).  Chunk 1 has the larger summed attention (1.53 vs
+    # 0.60) but one vote; chunk 0 has two and is kept.
+    s = [[0.00, 0.95, 0.05, 0.00],
+         [0.30, 0.29, 0.21, 0.20],
+         [0.30, 0.29, 0.21, 0.20]]
+    ends = np.array([1, 2, 3, 4])
+    assert _voted_chunks(s, 1, 0, ends) == [0]
+    assert _voted_chunks(s, 2, 0, ends) == [0, 1]
+
+
+def test_vote_single_layer_is_its_own_top_k():
+    r = np.random.default_rng(12)
+    ends = np.cumsum(r.integers(1, 9, 200))
+    for k, local in [(10, 0), (17, 3), (1, 5)]:
+        sc = r.random(200).astype(np.float32)
+        want = oracle.select_chunks(sc.astype(np.float64), ends, 0, local, k)
+        got = oracle.select_chunks(oracle.vote_key(sc[None], k, 1), ends, 0, local, k)
+        assert np.array_equal(got, want)
+        # identical layers vote as one
+        got3 = oracle.select_chunks(oracle.vote_key(np.stack([sc] * 3), k, 1), ends, 0, local, k)
+        assert np.array_equal(got3, want)
+
+
+def test_vote_key_orders_by_votes_then_attention():
+    r = np.random.default_rng(13)
+    L, nc, k, G = 5, 300, 20, 4
+    sc = (r.random((L, nc)) * G / nc * 3).astype(np.float32)
+    key = oracle.vote_key(sc, k, G)
+    votes = np.floor(key)
+    assert votes.max() <= L and votes.sum() == L * k
+    frac = key - votes
+    assert np.all(frac >= 0) and np.all(frac <= 0.5)
+    tot = sc.astype(np.float64).sum(0)
+    for v in np.unique(votes):
+        m = votes == v
+        o = np.argsort(-key[m], kind="stable")
+        assert np.all(np.diff(tot[m][o]) <= 1e-6)     # within a vote count: summed attention
