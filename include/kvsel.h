@@ -10,6 +10,7 @@
  *   kvsel_lmba         per-row 90 %-mass minimum budget (layer uncertainty)
  *                      and the attention a selection keeps
  *   kvsel_select       keep tokens per segment (top-B, chunk top-k or head policy)
+ *   kvsel_chunk_vote   ChunkLLM layer-wise vote: one chunk key from the layers' scores
  *   kvsel_compact      gather kept K/V rows into a packed variable-length cache
  *   kvsel_decode_attn  single-token GQA decode attention over that cache
  *   kvsel_append       add each decoded token under the head's eviction rule
@@ -206,6 +207,28 @@ typedef struct {
 kvsel_status kvsel_select(const kvsel_shape* s /*host*/, const kvsel_select_params* p /*host*/,
                           const float* scores, const int64_t* seg_off, int32_t* seg_len,
                           int32_t* idx, int64_t r_cap, hipStream_t stream);
+
+/* ----------------------------------------------------------- chunk vote --
+ * ChunkLLM page, §2.3: the chunks stored in the cache are chosen by a vote
+ * across layers (the page gives the rule only in words; reading taken):
+ * each of `layers` layers votes for its own top_k chunks (its chunk scores in
+ * TOPB order: score descending, lower index first); per (b, kvh) and chunk c
+ *   key[b][kvh][c] = votes_c + 0.5 * (sum_l scores[l][b][kvh][c] / (layers * G))
+ * computed in fp32 with the layers summed in order 0 .. layers-1 and a
+ * correctly rounded divide.  A chunk's attention summed over its G query
+ * heads is at most G, so kvsel_select CHUNK with top_chunks = top_k (and
+ * local_chunks) over key keeps the chunks with the most votes, ties to the
+ * larger summed attention, then to the lower index.
+ *   s        shape of the chunk scores: n = chunks per sequence, G = hq/hkv
+ *   scores   [layers][batch][hkv][n] fp32 (kvsel_score of each layer)
+ *   key      [batch][hkv][n] fp32 (out)
+ *   ws       at least kvsel_chunk_vote_workspace(s, layers, top_k) bytes
+ * Constraints: 1 <= layers <= 255, top_k >= 1 (top_k > n votes for every
+ * chunk), n bytes of vote counters must fit in one workgroup's LDS. */
+size_t kvsel_chunk_vote_workspace(const kvsel_shape* s /*host*/, int32_t layers, int32_t top_k);
+kvsel_status kvsel_chunk_vote(const kvsel_shape* s /*host*/, int32_t layers, int32_t top_k,
+                              const float* scores, float* key, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
 
 /* -------------------------------------------------------------- compact --
  * Packed variable-length cache: for every segment s and r < seg_len[s],

@@ -55,6 +55,11 @@ _SIGS = {
     "kvsel_score": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "kvsel_chunk_vote_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32,
+                                                     ctypes.c_int32]),
+    "kvsel_chunk_vote": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]),
     "kvsel_select": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(SelectParams),
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
@@ -155,6 +160,17 @@ def select_params(mode, budget=None, n_chunks=0, chunk_end=None, keep_tokens=0,
     return SelectParams(int(mode), _ptr(budget), int(n_chunks), _ptr(chunk_end), int(keep_tokens),
                         _ptr(head_kind), int(local_window), _ptr(special_pos), int(n_special),
                         int(local_chunks), int(top_chunks))
+
+
+def kvsel_chunk_vote_workspace(shape: Shape, layers: int, top_k: int) -> int:
+    return lib().kvsel_chunk_vote_workspace(ctypes.byref(shape), int(layers), int(top_k))
+
+
+def kvsel_chunk_vote(shape: Shape, layers: int, top_k: int, scores, key, ws, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().kvsel_chunk_vote(ctypes.byref(shape), int(layers), int(top_k), _ptr(scores),
+                                  _ptr(key), _ptr(ws), nbytes, _stream(stream)),
+           "kvsel_chunk_vote")
 
 
 def kvsel_select(shape: Shape, params: SelectParams, scores, seg_off, seg_len, idx, r_cap: int,

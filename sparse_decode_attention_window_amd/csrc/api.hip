@@ -291,6 +291,30 @@ kvsel_status kvsel_append(const kvsel_shape* s, const void* k_new, const void* v
                     "kvsel_append launch");
 }
 
+size_t kvsel_chunk_vote_workspace(const kvsel_shape* s, int32_t layers, int32_t top_k) {
+  if (!s || s->batch < 1 || s->hkv < 1 || s->n < 1 || layers < 1 || top_k < 1) return 0;
+  return vote_workspace_bytes(s->batch * s->hkv, layers, s->n, top_k);
+}
+
+kvsel_status kvsel_chunk_vote(const kvsel_shape* s, int32_t layers, int32_t top_k,
+                              const float* scores, float* key, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  g_err[0] = 0;
+  int S = 0, G = 0;
+  kvsel_status st = check_shape(s, &S, &G, 256);
+  if (st != KVSEL_OK) return st;
+  if (layers < 1 || layers > 255) return fail(KVSEL_EINVAL, "layers must be in [1, 255]");
+  if (top_k < 1) return fail(KVSEL_EINVAL, "top_k must be >= 1");
+  if (!scores || !key) return fail(KVSEL_EINVAL, "scores and key must be non-NULL");
+  if ((size_t)((s->n + 3) / 4) * 4 + 1024 > (size_t)device_info().max_lds)
+    return fail(KVSEL_EUNSUPPORTED, "%lld vote counters do not fit in LDS", (long long)s->n);
+  const size_t need = kvsel_chunk_vote_workspace(s, layers, top_k);
+  if (!ws || ws_bytes < need)
+    return fail(KVSEL_ENOSPC, "chunk vote workspace needs %zu bytes, got %zu", need, ws_bytes);
+  return hip_status(launch_vote(S, s->hkv, G, layers, s->n, top_k, scores, key, ws, stream),
+                    "kvsel_chunk_vote launch");
+}
+
 size_t kvsel_decode_workspace(const kvsel_shape* s, int64_t r_cap) {
   if (!s || s->batch < 1 || s->hkv < 1 || s->hq < s->hkv || r_cap < 0) return 0;
   return decode_workspace_bytes(s->batch * s->hkv, s->head_dim, s->hq / s->hkv, r_cap);

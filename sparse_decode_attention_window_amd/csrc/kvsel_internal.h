@@ -300,6 +300,12 @@ hipError_t launch_select_rank(int S, int hkv, int64_t n_items, const float* scor
                               const int64_t* seg_off, int32_t* seg_len, int32_t* idx,
                               int64_t r_cap, hipStream_t stream);
 
+// Layer-wise chunk voting: scratch bytes and the launches (per-layer TOPB
+// selects, then the vote keys).
+size_t vote_workspace_bytes(int S, int layers, int64_t n, int32_t k);
+hipError_t launch_vote(int S, int hkv, int G, int layers, int64_t n, int32_t k,
+                       const float* scores, float* key, void* ws, hipStream_t stream);
+
 hipError_t launch_select_policy(int S, int hkv, int64_t n, const int8_t* head_kind,
                                 int64_t local_window, const int32_t* special_pos,
                                 int64_t n_special, const int64_t* seg_off, int32_t* seg_len,

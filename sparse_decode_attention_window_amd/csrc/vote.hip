@@ -1,0 +1,99 @@
+// ChunkLLM layer-wise chunk voting (ChunkLLM page, §2.3: the chunks kept in
+// the cache are chosen by a vote across layers; the rule is given only in
+// words).  Each layer votes for its own top-k chunks; a chunk's key is
+//   votes + 0.5 * (sum over layers of its chunk attention / (layers * G)),
+// every step in fp32 with the layers summed in order, so a CHUNK selection of
+// the k best keys (plus the local chunks) keeps the chunks with the most
+// votes, ties to the larger summed attention, then to the lower index.
+//
+// The per-layer top-k runs through the TOPB select over the [layers * S]
+// score rows (one segment per (layer, b, kvh)); then vote_key_kernel, one
+// workgroup per (b, kvh), counts the votes in LDS and writes the keys.
+#include "kvsel_internal.h"
+
+namespace kvsel {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Budgets and segment offsets of the per-layer selections (k each).
+__global__ __launch_bounds__(kThreads) void vote_setup_kernel(int n_seg, int32_t k,
+                                                              int32_t* __restrict__ budget,
+                                                              int64_t* __restrict__ seg_off) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n_seg) {
+    budget[i] = k;
+    seg_off[i] = (int64_t)i * k;
+  }
+}
+
+// votes[c] lives in byte c of the LDS words (layers <= 255, so a byte never
+// carries into its neighbour).
+__global__ __launch_bounds__(kThreads) void vote_key_kernel(
+    const float* __restrict__ scores, int64_t n, int S, int layers, int32_t k, float lg,
+    const int32_t* __restrict__ ballots, float* __restrict__ key) {
+  extern __shared__ uint32_t votes[];   // (n + 3) / 4 words
+  const int s = blockIdx.x, tid = threadIdx.x;
+  const int64_t words = (n + 3) / 4;
+  for (int64_t i = tid; i < words; i += kThreads) votes[i] = 0u;
+  __syncthreads();
+  for (int l = 0; l < layers; ++l) {
+    const int32_t* b = ballots + ((int64_t)l * S + s) * k;
+    for (int i = tid; i < k; i += kThreads) {
+      const int32_t c = b[i];
+      if (c >= 0 && c < n) atomicAdd(&votes[c >> 2], 1u << (8 * (c & 3)));
+    }
+  }
+  __syncthreads();
+  for (int64_t c = tid; c < n; c += kThreads) {
+    float acc = 0.f;
+    for (int l = 0; l < layers; ++l) acc += scores[((int64_t)l * S + s) * n + c];
+    const uint32_t v = (votes[c >> 2] >> (8 * (c & 3))) & 0xffu;
+    key[(int64_t)s * n + c] = (float)v + 0.5f * (acc / lg);   // correctly rounded divide
+  }
+}
+
+}  // namespace
+
+size_t vote_workspace_bytes(int S, int layers, int64_t n, int32_t k) {
+  const int64_t kk = k < n ? k : n;
+  const size_t segs = (size_t)layers * S;
+  const size_t a = segs * sizeof(int32_t), b = segs * sizeof(int64_t);
+  const size_t head = ((a + 255) & ~(size_t)255) + ((b + 255) & ~(size_t)255) +
+                      ((a + 255) & ~(size_t)255);
+  return head + segs * (size_t)kk * sizeof(int32_t);
+}
+
+hipError_t launch_vote(int S, int hkv, int G, int layers, int64_t n, int32_t k,
+                       const float* scores, float* key, void* ws, hipStream_t stream) {
+  const int32_t kk = (int32_t)(k < n ? k : n);
+  const int segs = layers * S;
+  char* p = static_cast<char*>(ws);
+  auto take = [&](size_t bytes) {
+    char* q = p;
+    p += (bytes + 255) & ~(size_t)255;
+    return q;
+  };
+  auto* budget = reinterpret_cast<int32_t*>(take((size_t)segs * 4));
+  auto* seg_off = reinterpret_cast<int64_t*>(take((size_t)segs * 8));
+  auto* seg_len = reinterpret_cast<int32_t*>(take((size_t)segs * 4));
+  auto* ballots = reinterpret_cast<int32_t*>(p);
+  vote_setup_kernel<<<dim3((segs + kThreads - 1) / kThreads), dim3(kThreads), 0, stream>>>(
+      segs, kk, budget, seg_off);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_select_rank(segs, hkv, n, scores, budget, nullptr, 0, 0, 0, seg_off, seg_len,
+                         ballots, (int64_t)segs * kk, stream);
+  if (e != hipSuccess) return e;
+  const size_t lds = (size_t)((n + 3) / 4) * 4;
+  if (lds > 65536) {
+    e = hipFuncSetAttribute((const void*)vote_key_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  vote_key_kernel<<<dim3(S), dim3(kThreads), lds, stream>>>(
+      scores, n, S, layers, kk, (float)layers * (float)G, ballots, key);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

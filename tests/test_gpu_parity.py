@@ -951,3 +951,72 @@ def test_chunk_serving_loop_reselects_at_boundaries(kv):
     assert nb >= 2 and loop.reselections == nb
     print(f"  {cfg.name}: {nb} boundary re-selections in {steps} steps, decode max abs err "
           f"{worst:.2e}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# ChunkLLM layer-wise chunk voting (§2.3; reading: votes, then summed attention)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,layers,top,local", [(3000, 4, 16, 4), (20000, 6, 64, 8)])
+def test_chunk_vote_matches_oracle(kv, n, layers, top, local):
+    """Chunk scores of several layers over shared chunk boundaries (the chunk
+    adapter sits at the bottom layer), voted into one key per chunk: the key
+    equals the oracle's on the GPU's own fp32 scores bit for bit, each layer's
+    ballot differs from the float64 one only inside the tie band, and the
+    CHUNK selection over the key keeps exactly the oracle's chunks."""
+    from kvsynth import gen
+    kvsel, pipeline, torch = kv
+    cfg = kvsynth.get_config(4, n=n)
+    _say(cfg.name, "chunk vote, n", n, "layers", layers, "top", top, "local", local)
+    B, hkv, hq, G, cd = cfg.batch, cfg.hkv, cfg.hq, cfg.G, cfg.chunk_dim
+    S = B * hkv
+    ends = [gen.chunk_ends(cfg, b, 0) for b in range(B)]
+    nc = len(ends[0])
+    sshape = kvsel.make_shape(B, hq, hkv, cd, nc, cfg.dtype, cfg.scale)
+    allsc = torch.empty(layers * S * nc, dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvsel.kvsel_score_workspace(sshape, 1), dtype=torch.uint8, device="cuda")
+    ref = np.zeros((layers, S, nc))
+    for l in range(layers):
+        P = gen.chunk_projection(cfg, l)
+        ck = np.empty((B, hkv, nc, cd), np.uint16)
+        cq = np.empty((B, hq, 1, cd), np.uint16)
+        for b in range(B):
+            for h in range(hkv):
+                K, _ = gen.segment_kv(cfg, l, b, h)
+                _, qd = gen.segment_queries(cfg, l, b, h)
+                ck[b, h], cq[b, h * G:(h + 1) * G] = gen.segment_chunk_inputs(cfg, K, qd, ends[b], P)
+                ref[l, b * hkv + h] = oracle.window_scores(
+                    oracle.to_f64(cq[b, h * G:(h + 1) * G]), oracle.to_f64(ck[b, h]), cfg.scale,
+                    nc - 1)
+        kvsel.kvsel_score(sshape, 1, nc - 1, pipeline.device_tensor(cq), pipeline.device_tensor(ck),
+                          allsc[l * S * nc:(l + 1) * S * nc], ws)
+    key = torch.empty(S * nc, dtype=torch.float32, device="cuda")
+    vws = torch.empty(kvsel.kvsel_chunk_vote_workspace(sshape, layers, top), dtype=torch.uint8,
+                      device="cuda")
+    kvsel.kvsel_chunk_vote(sshape, layers, top, allsc, key, vws)
+    # the shared selection: local chunks + the top best keys, over the voted key
+    shape = kvsel.make_shape(B, hq, hkv, cfg.d, n, cfg.dtype, cfg.scale)
+    et = pipeline.device_tensor(np.stack(ends).astype(np.int64))
+    cap = pipeline.capacities(kvsel.KVSEL_SEL_CHUNK, B, hkv, n, max_chunk=int(max(
+        np.diff(np.concatenate([[0], e])).max() for e in ends)), local_chunks=local, top_chunks=top)
+    off, r_cap = pipeline.offsets(cap)
+    ln = torch.empty(S, dtype=torch.int32, device="cuda")
+    idx = torch.empty(max(r_cap, 1), dtype=torch.int32, device="cuda")
+    prm = kvsel.select_params(kvsel.KVSEL_SEL_CHUNK, n_chunks=nc, chunk_end=et,
+                              local_chunks=local, top_chunks=top)
+    kvsel.kvsel_select(shape, prm, key, pipeline.device_tensor(off), ln, idx, r_cap)
+    torch.cuda.synchronize()
+    sc = pu.to_host(allsc).reshape(layers, S, nc)
+    kg = pu.to_host(key).reshape(S, nc)
+    lens, ig = pu.to_host(ln), pu.to_host(idx)
+    for s in range(S):
+        b = s // hkv
+        for l in range(layers):
+            pu.check_scores(sc[l, s], ref[l, s], G, f"layer {l} seg {s}")
+            pu.check_topb_selection(oracle.select_topb(sc[l, s].astype(np.float64), top),
+                                    sc[l, s], ref[l, s], top, f"ballot layer {l} seg {s}")
+        want_key = oracle.vote_key(sc[:, s], top, G)
+        assert np.array_equal(kg[s].view(np.uint32), want_key.view(np.uint32)), f"seg {s} key"
+        want = oracle.select_chunks(want_key.astype(np.float64), ends[b], 0, local, top)
+        got = ig[off[s]:off[s] + lens[s]]
+        assert np.array_equal(got, want), f"seg {s}: voted selection"
