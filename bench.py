@@ -2,9 +2,11 @@
 """Benchmark: one step = the whole hot path over the 32-layer, 32K-context,
 batch-4 Llama-3-8B-shaped workload with per-layer bounded budgets:
 
-  window score (all layers) -> top-B select (all layers) -> gather-compact
-  (all layers) -> one decode step through all 32 layers over the compacted
-  caches, plus the host-side per-layer budget computation.
+  window score (all layers, one call) -> top-B select (all layers, one call)
+  -> gather-compact (all layers, one call) -> one decode step through all 32
+  layers over the compacted caches (one call per layer), plus the host-side
+  per-layer budget computation.  The same compression step issued one layer
+  at a time is timed too and reported beside it.
 
 Inputs are synthetic (seeded generator), resident in HBM before timing.  Each
 phase is captured once as a HIP graph of the library's launches and replayed
@@ -105,6 +107,11 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
     return out
 
 
+def pu_host(t):
+    """Device tensor -> numpy (int / float tensors only)."""
+    return t.detach().cpu().numpy()
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -180,8 +187,7 @@ def main() -> int:
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path needs no collective; see the sharding notes in DESIGN.md)",
-              file=sys.stderr)
+              "(the path runs on one GPU and needs no collective)", file=sys.stderr)
         return 2
 
     import torch
@@ -203,32 +209,36 @@ def main() -> int:
     log(f"[bench] generating {cfg.name}: {L} layers x batch {cfg.batch} x {cfg.hkv} KV heads "
         f"x {cfg.n} tokens x d {cfg.d} ({cfg.dtype})")
     t0 = time.perf_counter()
-    layers = []
-    for l in range(L):
-        inputs = kvsynth.layer_inputs(cfg, l)
-        layers.append(pipeline.build_layer(cfg, inputs, budget=budgets[l]))
-        del inputs
+
+    def progress(l):
         if l % 4 == 3:
             log(f"[bench] layer {l + 1}/{L} resident ({time.perf_counter() - t0:.1f} s)")
+    mr = pipeline.ModelRun.build(cfg, budgets, lambda l: kvsynth.layer_inputs(cfg, l),
+                                 log=progress)
     torch.cuda.synchronize()
+    S = cfg.batch * cfg.hkv
 
-    # One step = four phases over all layers, each captured once as a HIP graph
-    # (the kernels are the eager ones; the graph only removes host launch gaps).
+    # One step = the compression step over the whole model (score, select,
+    # compact: one call each for all L layers' segments) and one decode step
+    # through the L layers (one call per layer, as a model runs them).  Each
+    # phase is captured once as a HIP graph (the kernels are the eager ones;
+    # the graph only removes host launch gaps).
     phases = {
-        "score": lambda: [run.score() for run in layers],
-        "select": lambda: [run.select() for run in layers],
-        "compact": lambda: [run.compact() for run in layers],
-        "decode": lambda: [run.decode() for run in layers],
+        "score": mr.score,
+        "select": mr.select,
+        "compact": mr.compact,
+        "decode": lambda: [mr.decode(l) for l in range(L)],
     }
     for fn in phases.values():   # eager warm-up before capture
         fn()
     torch.cuda.synchronize()
-    graphs = {}
-    for name, fn in phases.items():
+
+    def capture(fn):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
-        graphs[name] = g
+        return g
+    graphs = {name: capture(fn) for name, fn in phases.items()}
     torch.cuda.synchronize()
 
     def step(ev):
@@ -256,25 +266,52 @@ def main() -> int:
     wall = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {wall:.3f} s")
 
+    # per-phase GPU time averaged over steps, per layer
+    st = {name: 0.0 for name in phases}
+    for ev in evs:
+        for i, name in enumerate(phases):
+            st[name] += ev[i].elapsed_time(ev[i + 1])
+    us = {k: v / (args.steps * L) * 1e3 for k, v in st.items()}       # µs per layer
+
+    # the same compression step issued one layer at a time (for comparison)
+    def timed(fn, reps=3):
+        g = capture(fn)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        g.replay()
+        e[0].record()
+        for _ in range(reps):
+            g.replay()
+        e[1].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / (reps * L) * 1e3
+    us_layerwise = {
+        "score": timed(lambda: [mr.score_layer(l) for l in range(L)]),
+        "select": timed(lambda: [mr.select_layer(l) for l in range(L)]),
+        "compact": timed(lambda: [mr.compact_layer(l) for l in range(L)]),
+    }
+    mr.score(); mr.select(); mr.compact()
+    torch.cuda.synchronize()
+
     # calibration extra, outside the timed steps: per-row LMBA of every layer
     # (ZigZagkv Eq. 3) and the attention the layer's top-B selection keeps
     # (Table 3's attention loss is max(0, 0.9 - kept)); one workspace serves
     # every layer since the launches are ordered on one stream
-    R, B_S = cfg.G * cfg.w, cfg.batch * cfg.hkv
-    lm_ws = torch.empty(kvsel.kvsel_lmba_workspace(layers[0].shape, cfg.w), dtype=torch.uint8,
-                        device="cuda")
-    lm = torch.empty(L, B_S * R, dtype=torch.int32, device="cuda")
-    km = torch.empty(L, B_S * R, dtype=torch.float32, device="cuda")
+    R = cfg.G * cfg.w
+    B = cfg.batch
+    ls = mr.layer_shape
+    lm_ws = torch.empty(kvsel.kvsel_lmba_workspace(ls, cfg.w), dtype=torch.uint8, device="cuda")
+    lm = torch.empty(L, S * R, dtype=torch.int32, device="cuda")
+    km = torch.empty(L, S * R, dtype=torch.float32, device="cuda")
 
     def lmba_all():
-        for l, run in enumerate(layers):
-            kvsel.kvsel_lmba(run.shape, cfg.w, cfg.n - cfg.w, run.q_win, run.k, lm[l], lm_ws,
-                             run.seg_off, run.seg_len, run.idx, run.r_cap, km[l])
+        for l in range(L):
+            rows = slice(l * S, (l + 1) * S)
+            kvsel.kvsel_lmba(ls, cfg.w, cfg.n - cfg.w, mr.q_win[l * B:(l + 1) * B],
+                             mr.k[l * B:(l + 1) * B], lm[l], lm_ws, mr.seg_off[rows],
+                             mr.seg_len[rows], mr.idx, mr.r_cap, km[l])
     lmba_all()
     torch.cuda.synchronize()
-    g_lm = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_lm):
-        lmba_all()
+    g_lm = capture(lmba_all)
     l_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     l_ev[0].record()
     for _ in range(2):
@@ -294,13 +331,13 @@ def main() -> int:
     step_tok = kvsynth.step_inputs(cfg, 0, 0)
     kn = pipeline.device_tensor(step_tok["k_new"])
     vn = pipeline.device_tensor(step_tok["v_new"])
-    for run in layers:
-        run.append(kn, vn, step_tok["pos"])
+
+    def append_all():
+        for l in range(L):
+            mr.append_layer(l, kn, vn, step_tok["pos"])
+    append_all()
     torch.cuda.synchronize()
-    g_app = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_app):
-        for run in layers:
-            run.append(kn, vn, step_tok["pos"])
+    g_app = capture(append_all)
     a_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     a_ev[0].record()
     for _ in range(5):
@@ -309,17 +346,10 @@ def main() -> int:
     torch.cuda.synchronize()
     append_us = a_ev[0].elapsed_time(a_ev[1]) / (5 * L) * 1e3
 
-    # per-phase GPU time (ms) averaged over steps, then per layer
-    st = {name: 0.0 for name in phases}
-    for ev in evs:
-        for i, name in enumerate(phases):
-            st[name] += ev[i].elapsed_time(ev[i + 1])
-    launches = args.steps * L
-    us = {k: v / launches * 1e3 for k, v in st.items()}       # µs per layer
-
-    es, d, B, hq, hkv, n = cfg.es, cfg.d, cfg.batch, cfg.hq, cfg.hkv, cfg.n
-    rows = [int(layers[l].seg_len.sum().item()) for l in range(L)]
-    assert rows == [B * hkv * b for b in budgets]
+    es, d, hq, hkv, n = cfg.es, cfg.d, cfg.hq, cfg.hkv, cfg.n
+    lens = pu_host(mr.seg_len).reshape(L, S)
+    rows = [int(lens[l].sum()) for l in range(L)]
+    assert rows == [S * b for b in budgets]
     mean_rows = sum(rows) / L
     dec_bytes = mean_rows * d * es * 2 + B * hq * d * (es + 4)
     cmp_bytes = mean_rows * (d * es * 4 + 4)
@@ -353,7 +383,9 @@ def main() -> int:
         "config": {"workload": cfg.name, "layers": L, "batch": B, "hq": hq, "hkv": hkv,
                    "head_dim": d, "context": n, "window": cfg.w,
                    "avg_budget": cfg.avg_budget, "floor_budget": cfg.floor_budget,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "compression_calls": "one score, select and compact call for all layers; "
+                                        "one decode call per layer"},
         "pct_peak_hbm": round(100 * dec_gbs / PEAK_HBM_GBS, 1),
         "select_and_compact_us_per_layer": round(us["select"] + us["compact"], 2),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
@@ -363,6 +395,9 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": int(dec_bytes),
                      "avg_launch_us": round(us["decode"], 3)},
         "stages_us_per_layer": {k: round(v, 3) for k, v in us.items()},
+        "stages_us_per_layer_one_call_per_layer": {k: round(v, 3) for k, v in us_layerwise.items()},
+        "select_and_compact_us_per_layer_one_call_per_layer":
+            round(us_layerwise["select"] + us_layerwise["compact"], 2),
         "hbm_copy_reference_GBps": round(copy_gbs, 1),
         "extras": {"append_us_per_layer": round(append_us, 3),
                    "append_note": "kvsel_append of one decoded token into all 32 full "

@@ -390,3 +390,145 @@ class ChunkServingLoop:
                         run.idx, run.k_c, run.v_c, run.r_cap, stream)
         self.reselections += 1
         return True
+
+
+@dataclass
+class ModelRun:
+    """Every layer of a top-B model in one layout, so that the compression
+    step (score, select, compact) can run as one call each for the whole model
+    (L*b*hkv segments fill the chip where one layer's b*hkv do not) while the
+    decode stays one call per layer, as a model runs it.
+
+    Segment g = l*S + s of layer l (s = b*hkv + kvh): keys and values
+    [L*b][hkv][n][d] (layer-major), window queries [L*b][hq][w][d], scores
+    [L*S][n], one packed cache in which layer l's segments occupy rows
+    [base[l], base[l] + r_caps[l]).  seg_off holds absolute rows (select,
+    compact, append); seg_off_rel[l] the rows relative to base[l] (decode,
+    which sizes its launch from one layer's rows)."""
+    L: int
+    shape: K.Shape
+    layer_shape: K.Shape
+    k: object
+    v: object
+    q_win: object
+    q_dec: object
+    w: int
+    q_pos0: int
+    budget: object
+    params: K.SelectParams
+    seg_off: object
+    seg_cap: object
+    seg_off_rel: list
+    base: list
+    r_caps: list
+    r_cap: int
+    scores: object = None
+    ws_score: object = None
+    ws_score_layer: object = None
+    seg_len: object = None
+    idx: object = None
+    k_c: object = None
+    v_c: object = None
+    out: object = None
+    ws_dec: object = None
+    keep: list = field(default_factory=list)
+
+    @staticmethod
+    def build(cfg, budgets, inputs_of, device="cuda", log=None) -> "ModelRun":
+        """cfg: a top-B kvsynth Config; budgets [L] per-layer budgets;
+        inputs_of(l) -> kvsynth.layer_inputs(cfg, l) (called once per layer)."""
+        import torch
+        assert cfg.mode == "topb"
+        L, B, hq, hkv, d, n, w = cfg.layers, cfg.batch, cfg.hq, cfg.hkv, cfg.d, cfg.n, cfg.w
+        S = B * hkv
+        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        k = torch.empty((L * B, hkv, n, d), dtype=tdt, device=device)
+        v = torch.empty_like(k)
+        q_win = torch.empty((L * B, hq, w, d), dtype=tdt, device=device)
+        q_dec = torch.empty((L, B, hq, d), dtype=tdt, device=device)
+        for l in range(L):
+            inp = inputs_of(l)
+            k[l * B:(l + 1) * B] = device_tensor(inp["K"], device)
+            v[l * B:(l + 1) * B] = device_tensor(inp["V"], device)
+            q_win[l * B:(l + 1) * B] = device_tensor(inp["q_win"], device)
+            q_dec[l] = device_tensor(inp["q_dec"], device)
+            del inp
+            if log:
+                log(l)
+        bud = np.repeat(np.asarray(budgets, np.int32), S)
+        cap = capacities(K.KVSEL_SEL_TOPB, L * B, hkv, n, budget=bud)
+        off, r_cap = offsets(cap)
+        base = [int(off[l * S]) for l in range(L)]
+        r_caps = [int(cap[l * S:(l + 1) * S].sum()) for l in range(L)]
+        shape = K.make_shape(L * B, hq, hkv, d, n, cfg.dtype, cfg.scale)
+        layer_shape = K.make_shape(B, hq, hkv, d, n, cfg.dtype, cfg.scale)
+        bt = device_tensor(bud, device)
+        run = ModelRun(L, shape, layer_shape, k, v, q_win, q_dec, w, n - w, bt,
+                       K.select_params(K.KVSEL_SEL_TOPB, budget=bt),
+                       device_tensor(off, device), device_tensor(cap.astype(np.int64), device),
+                       [device_tensor(off[l * S:(l + 1) * S] - base[l], device) for l in range(L)],
+                       base, r_caps, r_cap)
+        run.keep = [bt]
+        run.scores = torch.empty(L * S * n, dtype=torch.float32, device=device)
+        run.ws_score = torch.empty(K.kvsel_score_workspace(shape, w), dtype=torch.uint8,
+                                   device=device)
+        run.ws_score_layer = torch.empty(K.kvsel_score_workspace(layer_shape, w),
+                                         dtype=torch.uint8, device=device)
+        run.seg_len = torch.empty(L * S, dtype=torch.int32, device=device)
+        run.idx = torch.empty(max(r_cap, 1), dtype=torch.int32, device=device)
+        run.k_c = torch.empty((max(r_cap, 1), d), dtype=tdt, device=device)
+        run.v_c = torch.empty_like(run.k_c)
+        run.out = torch.empty((L, B, hq, d), dtype=torch.float32, device=device)
+        nb = max(K.kvsel_decode_workspace(layer_shape, rc) for rc in r_caps)
+        run.ws_dec = torch.zeros(max(nb, 1), dtype=torch.uint8, device=device)
+        return run
+
+    # ---- the whole model, one call each ----------------------------------
+    def score(self, stream=None):
+        K.kvsel_score(self.shape, self.w, self.q_pos0, self.q_win, self.k, self.scores,
+                      self.ws_score, stream)
+
+    def select(self, stream=None):
+        K.kvsel_select(self.shape, self.params, self.scores, self.seg_off, self.seg_len,
+                       self.idx, self.r_cap, stream)
+
+    def compact(self, stream=None):
+        K.kvsel_compact(self.shape, self.k, self.v, self.seg_off, self.seg_len, self.idx,
+                        self.k_c, self.v_c, self.r_cap, stream)
+
+    # ---- one layer -------------------------------------------------------
+    def _rows(self, l):
+        S = self.layer_shape.batch * self.layer_shape.hkv
+        return slice(l * S, (l + 1) * S)
+
+    def decode(self, l, stream=None):
+        b0 = self.base[l]
+        K.kvsel_decode_attn(self.layer_shape, self.q_dec[l], self.k_c[b0:], self.v_c[b0:],
+                            self.seg_off_rel[l], self.seg_len[self._rows(l)], self.r_caps[l],
+                            self.out[l], self.ws_dec, stream)
+
+    def score_layer(self, l, stream=None):
+        B, n = self.layer_shape.batch, self.layer_shape.n
+        r = self._rows(l)
+        K.kvsel_score(self.layer_shape, self.w, self.q_pos0, self.q_win[l * B:(l + 1) * B],
+                      self.k[l * B:(l + 1) * B], self.scores[r.start * n:r.stop * n],
+                      self.ws_score_layer, stream)
+
+    def select_layer(self, l, stream=None):
+        n = self.layer_shape.n
+        r = self._rows(l)
+        prm = K.select_params(K.KVSEL_SEL_TOPB, budget=self.budget[r])
+        K.kvsel_select(self.layer_shape, prm, self.scores[r.start * n:r.stop * n],
+                       self.seg_off[r], self.seg_len[r], self.idx, self.r_cap, stream)
+
+    def compact_layer(self, l, stream=None):
+        B = self.layer_shape.batch
+        r = self._rows(l)
+        K.kvsel_compact(self.layer_shape, self.k[l * B:(l + 1) * B], self.v[l * B:(l + 1) * B],
+                        self.seg_off[r], self.seg_len[r], self.idx, self.k_c, self.v_c,
+                        self.r_cap, stream)
+
+    def append_layer(self, l, k_new, v_new, pos: int, limit=None, stream=None):
+        r = self._rows(l)
+        K.kvsel_append(self.layer_shape, k_new, v_new, pos, self.seg_off[r], self.seg_cap[r],
+                       limit, self.seg_len[r], self.idx, self.k_c, self.v_c, self.r_cap, stream)

@@ -1020,3 +1020,51 @@ def test_chunk_vote_matches_oracle(kv, n, layers, top, local):
         want = oracle.select_chunks(want_key.astype(np.float64), ends[b], 0, local, top)
         got = ig[off[s]:off[s] + lens[s]]
         assert np.array_equal(got, want), f"seg {s}: voted selection"
+
+
+# ---------------------------------------------------------------------------
+# the whole model in one layout: one compression call per step, decode per layer
+# ---------------------------------------------------------------------------
+
+def test_model_run_matches_layer_runs(kv):
+    """Score, select and compact for all layers in one call each (segments of
+    every layer) give bit for bit what the per-layer calls give, and the
+    per-layer decode over the shared packed cache equals a separate layer's."""
+    kvsel, pipeline, torch = kv
+    cfg = kvsynth.get_config(2, n=3000, layers=3, batch=2)
+    _say(cfg.name, "model run, layers", cfg.layers, "n", cfg.n)
+    budgets = kvsel.kvsel_zigzag_budgets(kvsynth.zigzag_profile(cfg), cfg.n, 600, 150)
+    inputs = [kvsynth.layer_inputs(cfg, l) for l in range(cfg.layers)]
+    mr = pipeline.ModelRun.build(cfg, budgets, lambda l: inputs[l])
+    mr.score(); mr.select(); mr.compact()
+    for l in range(cfg.layers):
+        mr.decode(l)
+    torch.cuda.synchronize()
+    S, n = cfg.batch * cfg.hkv, cfg.n
+    sc_all, len_all = pu.to_host(mr.scores).copy(), pu.to_host(mr.seg_len).copy()
+    idx_all, kc_all, out_all = pu.to_host(mr.idx).copy(), pu.to_host(mr.k_c).copy(), \
+        pu.to_host(mr.out).copy()
+    # per-layer calls on the same buffers
+    mr.scores.zero_(); mr.idx.fill_(-1); mr.k_c.zero_(); mr.out.zero_()
+    for l in range(cfg.layers):
+        mr.score_layer(l); mr.select_layer(l); mr.compact_layer(l); mr.decode(l)
+    torch.cuda.synchronize()
+    assert np.array_equal(pu.to_host(mr.scores).view(np.uint32), sc_all.view(np.uint32))
+    assert np.array_equal(pu.to_host(mr.seg_len), len_all)
+    assert np.array_equal(pu.to_host(mr.idx), idx_all)
+    assert np.array_equal(pu.to_host(mr.k_c).view(np.uint16), kc_all.view(np.uint16))
+    assert np.array_equal(pu.to_host(mr.out).view(np.uint32), out_all.view(np.uint32))
+    off = pu.to_host(mr.seg_off)
+    for l in range(cfg.layers):
+        run = pipeline.build_layer(cfg, inputs[l], budget=budgets[l])
+        run.run()
+        torch.cuda.synchronize()
+        h = _host(run)
+        assert np.array_equal(h["scores"].view(np.uint32),
+                              sc_all[l * S * n:(l + 1) * S * n].view(np.uint32))
+        assert np.array_equal(h["out"].view(np.uint32), out_all[l].view(np.uint32))
+        for s in range(S):
+            g = l * S + s
+            a = h["idx"][h["seg_off"][s]:h["seg_off"][s] + h["seg_len"][s]]
+            b = idx_all[off[g]:off[g] + len_all[g]]
+            assert np.array_equal(a, b), (l, s)
