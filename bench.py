@@ -175,6 +175,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layerwise", action="store_true",
+                    help="skip the one-call-per-layer comparison of the compression step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the decode traffic file from two rocprofv3 --pmc runs and exit")
@@ -284,13 +286,15 @@ def main() -> int:
         e[1].record()
         torch.cuda.synchronize()
         return e[0].elapsed_time(e[1]) / (reps * L) * 1e3
-    us_layerwise = {
-        "score": timed(lambda: [mr.score_layer(l) for l in range(L)]),
-        "select": timed(lambda: [mr.select_layer(l) for l in range(L)]),
-        "compact": timed(lambda: [mr.compact_layer(l) for l in range(L)]),
-    }
-    mr.score(); mr.select(); mr.compact()
-    torch.cuda.synchronize()
+    us_layerwise = {}
+    if not args.no_layerwise:
+        us_layerwise = {
+            "score": timed(lambda: [mr.score_layer(l) for l in range(L)]),
+            "select": timed(lambda: [mr.select_layer(l) for l in range(L)]),
+            "compact": timed(lambda: [mr.compact_layer(l) for l in range(L)]),
+        }
+        mr.score(); mr.select(); mr.compact()
+        torch.cuda.synchronize()
 
     # calibration extra, outside the timed steps: per-row LMBA of every layer
     # (ZigZagkv Eq. 3) and the attention the layer's top-B selection keeps
@@ -397,7 +401,7 @@ def main() -> int:
         "stages_us_per_layer": {k: round(v, 3) for k, v in us.items()},
         "stages_us_per_layer_one_call_per_layer": {k: round(v, 3) for k, v in us_layerwise.items()},
         "select_and_compact_us_per_layer_one_call_per_layer":
-            round(us_layerwise["select"] + us_layerwise["compact"], 2),
+            round(us_layerwise["select"] + us_layerwise["compact"], 2) if us_layerwise else None,
         "hbm_copy_reference_GBps": round(copy_gbs, 1),
         "extras": {"append_us_per_layer": round(append_us, 3),
                    "append_note": "kvsel_append of one decoded token into all 32 full "
