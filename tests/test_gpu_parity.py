@@ -1068,3 +1068,67 @@ def test_model_run_matches_layer_runs(kv):
             a = h["idx"][h["seg_off"][s]:h["seg_off"][s] + h["seg_len"][s]]
             b = idx_all[off[g]:off[g] + len_all[g]]
             assert np.array_equal(a, b), (l, s)
+
+
+def test_c2_model_full_sampled(kv):
+    """The bench's launch configuration: all 32 C2 layers at full size, score,
+    select and compact as one call each (1024 segments), decode per layer.
+    Every segment: kept count = its layer's budget, indices strictly ascending
+    inside [0, n).  Sampled segments across the layers: scores, selection
+    (tie band), compaction (bit-exact) and decode against the oracle; one
+    layer's LMBA rows (float64 band) and kept mass on two of them."""
+    kvsel, pipeline, torch = kv
+    cfg = kvsynth.get_config(2)
+    _say(cfg.name, "full model, one compression call per phase")
+    L, S, n, G, w = cfg.layers, cfg.batch * cfg.hkv, cfg.n, cfg.G, cfg.w
+    budgets = kvsel.kvsel_zigzag_budgets(kvsynth.zigzag_profile(cfg), n, cfg.avg_budget,
+                                         cfg.floor_budget)
+    mr = pipeline.ModelRun.build(cfg, budgets, lambda l: kvsynth.layer_inputs(cfg, l))
+    mr.score(); mr.select(); mr.compact()
+    for l in range(L):
+        mr.decode(l)
+    torch.cuda.synchronize()
+    lens = pu.to_host(mr.seg_len).reshape(L, S)
+    off = pu.to_host(mr.seg_off)
+    idx = pu.to_host(mr.idx)
+    for l in range(L):
+        assert np.all(lens[l] == budgets[l]), l
+    for g in range(L * S):
+        seg = idx[off[g]:off[g] + lens.ravel()[g]]
+        assert seg[0] >= 0 and seg[-1] < n and np.all(np.diff(seg) > 0), g
+    sc = pu.to_host(mr.scores).reshape(L * S, n)
+    kc, vc, out = pu.to_host(mr.k_c), pu.to_host(mr.v_c), pu.to_host(mr.out)
+    for l, s in [(0, 0), (7, 13), (19, 5), (31, 31)]:
+        b, kvh = divmod(s, cfg.hkv)
+        g = l * S + s
+        x = kvsynth.segment_inputs(cfg, l, b, kvh)
+        ref = oracle.window_scores(oracle.to_f64(x["q_win"]), oracle.to_f64(x["K"]), cfg.scale,
+                                   n - w)
+        kept = idx[off[g]:off[g] + lens[l, s]].astype(np.int64)
+        what = f"layer {l} seg {s}"
+        pu.check_scores(sc[g], ref, G * w, what)
+        pu.check_topb_selection(kept, sc[g], ref, int(budgets[l]), what)
+        pu.check_compact(kc[off[g]:off[g] + len(kept)], vc[off[g]:off[g] + len(kept)], x["K"],
+                         x["V"], kept, what)
+        pu.check_decode(out[l, b, kvh * G:(kvh + 1) * G], x["q_dec"], x["K"], x["V"], kept,
+                        cfg.scale, cfg.dtype, what)
+    # LMBA and kept mass of layer 5 (the bench's calibration extra), two segments
+    l, B = 5, cfg.batch
+    ls, R = mr.layer_shape, G * w
+    rows = slice(l * S, (l + 1) * S)
+    lm = torch.empty(S * R, dtype=torch.int32, device="cuda")
+    km = torch.empty(S * R, dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvsel.kvsel_lmba_workspace(ls, w), dtype=torch.uint8, device="cuda")
+    kvsel.kvsel_lmba(ls, w, n - w, mr.q_win[l * B:(l + 1) * B], mr.k[l * B:(l + 1) * B], lm, ws,
+                     mr.seg_off[rows], mr.seg_len[rows], mr.idx, mr.r_cap, km)
+    torch.cuda.synchronize()
+    lmh, kmh = pu.to_host(lm).reshape(S, R), pu.to_host(km).reshape(S, R)
+    for s in (2, 29):
+        b, kvh = divmod(s, cfg.hkv)
+        x = kvsynth.segment_inputs(cfg, l, b, kvh)
+        P = oracle.window_probabilities(oracle.to_f64(x["q_win"]), oracle.to_f64(x["K"]),
+                                        cfg.scale, n - w)
+        pu.check_lmba(lmh[s], P, f"layer {l} seg {s}")
+        g = l * S + s
+        kept = idx[off[g]:off[g] + lens[l, s]].astype(np.int64)
+        assert np.max(np.abs(kmh[s] - P[:, kept].sum(axis=1))) <= 1e-5
