@@ -36,7 +36,7 @@ METRIC = "compacted decode-attn HBM GB/s (% peak) + select-and-compact µs/layer
 COUNTERS = os.path.join(ROOT, "profiles", "decode_c2_counters.json")
 CSRC = os.path.join(ROOT, "sparse_decode_attention_window_amd", "csrc")
 DECODE_SRCS = [os.path.join(CSRC, f) for f in ("decode.hip", "kvsel_internal.h")]
-DECODE_KERNELS = ("decode_split_kernel", "decode_combine_kernel")
+DECODE_KERNELS = ("decode_split_kernel", "decode_combine_head_kernel")
 COPY_BYTES = 1 << 30           # plain device copy used as HBM reference and counter calibration
 
 
@@ -395,7 +395,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "kvsel_decode_attn (decode_split_kernel + decode_combine_kernel)",
+                     "kernel": "kvsel_decode_attn (decode_split_kernel + decode_combine_head_kernel)",
                      "algorithmic_bytes_per_launch": int(dec_bytes),
                      "avg_launch_us": round(us["decode"], 3)},
         "stages_us_per_layer": {k: round(v, 3) for k, v in us.items()},

@@ -17,8 +17,8 @@
 //   PV    on the vector ALUs in fp32: lane (slot g, chunk c) owns 16 bytes
 //         of value row 4t+g and accumulates heads x elements.
 // Each item keeps (running max, sum of exponentials, unnormalised output) in
-// the workspace; a second kernel (one workgroup per segment) merges a
-// segment's items (the split-softmax identity) and normalises.  Softmax runs
+// the workspace; a second kernel (one wavefront per segment and query head)
+// merges a segment's items (the split-softmax identity) and normalises.  Softmax runs
 // in the log2 domain with the scale folded into one multiply.
 #include <algorithm>
 #include <atomic>
@@ -187,96 +187,6 @@ __device__ __forceinline__ void compute_tile(WaveState<T, D, HG>& st, const Tile
   __builtin_amdgcn_wave_barrier();
 }
 
-// Merge `cnt` items (first .. first + cnt) of one segment for its G query
-// heads with the split-softmax identity and write the normalised rows to o
-// ([G][D]).  Wavefront h reduces head h's (max, sum); thread t owns output
-// float pair t and sums the weighted partial outputs over all items with up to
-// kBatch loads in flight; the first batch is requested before the statistics
-// so its latency overlaps the reduction.  Called by a whole workgroup.
-template <int HG, int D>
-__device__ void merge_segment(const float2* __restrict__ part_ml, const float* __restrict__ part_o,
-                              int64_t first, int cnt, float* __restrict__ o, int G) {
-  constexpr int kChunk = 64;                      // items weighted per pass
-  constexpr int kBatch = 16;                      // item loads in flight per thread
-  constexpr int E = HG * D;                       // partial-output floats per item
-  constexpr int NP = E / 2;                       // float pairs per item
-  static_assert(D % 2 == 0 && NP <= kThreads && HG <= kWaves, "merge layout");
-  __shared__ float sw[kChunk + kBatch][HG];
-  __shared__ float s_ms[HG], s_inv[HG];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int pr = min(tid, NP - 1);                // this thread's float pair
-  const int h = (2 * pr) / D;
-  const float* po = part_o + first * E + 2 * pr;
-
-  // first batch of partial outputs in flight before the statistics
-  float2 v0[kBatch];
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    v0[u] = *reinterpret_cast<const float2*>(po + (int64_t)min(u, cnt - 1) * E);
-  }
-  float2 mine = make_float2(-INFINITY, 0.f);
-  if (wid < HG) {
-    if (lane < cnt) mine = part_ml[(first + lane) * HG + wid];
-    float M = mine.x, L = mine.y;
-    for (int it = lane + 64; it < cnt; it += 64) {
-      const float2 ml = part_ml[(first + it) * HG + wid];
-      const float mn = fmaxf(M, ml.x);
-      const float ms = mn == -INFINITY ? 0.f : mn;
-      L = L * __builtin_amdgcn_exp2f(M - ms) + ml.y * __builtin_amdgcn_exp2f(ml.x - ms);
-      M = mn;
-    }
-    float Mw = M;
-#pragma unroll
-    for (int x = 1; x < 64; x <<= 1) Mw = fmaxf(Mw, __shfl_xor(Mw, x));
-    const float Ms = Mw == -INFINITY ? 0.f : Mw;
-    float Lw = L * __builtin_amdgcn_exp2f(M - Ms);
-#pragma unroll
-    for (int x = 1; x < 64; x <<= 1) Lw += __shfl_xor(Lw, x);
-    if (lane == 0) {
-      s_ms[wid] = Ms;
-      s_inv[wid] = (Mw == -INFINITY || !(Lw > 0.f)) ? 0.f : 1.f / Lw;
-    }
-  }
-  __syncthreads();
-
-  float2 acc = make_float2(0.f, 0.f);
-  for (int c0 = 0; c0 < cnt; c0 += kChunk) {
-    const int nn = min(kChunk, cnt - c0);
-    if (wid < HG) {
-      const int it = c0 + lane;
-      const float mx = it >= cnt ? -INFINITY
-                                 : (c0 == 0 ? mine.x : part_ml[(first + it) * HG + wid].x);
-      sw[lane][wid] = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - s_ms[wid]) * s_inv[wid];
-      if (lane < kBatch) sw[kChunk + lane][wid] = 0.f;
-    }
-    __syncthreads();
-    for (int j0 = 0; j0 < nn; j0 += kBatch) {
-      float2 v[kBatch];
-      if (c0 == 0 && j0 == 0) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) v[u] = v0[u];
-      } else {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          v[u] = *reinterpret_cast<const float2*>(po + (int64_t)(c0 + min(j0 + u, nn - 1)) * E);
-        }
-      }
-      // weights past the chunk's last item are zero (rows nn .. kChunk + kBatch of sw)
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float wgt = sw[j0 + u][h];
-        acc.x += wgt * v[u].x;
-        acc.y += wgt * v[u].y;
-      }
-    }
-    __syncthreads();
-  }
-  if (tid < NP && h < G) {
-    o[2 * tid] = acc.x;
-    o[2 * tid + 1] = acc.y;
-  }
-}
-
 #ifndef KVSEL_DECODE_MIN_BLOCKS
 #define KVSEL_DECODE_MIN_BLOCKS 1
 #endif
@@ -436,30 +346,82 @@ __global__ __launch_bounds__(kThreads, KVSEL_DECODE_MIN_BLOCKS) void decode_spli
   }
 }
 
-// Second launch, one workgroup per segment: merge the segment's items.  The
-// merge runs in its own kernel on purpose: a hand-off between workgroups of one
-// launch needs device-scope visibility of the partials across the XCDs' L2
-// caches, and both ways of getting it (write-through atomic stores, or L2
-// write-back and invalidate fences) measured far slower than this launch.
+// Second launch: merge each segment's items.  The merge runs in its own kernel
+// on purpose: a hand-off between workgroups of one launch needs device-scope
+// visibility of the partials across the XCDs' L2 caches, and both ways of
+// getting it (write-through atomic stores, or L2 write-back and invalidate
+// fences) measured far slower than this launch.  One single-wavefront
+// workgroup per (segment, query head): the head's statistics over the
+// segment's partials, then its output slice with a chunk of partial loads in
+// flight at once (lane l owns floats 2l, 2l + 1 of the head's D outputs);
+// S*G small workgroups finish sooner than S workgroups doing G heads each.
+constexpr int kHeadChunk = 32;   // partial outputs loaded per round
+
 template <int HG, int D>
-__global__ __launch_bounds__(kThreads) void decode_combine_kernel(
+__global__ __launch_bounds__(64) void decode_combine_head_kernel(
     const float2* __restrict__ part_ml, const float* __restrict__ part_o,
     const int64_t* __restrict__ seg_off, const int32_t* __restrict__ seg_len, int64_t r_cap,
     int hq, int hkv, int G, int S, int rpw, int64_t items_max, float* __restrict__ out) {
-  const int s = blockIdx.x, b = s / hkv, kvh = s % hkv;
+  __shared__ float sw[kHeadChunk];
+  const int s = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  if (h >= G) return;
+  const int b = s / hkv, kvh = s % hkv;
   const uint32_t rpi = (uint32_t)((int64_t)kWaves * rpw);
   const SegLoc loc = wave_locate(seg_off, seg_len, S, r_cap, s, false,
                                  [=](uint32_t l) { return (l + rpi - 1) / rpi; });
-  // overlapping segments (a violated precondition) can ask for more items than
-  // were launched; those were never computed, so clip the range
   const int64_t first = min(loc.first, items_max);
   const int cnt = (int)(min(loc.first + loc.units, items_max) - first);
-  float* o = out + ((int64_t)b * hq + (int64_t)kvh * G) * D;
-  if (cnt <= 0) {  // empty segment: zero output
-    for (int e = threadIdx.x; e < G * D; e += kThreads) o[e] = 0.f;
+  float* o = out + ((int64_t)b * hq + (int64_t)kvh * G + h) * D;
+  constexpr int E = HG * D;
+  const bool mine = 2 * lane < D;
+  const float* po = part_o + first * E + h * D + (mine ? 2 * lane : 0);
+  if (cnt <= 0) {
+    if (mine) *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(0.f, 0.f);
     return;
   }
-  merge_segment<HG, D>(part_ml, part_o, first, cnt, o, G);
+  // first chunk of outputs in flight while the statistics are reduced
+  float2 v[kHeadChunk];
+#pragma unroll
+  for (int u = 0; u < kHeadChunk; ++u)
+    v[u] = *reinterpret_cast<const float2*>(po + (int64_t)min(u, cnt - 1) * E);
+  float M = -INFINITY, L = 0.f;
+  for (int it = lane; it < cnt; it += 64) {
+    const float2 ml = part_ml[(first + it) * HG + h];
+    const float mn = fmaxf(M, ml.x);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    L = L * __builtin_amdgcn_exp2f(M - ms) + ml.y * __builtin_amdgcn_exp2f(ml.x - ms);
+    M = mn;
+  }
+  float Mw = M;
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) Mw = fmaxf(Mw, __shfl_xor(Mw, x));
+  const float Ms = Mw == -INFINITY ? 0.f : Mw;
+  float Lw = L * __builtin_amdgcn_exp2f(M - Ms);
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) Lw += __shfl_xor(Lw, x);
+  const float inv = (Mw == -INFINITY || !(Lw > 0.f)) ? 0.f : 1.f / Lw;
+  float2 acc = make_float2(0.f, 0.f);
+  for (int c0 = 0; c0 < cnt; c0 += kHeadChunk) {
+    const int nn = min(kHeadChunk, cnt - c0);
+    if (c0) {
+#pragma unroll
+      for (int u = 0; u < kHeadChunk; ++u)
+        v[u] = *reinterpret_cast<const float2*>(po + (int64_t)(c0 + min(u, nn - 1)) * E);
+    }
+    if (lane < kHeadChunk) {
+      const float mx = lane < nn ? part_ml[(first + c0 + lane) * HG + h].x : -INFINITY;
+      sw[lane] = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - Ms) * inv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kHeadChunk; ++u) {
+      const float wgt = sw[u];   // zero past the chunk's last item
+      acc.x += wgt * v[u].x;
+      acc.y += wgt * v[u].y;
+    }
+    __syncthreads();
+  }
+  if (mine) *reinterpret_cast<float2*>(o + 2 * lane) = acc;
 }
 
 int hg_for(int G) { return G <= 1 ? 1 : (G <= 2 ? 2 : 4); }
@@ -499,7 +461,7 @@ hipError_t run(int batch, int hq, int hkv, float scale, const void* q, const voi
       static_cast<const char*>(q), static_cast<const char*>(k_c),
       static_cast<const char*>(v_c), seg_off, seg_len, r_cap, S, hq, hkv, G, c, rpw, ml, po, rope,
       q_pos);
-  decode_combine_kernel<HG, D><<<dim3(S), dim3(kThreads), 0, stream>>>(
+  decode_combine_head_kernel<HG, D><<<dim3(S, HG), dim3(64), 0, stream>>>(
       ml, po, seg_off, seg_len, r_cap, hq, hkv, G, S, rpw, items, out);
   return hipGetLastError();
 }
