@@ -1132,3 +1132,63 @@ def test_c2_model_full_sampled(kv):
         g = l * S + s
         kept = idx[off[g]:off[g] + lens[l, s]].astype(np.int64)
         assert np.max(np.abs(kmh[s] - P[:, kept].sum(axis=1))) <= 1e-5
+
+
+def test_graph_replays_lmba_vote_rope(kv):
+    """The multi-launch entry points under HIP graph capture: kvsel_lmba (rows,
+    mask, row select), kvsel_chunk_vote (setup, per-layer select, keys) and the
+    fused-RoPE score and decode, captured once and replayed with eager work and
+    workspace clobbering in between; every replay equals the eager results bit
+    for bit."""
+    kvsel, pipeline, torch = kv
+    _say("graph replay: lmba, chunk vote, fused RoPE")
+    cfg = kvsynth.get_config(1, n=3000)
+    inputs, run = _run(kv, cfg)
+    S, R = cfg.batch * cfg.hkv, cfg.G * cfg.w
+    lm = torch.empty(S * R, dtype=torch.int32, device="cuda")
+    km = torch.empty(S * R, dtype=torch.float32, device="cuda")
+    lws = torch.empty(kvsel.kvsel_lmba_workspace(run.shape, cfg.w), dtype=torch.uint8, device="cuda")
+    # chunk vote over three "layers" of scores (the window scores, scaled differently)
+    vsh = kvsel.make_shape(cfg.batch, cfg.hq, cfg.hkv, 64, cfg.n, "bf16", 1.0)
+    lay = torch.stack([run.scores, run.scores.flip(0), run.scores * 0.5]).contiguous()
+    key = torch.empty(S * cfg.n, dtype=torch.float32, device="cuda")
+    vws = torch.empty(kvsel.kvsel_chunk_vote_workspace(vsh, 3, 40), dtype=torch.uint8,
+                      device="cuda")
+    # fused RoPE score and decode on the same layer (identity pair list)
+    tab = pipeline.device_tensor(kvsynth.rope_table(cfg.n + 8, 64))
+    pairs = pipeline.device_tensor(np.tile(np.arange(64, dtype=np.int32), (cfg.hkv, 1)))
+    sh = run.shape
+    fused = kvsel.make_shape(sh.batch, sh.hq, sh.hkv, sh.head_dim, sh.n, sh.dtype, sh.scale,
+                             rope=kvsel.make_rope(tab, pairs, q_pos=cfg.n))
+    rsc = torch.empty_like(run.scores)
+    rws = torch.empty(kvsel.kvsel_score_workspace(fused, cfg.w), dtype=torch.uint8, device="cuda")
+    rout = torch.empty_like(run.out)
+
+    def work():
+        kvsel.kvsel_lmba(run.shape, cfg.w, cfg.n - cfg.w, run.q_win, run.k, lm, lws,
+                         run.seg_off, run.seg_len, run.idx, run.r_cap, km)
+        kvsel.kvsel_chunk_vote(vsh, 3, 40, lay, key, vws)
+        kvsel.kvsel_score(fused, cfg.w, cfg.n - cfg.w, run.q_win, run.k, rsc, rws)
+        kvsel.kvsel_decode_attn(fused, run.q_dec, run.k_c, run.v_c, run.seg_off, run.seg_len,
+                                run.r_cap, rout, run.ws_dec)
+    outs = (lm, km, key, rsc, rout)
+    work()
+    torch.cuda.synchronize()
+    want = [pu.to_host(t).copy() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+    other_inputs, other = _run(kv, kvsynth.get_config(1, n=1111))
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        for w_ in (lws, vws, rws):
+            w_.fill_(0x5A + rep)
+        other.run()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, t in enumerate(outs):
+            got = pu.to_host(t)
+            assert np.array_equal(got.view(np.uint8), want[i].view(np.uint8)), (rep, i)
