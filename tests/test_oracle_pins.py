@@ -662,3 +662,31 @@ def test_vote_key_orders_by_votes_then_attention():
         m = votes == v
         o = np.argsort(-key[m], kind="stable")
         assert np.all(np.diff(tot[m][o]) <= 1e-6)     # within a vote count: summed attention
+
+
+def test_score_c0_against_plain_loops():
+    """A guard against array-broadcasting slips: the C0 window score written as
+    plain loops over heads, window rows, keys and dimensions (math.exp, fsum)
+    equals the vectorised oracle on one C0 segment."""
+    import kvsynth
+    cfg = kvsynth.get_config(0)
+    x = kvsynth.segment_inputs(cfg, 0, 0, 1)
+    q = oracle.to_f64(x["q_win"])          # [G][w][d]
+    k = oracle.to_f64(x["K"])              # [n][d]
+    G, w, d = q.shape
+    n = k.shape[0]
+    q0 = n - w
+    kl, ql = k.tolist(), q.tolist()
+    s = [0.0] * n
+    for h in range(G):
+        for i in range(w):
+            vis = q0 + i + 1
+            logits = [cfg.scale * math.fsum(ql[h][i][c] * kl[j][c] for c in range(d))
+                      for j in range(vis)]
+            m = max(logits)
+            e = [math.exp(v - m) for v in logits]
+            z = math.fsum(e)
+            for j in range(vis):
+                s[j] += e[j] / z
+    want = oracle.window_scores(q, k, cfg.scale, q0)
+    assert np.max(np.abs(np.array(s) - want)) < 1e-12
