@@ -350,6 +350,32 @@ def main() -> int:
     torch.cuda.synchronize()
     append_us = a_ev[0].elapsed_time(a_ev[1]) / (5 * L) * 1e3
 
+    # C3 extra, outside the timed steps: FastGen head policies over RAP
+    # pair-pruned keys (d = 88), one layer: ragged segments of 32768 / 2048 /
+    # 656 rows; its compact and decode rates beside C2's
+    c3 = kvsynth.get_config(3)
+    run3 = pipeline.build_layer(c3, kvsynth.layer_inputs(c3, 0))
+    run3.select(); run3.compact(); run3.decode()
+    torch.cuda.synchronize()
+    rows3 = int(pu_host(run3.seg_len).sum())
+
+    def rate(fn, reps):
+        g = capture(fn)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        g.replay()
+        e[0].record()
+        for _ in range(reps):
+            g.replay()
+        e[1].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / reps * 1e3
+    c3_dec_us, c3_cmp_us = rate(run3.decode, 10), rate(run3.compact, 5)
+    c3_dec_bytes = rows3 * c3.d * c3.es * 2 + c3.batch * c3.hq * c3.d * (c3.es + 4)
+    c3_cmp_bytes = rows3 * (c3.d * c3.es * 4 + 4)
+    del run3
+    log(f"[bench] C3: decode {c3_dec_us:.1f} us ({c3_dec_bytes / c3_dec_us / 1e3:.0f} GB/s), "
+        f"compact {c3_cmp_us:.1f} us ({c3_cmp_bytes / c3_cmp_us / 1e3:.0f} GB/s)")
+
     es, d, hq, hkv, n = cfg.es, cfg.d, cfg.hq, cfg.hkv, cfg.n
     lens = pu_host(mr.seg_len).reshape(L, S)
     rows = [int(lens[l].sum()) for l in range(L)]
@@ -412,6 +438,16 @@ def main() -> int:
                                 "32 segments of a layer (rows materialised, 90 %-mass radix "
                                 "select per row, kept mass of the top-B selection), outside "
                                 "the timed step",
+                   "c3_policy_d88": {
+                       "rows": rows3,
+                       "decode_us": round(c3_dec_us, 2),
+                       "decode_GBps": round(c3_dec_bytes / c3_dec_us / 1e3, 1),
+                       "decode_frac": round(c3_dec_bytes / c3_dec_us / 1e3 / PEAK_HBM_GBS, 4),
+                       "compact_us": round(c3_cmp_us, 2),
+                       "compact_GBps": round(c3_cmp_bytes / c3_cmp_us / 1e3, 1),
+                       "compact_frac": round(c3_cmp_bytes / c3_cmp_us / 1e3 / PEAK_HBM_GBS, 4),
+                       "note": "one C3 layer (batch 8, FastGen local / special / global heads, "
+                               "RAP pair-pruned d = 88), outside the timed step"},
                    "layer_lmba_mean_tokens": [round(x, 1) for x in layer_lmba],
                    "attention_loss_topb_per_layer": [round(x, 5) for x in att_loss]},
         "decode_frac_of_copy_reference": round(dec_gbs / copy_gbs, 4),
