@@ -376,6 +376,21 @@ def main() -> int:
     log(f"[bench] C3: decode {c3_dec_us:.1f} us ({c3_dec_bytes / c3_dec_us / 1e3:.0f} GB/s), "
         f"compact {c3_cmp_us:.1f} us ({c3_cmp_bytes / c3_cmp_us / 1e3:.0f} GB/s)")
 
+    # C4 extra: ChunkLLM at 128K context, one layer: chunk scores (w = 1 over
+    # the compressed chunk keys), chunk select to 48 % of the tokens, compact,
+    # decode
+    c4 = kvsynth.get_config(4)
+    run4 = pipeline.build_layer(c4, kvsynth.layer_inputs(c4, 0))
+    run4.run()
+    torch.cuda.synchronize()
+    rows4 = int(pu_host(run4.seg_len).sum())
+    c4_us = {k: rate(getattr(run4, k), 5) for k in ("score", "select", "compact", "decode")}
+    c4_dec_bytes = rows4 * c4.d * c4.es * 2 + c4.batch * c4.hq * c4.d * (c4.es + 4)
+    c4_cmp_bytes = rows4 * (c4.d * c4.es * 4 + 4)
+    del run4
+    log(f"[bench] C4: score {c4_us['score']:.1f} select {c4_us['select']:.1f} compact "
+        f"{c4_us['compact']:.1f} decode {c4_us['decode']:.1f} us")
+
     es, d, hq, hkv, n = cfg.es, cfg.d, cfg.hq, cfg.hkv, cfg.n
     lens = pu_host(mr.seg_len).reshape(L, S)
     rows = [int(lens[l].sum()) for l in range(L)]
@@ -448,6 +463,16 @@ def main() -> int:
                        "compact_frac": round(c3_cmp_bytes / c3_cmp_us / 1e3 / PEAK_HBM_GBS, 4),
                        "note": "one C3 layer (batch 8, FastGen local / special / global heads, "
                                "RAP pair-pruned d = 88), outside the timed step"},
+                   "c4_chunk_128k": {
+                       "rows": rows4,
+                       "stages_us": {k: round(v, 2) for k, v in c4_us.items()},
+                       "decode_GBps": round(c4_dec_bytes / c4_us["decode"] / 1e3, 1),
+                       "decode_frac": round(c4_dec_bytes / c4_us["decode"] / 1e3 / PEAK_HBM_GBS, 4),
+                       "compact_GBps": round(c4_cmp_bytes / c4_us["compact"] / 1e3, 1),
+                       "compact_frac": round(c4_cmp_bytes / c4_us["compact"] / 1e3 / PEAK_HBM_GBS,
+                                             4),
+                       "note": "one C4 layer (batch 1, 131072 tokens, chunk keys of 64 dims, "
+                               "chunks kept to 48 % of the tokens), outside the timed step"},
                    "layer_lmba_mean_tokens": [round(x, 1) for x in layer_lmba],
                    "attention_loss_topb_per_layer": [round(x, 5) for x in att_loss]},
         "decode_frac_of_copy_reference": round(dec_gbs / copy_gbs, 4),
