@@ -248,6 +248,7 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
   __shared__ uint32_t blk_a[kWaves * KPT], blk_b[kWaves * KPT];
   __shared__ uint32_t wave_tot[kWaves];
   __shared__ uint32_t sel_digit, sel_above;
+  __shared__ uint32_t w_before[kWaves][64], w_start[kWaves][64];   // per-wave emission tables
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int s = blockIdx.x;
@@ -366,18 +367,32 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
   __syncthreads();
   const uint32_t kept_total = block_scan_lds(blk_b, KPT * kWaves, wave_tot);
   if (tid == 0) seg_len[s] = (int32_t)kept_total;
-  // 3) write the kept chunks' token ranges
+  // 3) write the kept chunks' token ranges.  The 64 chunks of a wavefront
+  // (fixed k) are consecutive, so their kept tokens fill one contiguous run of
+  // the output; the lanes write that run together (coalesced), each output
+  // slot finding its chunk by a binary search over the wavefront's exclusive
+  // prefix of kept tokens (the last chunk whose prefix is <= the slot).
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const int64_t j = (int64_t)k * kThreads + tid;
     const uint32_t kw = kept_tokens(k);
-    const uint32_t before = wave_incl_scan_u32(kw) - kw;
-    const int64_t pos = (int64_t)blk_b[k * kWaves + wid] + before;
-    if (kw) {
-      const int64_t st = j ? ce[j - 1] : 0;
-      for (uint32_t t = 0; t < kw; ++t)
-        if (pos + t < room) idx[off + pos + t] = (int32_t)(st + t);
+    const uint32_t incl = wave_incl_scan_u32(kw);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    w_before[wid][lane] = incl - kw;
+    w_start[wid][lane] = (uint32_t)(j < N ? (j ? ce[j - 1] : 0) : 0);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t base = (int64_t)blk_b[k * kWaves + wid];
+    for (uint32_t p = lane; p < total; p += 64) {
+      int lo = 0;
+#pragma unroll
+      for (int step = 32; step > 0; step >>= 1)
+        if (w_before[wid][lo + step] <= p) lo += step;
+      const int64_t pos = base + p;
+      if (pos < room) idx[off + pos] = (int32_t)(w_start[wid][lo] + (p - w_before[wid][lo]));
     }
+    __builtin_amdgcn_wave_barrier();   // the tables are rewritten for the next k
   }
 }
 
