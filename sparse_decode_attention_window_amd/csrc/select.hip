@@ -248,7 +248,6 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
   __shared__ uint32_t blk_a[kWaves * KPT], blk_b[kWaves * KPT];
   __shared__ uint32_t wave_tot[kWaves];
   __shared__ uint32_t sel_digit, sel_above;
-  __shared__ uint32_t w_before[kWaves][64], w_start[kWaves][64];   // per-wave emission tables
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int s = blockIdx.x;
@@ -278,6 +277,7 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
 
   // ---- chunks into registers (all loads independent) ----------------------
   uint32_t key[KPT], wt[KPT];   // wt: the chunk's token count (0 past N)
+  uint32_t first_tok[KPT];      // the chunk's first token position
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const int64_t j = (int64_t)k * kThreads + tid;
@@ -285,6 +285,7 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
     key[k] = jc >= first_local ? kForcedKey : score_key(sc[jc]);
     const int64_t lo = jc ? ce[jc - 1] : 0;
     wt[k] = j < N ? (uint32_t)(ce[jc] - lo) : 0u;
+    first_tok[k] = (uint32_t)lo;
   }
   // selection weight: 1 per chunk (count mode) or its token count
   auto wsel = [&](int k) -> uint32_t { return by_count ? (wt[k] ? 1u : 0u) : wt[k]; };
@@ -369,30 +370,24 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
   if (tid == 0) seg_len[s] = (int32_t)kept_total;
   // 3) write the kept chunks' token ranges.  The 64 chunks of a wavefront
   // (fixed k) are consecutive, so their kept tokens fill one contiguous run of
-  // the output; the lanes write that run together (coalesced), each output
-  // slot finding its chunk by a binary search over the wavefront's exclusive
-  // prefix of kept tokens (the last chunk whose prefix is <= the slot).
+  // the output; the wavefront walks its kept chunks (set bits of a ballot)
+  // and writes each chunk's range with all lanes, coalesced.
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
-    const int64_t j = (int64_t)k * kThreads + tid;
     const uint32_t kw = kept_tokens(k);
-    const uint32_t incl = wave_incl_scan_u32(kw);
-    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    w_before[wid][lane] = incl - kw;
-    w_start[wid][lane] = (uint32_t)(j < N ? (j ? ce[j - 1] : 0) : 0);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t before = wave_incl_scan_u32(kw) - kw;
+    const uint32_t st = first_tok[k];
     const int64_t base = (int64_t)blk_b[k * kWaves + wid];
-    for (uint32_t p = lane; p < total; p += 64) {
-      int lo = 0;
-#pragma unroll
-      for (int step = 32; step > 0; step >>= 1)
-        if (w_before[wid][lo + step] <= p) lo += step;
-      const int64_t pos = base + p;
-      if (pos < room) idx[off + pos] = (int32_t)(w_start[wid][lo] + (p - w_before[wid][lo]));
+    uint64_t m = __ballot(kw > 0u);
+    while (m) {
+      const int c = __builtin_ctzll(m);
+      m &= m - 1;
+      const uint32_t kc = (uint32_t)__builtin_amdgcn_readlane((int)kw, c);
+      const int64_t pc = base + (uint32_t)__builtin_amdgcn_readlane((int)before, c);
+      const uint32_t sc = (uint32_t)__builtin_amdgcn_readlane((int)st, c);
+      for (uint32_t t = lane; t < kc; t += 64)
+        if (pc + t < room) idx[off + pc + t] = (int32_t)(sc + t);
     }
-    __builtin_amdgcn_wave_barrier();   // the tables are rewritten for the next k
   }
 }
 
