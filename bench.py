@@ -93,9 +93,12 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
         rs = rows(path, counter)
         copies = [reference_copy(rs)]
         factor = known / (copies[0] * 1024)
+        # the C2 step's decode dispatches all come before the first extra
+        # workload (LMBA opens them); the C3 / C4 extras reuse the decode kernels
+        end = next((i for i, (k, _) in enumerate(rs) if "lmba_row_kernel" in k), len(rs))
         kern = {}
         for name in DECODE_KERNELS:
-            vals = [v for k, v in rs if name in k]
+            vals = [v for k, v in rs[:end] if name in k]
             assert vals, f"no {name} dispatch in {path}"
             kern[name] = {"dispatches": len(vals), "mean_KiB": sum(vals) / len(vals)}
         launch_kib = sum(k["mean_KiB"] for k in kern.values())
