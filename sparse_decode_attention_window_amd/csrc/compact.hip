@@ -6,6 +6,8 @@
 // balanced however uneven the segment lengths are: consecutive lanes take
 // consecutive 16-byte chunks of the destination, so every store is fully
 // coalesced and every gathered source row is read as one contiguous run.
+// Source rows are read with non-temporal loads (each is read once); the
+// packed rows are stored plainly (non-temporal stores measured slower here).
 #include "kvsel_internal.h"
 
 namespace kvsel {
@@ -31,21 +33,32 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
   segment_table<kThreads>(seg_off, seg_len, S, r_cap, pre, off, len,
                           [](int64_t l) { return l; });
   const int64_t total = pre[S] * CPR;
-  const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
+  // each wavefront copies runs of 64 * kUnroll consecutive destination vectors;
+  // the segment of a run's first row is looked up once, and lanes whose row
+  // lies further on step forward from it
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  constexpr int64_t kRun = 64 * kUnroll;
+  const int64_t stride = (int64_t)gridDim.x * (kThreads / 64) * kRun;
   const u32x4 zero = {0, 0, 0, 0};
-  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll; base < total; base += step) {
-    // phase 1: locate every vector and fetch its source index (all loads independent)
+  for (int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wid) * kRun; base < total;
+       base += stride) {
+    const int seg0 = __builtin_amdgcn_readfirstlane(find_segment(pre, S, base / CPR));
     int64_t row[kUnroll];
     int seg[kUnroll], col[kUnroll];
     int32_t src[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t g0 = base + u * kThreads + threadIdx.x;
+      const int64_t g0 = base + u * 64 + lane;
       const int64_t g = g0 < total ? g0 : total - 1;   // clamped: always a real vector
       const int64_t flat = g / CPR;
       col[u] = (int)(g - flat * CPR);
-      seg[u] = find_segment(pre, S, flat);
-      row[u] = off[seg[u]] + (flat - pre[seg[u]]);
+      int sg = seg0;
+      for (int step = 0; sg + 1 < S && pre[sg + 1] <= flat; ++step) {
+        if (step == 8) { sg = find_segment(pre, S, flat); break; }
+        ++sg;
+      }
+      seg[u] = sg;
+      row[u] = off[sg] + (flat - pre[sg]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) src[u] = idx[row[u]];
@@ -62,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
     // phase 3: coalesced stores
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (base + u * kThreads + threadIdx.x < total) {
+      if (base + u * 64 + lane < total) {
         const int64_t d = row[u] * CPR + col[u];
         k_c[d] = ok[u] ? kv[u] : zero;
         v_c[d] = ok[u] ? vv[u] : zero;
