@@ -69,6 +69,39 @@ def copy_reference(torch, reps: int = 5) -> float:
     return 2 * COPY_BYTES / t / 1e9
 
 
+def stream_ceiling(torch, kvsel, mode: int, moved: int, nb: int = 4, calls: int = 8) -> float:
+    """GB/s of the library's non-temporal HBM stream (kvsel_hbm_probe) at one
+    call's size: `moved` bytes per call (read, or read + write for a copy), in
+    a graph of `calls` back-to-back calls over `nb` rotating buffers."""
+    per = (moved if mode == kvsel.KVSEL_PROBE_READ else moved // 2) // 16 * 16
+    srcs = [torch.ones(per // 2, dtype=torch.bfloat16, device="cuda") for _ in range(nb)]
+    dst_bytes = kvsel.KVSEL_PROBE_BLOCKS * 16 if mode == kvsel.KVSEL_PROBE_READ else per
+    dsts = [torch.empty(dst_bytes, dtype=torch.uint8, device="cuda") for _ in range(nb)]
+
+    def run():
+        for i in range(calls):
+            kvsel.kvsel_hbm_probe(mode, srcs[i % nb], dsts[i % nb], per)
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(10):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        g.replay()
+        e[1].record()
+        torch.cuda.synchronize()
+        ts.append(e[0].elapsed_time(e[1]) * 1e-3 / calls)
+    del g, srcs, dsts
+    ts.sort()
+    moved_per = per if mode == kvsel.KVSEL_PROBE_READ else 2 * per
+    return moved_per / ts[len(ts) // 2] / 1e9
+
+
 def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
     """HBM bytes per decode launch from two rocprofv3 --pmc runs of this
     script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by the
@@ -407,6 +440,12 @@ def main() -> int:
     gbs = lambda b, t_us: b / (t_us * 1e-6) / 1e9
 
     dec_gbs = gbs(dec_bytes, us["decode"])
+    cmp_gbs = gbs(cmp_bytes, us["compact"])
+    # what a plain non-temporal stream of the same size per call reaches here
+    read_ceiling = stream_ceiling(torch, kvsel, kvsel.KVSEL_PROBE_READ, int(dec_bytes))
+    copy_ceiling = stream_ceiling(torch, kvsel, kvsel.KVSEL_PROBE_COPY, int(cmp_bytes))
+    log(f"[bench] stream ceilings at the call sizes: read {read_ceiling:.0f} GB/s, "
+        f"copy {copy_ceiling:.0f} GB/s")
     traffic = None
     if os.path.exists(COUNTERS):
         with open(COUNTERS) as f:
@@ -479,7 +518,15 @@ def main() -> int:
                    "layer_lmba_mean_tokens": [round(x, 1) for x in layer_lmba],
                    "attention_loss_topb_per_layer": [round(x, 5) for x in att_loss]},
         "decode_frac_of_copy_reference": round(dec_gbs / copy_gbs, 4),
-        "compact_frac_of_copy_reference": round(gbs(cmp_bytes, us["compact"]) / copy_gbs, 4),
+        "compact_frac_of_copy_reference": round(cmp_gbs / copy_gbs, 4),
+        "hbm_stream_ceilings": {
+            "read_GBps": round(read_ceiling, 1), "read_bytes_per_call": int(dec_bytes),
+            "copy_GBps": round(copy_ceiling, 1), "copy_bytes_per_call": int(cmp_bytes),
+            "method": "kvsel_hbm_probe non-temporal read / copy streams at the decode and "
+                      "compact call sizes, graph of 8 back-to-back calls over 4 rotating "
+                      "buffers"},
+        "decode_frac_of_read_ceiling": round(dec_gbs / read_ceiling, 4),
+        "compact_frac_of_copy_ceiling": round(cmp_gbs / copy_ceiling, 4),
         "stages_roofline": {
             "score": {"bound": "hbm", "GB/s": round(gbs(sc_bytes, us["score"]), 1),
                       "frac": round(gbs(sc_bytes, us["score"]) / PEAK_HBM_GBS, 4),
@@ -489,8 +536,8 @@ def main() -> int:
                       "algorithmic_bytes": int(sc_bytes)},
             "select": {"GB/s": round(gbs(sel_bytes, us["select"]), 1),
                        "algorithmic_bytes": int(sel_bytes)},
-            "compact": {"bound": "hbm", "GB/s": round(gbs(cmp_bytes, us["compact"]), 1),
-                        "frac": round(gbs(cmp_bytes, us["compact"]) / PEAK_HBM_GBS, 4),
+            "compact": {"bound": "hbm", "GB/s": round(cmp_gbs, 1),
+                        "frac": round(cmp_gbs / PEAK_HBM_GBS, 4),
                         "algorithmic_bytes": int(cmp_bytes)},
             "decode": {"bound": "hbm", "GB/s": round(dec_gbs, 1),
                        "frac": round(dec_gbs / PEAK_HBM_GBS, 4),

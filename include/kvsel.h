@@ -295,6 +295,23 @@ kvsel_status kvsel_append(const kvsel_shape* s /*host*/, const void* k_new, cons
 kvsel_status kvsel_zigzag_budgets(const double* profile, int32_t L, int64_t n,
                                   int64_t avg_budget, int64_t floor_budget, int32_t* out);
 
+/* ------------------------------------------------------ measurement aid --
+ * Not part of the method: a plain HBM stream that sets the rate a call of a
+ * given size can reach on this GPU, for the bandwidth figures beside each
+ * kernel's own.  16-byte non-temporal accesses over a fixed grid of
+ * KVSEL_PROBE_BLOCKS workgroups; asynchronous on `stream`.
+ *   mode   KVSEL_PROBE_READ: read src; dst receives one 16-byte XOR fold per
+ *          workgroup, dst[KVSEL_PROBE_BLOCKS][16 bytes] (the XOR of those
+ *          words is the XOR of all of src's 16-byte words);
+ *          KVSEL_PROBE_COPY: copy `bytes` of src to dst (not overlapping).
+ *   src, dst  device pointers, 16-byte aligned; bytes > 0, a multiple of 16.
+ * Errors: EINVAL for another mode, NULL or misaligned pointers, or bytes not
+ * a positive multiple of 16. */
+#define KVSEL_PROBE_BLOCKS 2048
+typedef enum { KVSEL_PROBE_READ = 0, KVSEL_PROBE_COPY = 1 } kvsel_probe_mode;
+kvsel_status kvsel_hbm_probe(int32_t mode, const void* src, void* dst, int64_t bytes,
+                             hipStream_t stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* kvsel_last_error(void);
 

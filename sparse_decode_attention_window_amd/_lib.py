@@ -86,6 +86,8 @@ _SIGS = {
     "kvsel_zigzag_budgets": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.c_int32,
                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.POINTER(ctypes.c_int32)]),
+    "kvsel_hbm_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_void_p]),
     "kvsel_last_error": (ctypes.c_char_p, []),
     "kvsel_version": (ctypes.c_char_p, []),
 }
@@ -227,6 +229,16 @@ def kvsel_zigzag_budgets(profile, n: int, avg_budget: int, floor_budget: int):
     _check(lib().kvsel_zigzag_budgets(arr, L, int(n), int(avg_budget), int(floor_budget), out),
            "kvsel_zigzag_budgets")
     return [int(out[i]) for i in range(L)]
+
+
+KVSEL_PROBE_READ, KVSEL_PROBE_COPY, KVSEL_PROBE_BLOCKS = 0, 1, 2048
+
+
+def kvsel_hbm_probe(mode: int, src, dst, nbytes: int, stream=None) -> None:
+    """Measurement aid: non-temporal HBM read (dst gets one 16-byte fold per
+    workgroup) or copy stream over `nbytes` of src."""
+    _check(lib().kvsel_hbm_probe(int(mode), _ptr(src), _ptr(dst), int(nbytes), _stream(stream)),
+           "kvsel_hbm_probe")
 
 
 def kvsel_last_error() -> str:

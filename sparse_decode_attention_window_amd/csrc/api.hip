@@ -118,6 +118,19 @@ const char* kvsel_last_error(void) { return g_err; }
 
 const char* kvsel_version(void) { return "kvsel 0.1.0 gfx950"; }
 
+kvsel_status kvsel_hbm_probe(int32_t mode, const void* src, void* dst, int64_t bytes,
+                             hipStream_t stream) {
+  g_err[0] = 0;
+  static_assert(KVSEL_PROBE_BLOCKS == kProbeBlocks, "probe grid");
+  if (mode != KVSEL_PROBE_READ && mode != KVSEL_PROBE_COPY)
+    return fail(KVSEL_EINVAL, "probe mode must be KVSEL_PROBE_READ or KVSEL_PROBE_COPY");
+  if (!src || !dst) return fail(KVSEL_EINVAL, "src and dst must be non-NULL");
+  if (((uintptr_t)src | (uintptr_t)dst) % 16)
+    return fail(KVSEL_EINVAL, "src and dst must be 16-byte aligned");
+  if (bytes <= 0 || bytes % 16) return fail(KVSEL_EINVAL, "bytes must be a positive multiple of 16");
+  return hip_status(launch_probe(mode, src, dst, bytes, stream), "kvsel_hbm_probe launch");
+}
+
 // Score workspace of a valid shape (unrotated queries add their rotated copy).
 static size_t score_ws(const kvsel_shape* s, int32_t w) {
   const size_t rope = s->rope ? (size_t)s->batch * s->hq * w * s->head_dim * elem_size(s) : 0;

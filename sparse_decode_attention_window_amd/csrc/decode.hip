@@ -84,11 +84,15 @@ int64_t max_items(int64_t r_cap, int S) {
   return (r_cap + kWaves * kTile - 1) / (kWaves * kTile) + S;
 }
 
-// K and V rows are read exactly once per call: non-temporal loads keep them
-// from displacing what the caches hold (measured 2 % faster at 6553 rows per
-// segment, 7 % at 14358).
+// K and V rows are read exactly once per call: when rows fill whole 128-byte
+// cache lines, non-temporal loads keep them from displacing what the caches
+// hold (2 % faster at 6553 rows per segment, 6 % on 8 x 62946 rows).  Rows
+// that share lines with their neighbours (head_dim 88: 176 or 352 bytes) use
+// plain loads: streamed lines were refetched for the next row (8 % slower).
+template <bool STREAM>
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return load16(p);
 }
 
 template <typename T, int D>
@@ -112,9 +116,9 @@ __device__ __forceinline__ void load_tile(TileRegs<T, D>& r, const char* kt, con
   for (int a = 0; a < Gm::NA; ++a) {
     const int o = 64 * a + 16 * grp;
     if (64 * (a + 1) <= Gm::RB) {
-      r.k[a] = load16_stream(kt + kr + o);
+      r.k[a] = load16_stream<Gm::RB % 128 == 0>(kt + kr + o);
     } else {  // last, partial step (head_dim 88): lanes past the row read zeros
-      const u32x4 x = load16_stream(kt + kr + min(o, Gm::RB - 16));
+      const u32x4 x = load16_stream<Gm::RB % 128 == 0>(kt + kr + min(o, Gm::RB - 16));
       r.k[a] = o < Gm::RB ? x : zero;
     }
   }
@@ -125,7 +129,7 @@ __device__ __forceinline__ void load_tile(TileRegs<T, D>& r, const char* kt, con
     for (int x = 0; x < Gm::CPL; ++x) {
       // lanes past the row's last chunk reread it; their sums are never stored
       const int ch = min(l16 + 16 * x, Gm::NCH - 1);
-      r.v[t][x] = load16_stream(vt + vr + 16 * ch);
+      r.v[t][x] = load16_stream<Gm::RB % 128 == 0>(vt + vr + 16 * ch);
     }
   }
 }

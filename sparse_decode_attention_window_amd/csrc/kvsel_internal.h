@@ -311,6 +311,11 @@ hipError_t launch_select_policy(int S, int hkv, int64_t n, const int8_t* head_ki
                                 int64_t n_special, const int64_t* seg_off, int32_t* seg_len,
                                 int32_t* idx, int64_t r_cap, hipStream_t stream);
 
+// Measurement aid: HBM read (mode 0, one 16-byte fold per workgroup into dst)
+// or copy (mode 1) stream over a fixed grid of kProbeBlocks workgroups.
+constexpr int kProbeBlocks = 2048;
+hipError_t launch_probe(int mode, const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 size_t decode_workspace_bytes(int S, int head_dim, int G, int64_t r_cap);
 hipError_t launch_decode(int dtype, int head_dim, int batch, int hq, int hkv, float scale,
                          const void* q, const void* k_c, const void* v_c,

@@ -254,3 +254,26 @@ def test_budgets_reject():
         kvsel.kvsel_zigzag_budgets([1.0, -2.0], 100, 10, 1)
     with pytest.raises(kvsel.KvselError):
         kvsel.kvsel_zigzag_budgets([], 100, 10, 1)
+
+
+def test_hbm_probe_rejects_bad_arguments():
+    """The measurement stream checks mode, pointers, alignment and size on the
+    host and enqueues nothing when a check fails."""
+    probe = kvsel.lib().kvsel_hbm_probe
+    ok_src, ok_dst = FAKE, FAKE + 0x100000
+    cases = [
+        (2, ok_src, ok_dst, 1024),          # unknown mode
+        (-1, ok_src, ok_dst, 1024),
+        (0, None, ok_dst, 1024),            # NULL source
+        (1, ok_src, None, 1024),            # NULL destination
+        (1, ok_src + 8, ok_dst, 1024),      # misaligned source
+        (0, ok_src, ok_dst + 4, 1024),      # misaligned destination
+        (1, ok_src, ok_dst, 0),             # empty
+        (1, ok_src, ok_dst, -16),
+        (0, ok_src, ok_dst, 1000),          # not a multiple of 16
+    ]
+    for mode, src, dst, nbytes in cases:
+        st = probe(mode, src, dst, nbytes, None)
+        assert st == 1, (mode, src, dst, nbytes, st)   # KVSEL_EINVAL
+        assert kvsel.kvsel_last_error()
+    assert kvsel.KVSEL_PROBE_BLOCKS == 2048
