@@ -251,6 +251,9 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int s = blockIdx.x;
+  // the segment's gridDim.y workgroups all select; part y writes only output
+  // positions [y * span, (y + 1) * span) of the kept tokens
+  const int part = blockIdx.y, parts = gridDim.y;
   const int b = s / hkv;
   const float* sc = scores + (int64_t)s * N;
   const int64_t* ce = chunk_end + (int64_t)b * N;
@@ -270,8 +273,11 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
   tgt = tgt < 0 ? 0 : (tgt > total ? total : tgt);
   if (tgt == 0 || tgt == total) {
     const int64_t keep = tgt == 0 ? 0 : tokens;   // nothing, or every chunk: [0, tokens)
-    for (int64_t r = tid; r < keep && r < room; r += kThreads) idx[off + r] = (int32_t)r;
-    if (tid == 0) seg_len[s] = (int32_t)keep;
+    const int64_t span = (keep + parts - 1) / parts;
+    const int64_t hi = min(keep, (int64_t)(part + 1) * span);
+    for (int64_t r = (int64_t)part * span + tid; r < hi && r < room; r += kThreads)
+      idx[off + r] = (int32_t)r;
+    if (tid == 0 && part == 0) seg_len[s] = (int32_t)keep;
     return;
   }
 
@@ -367,17 +373,24 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
   }
   __syncthreads();
   const uint32_t kept_total = block_scan_lds(blk_b, KPT * kWaves, wave_tot);
-  if (tid == 0) seg_len[s] = (int32_t)kept_total;
-  // 3) write the kept chunks' token ranges.  The 64 chunks of a wavefront
-  // (fixed k) are consecutive, so their kept tokens fill one contiguous run of
-  // the output; the wavefront walks its kept chunks (set bits of a ballot)
-  // and writes each chunk's range with all lanes, coalesced.
+  if (tid == 0 && part == 0) seg_len[s] = (int32_t)kept_total;
+  const int64_t span = ((int64_t)kept_total + parts - 1) / parts;
+  const int64_t out_lo = (int64_t)part * span;
+  const int64_t out_hi = min((int64_t)kept_total, out_lo + span);
+  // 3) write the kept chunks' token ranges that fall in this part's output
+  // positions.  The 64 chunks of a wavefront (fixed k) are consecutive, so
+  // their kept tokens fill one contiguous run of the output; the wavefront
+  // walks its kept chunks (set bits of a ballot) and writes each chunk's
+  // range with all lanes, coalesced.
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
+    const int blk = k * kWaves + wid;
+    const int64_t base = (int64_t)blk_b[blk];
+    const int64_t base_end = blk + 1 < KPT * kWaves ? (int64_t)blk_b[blk + 1] : (int64_t)kept_total;
+    if (base_end <= out_lo || base >= out_hi) continue;   // wave-uniform
     const uint32_t kw = kept_tokens(k);
     const uint32_t before = wave_incl_scan_u32(kw) - kw;
     const uint32_t st = first_tok[k];
-    const int64_t base = (int64_t)blk_b[k * kWaves + wid];
     uint64_t m = __ballot(kw > 0u);
     while (m) {
       const int c = __builtin_ctzll(m);
@@ -385,7 +398,8 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
       const uint32_t kc = (uint32_t)__builtin_amdgcn_readlane((int)kw, c);
       const int64_t pc = base + (uint32_t)__builtin_amdgcn_readlane((int)before, c);
       const uint32_t sc = (uint32_t)__builtin_amdgcn_readlane((int)st, c);
-      for (uint32_t t = lane; t < kc; t += 64)
+      const int64_t t0 = max((int64_t)0, out_lo - pc), t1 = min((int64_t)kc, out_hi - pc);
+      for (int64_t t = t0 + lane; t < t1; t += 64)
         if (pc + t < room) idx[off + pc + t] = (int32_t)(sc + t);
     }
   }
@@ -792,7 +806,10 @@ hipError_t launch_chunk(int S, int hkv, int64_t N, const float* scores, const in
                         int64_t keep_tokens, int64_t local_chunks, int64_t top_chunks,
                         const int64_t* seg_off, int32_t* seg_len, int32_t* idx, int64_t r_cap,
                         hipStream_t stream) {
-  select_chunk_kernel<KPT><<<dim3(S), dim3(kThreads), 0, stream>>>(
+  // several workgroups per segment when segments are few: each repeats the
+  // (cheap) selection and writes one slice of the kept positions
+  const int parts = (int)std::max(1, std::min(16, device_info().cus / std::max(S, 1)));
+  select_chunk_kernel<KPT><<<dim3(S, parts), dim3(kThreads), 0, stream>>>(
       scores, N, hkv, chunk_end, keep_tokens, local_chunks, top_chunks, seg_off, seg_len, idx,
       r_cap);
   return hipGetLastError();
