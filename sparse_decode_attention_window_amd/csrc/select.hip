@@ -271,15 +271,6 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
   int64_t tgt = by_count ? n_local + top_chunks
                          : (keep_tokens > local_tokens ? keep_tokens : local_tokens);
   tgt = tgt < 0 ? 0 : (tgt > total ? total : tgt);
-  if (tgt == 0 || tgt == total) {
-    const int64_t keep = tgt == 0 ? 0 : tokens;   // nothing, or every chunk: [0, tokens)
-    const int64_t span = (keep + parts - 1) / parts;
-    const int64_t hi = min(keep, (int64_t)(part + 1) * span);
-    for (int64_t r = (int64_t)part * span + tid; r < hi && r < room; r += kThreads)
-      idx[off + r] = (int32_t)r;
-    if (tid == 0 && part == 0) seg_len[s] = (int32_t)keep;
-    return;
-  }
 
   // ---- chunks into registers (all loads independent) ----------------------
   uint32_t key[KPT], wt[KPT];   // wt: the chunk's token count (0 past N)
@@ -295,6 +286,16 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
   }
   // selection weight: 1 per chunk (count mode) or its token count
   auto wsel = [&](int k) -> uint32_t { return by_count ? (wt[k] ? 1u : 0u) : wt[k]; };
+  // (checked after the chunk loads so that every load is in flight at once)
+  if (tgt == 0 || tgt == total) {
+    const int64_t keep = tgt == 0 ? 0 : tokens;   // nothing, or every chunk: [0, tokens)
+    const int64_t span = (keep + parts - 1) / parts;
+    const int64_t hi = min(keep, (int64_t)(part + 1) * span);
+    for (int64_t r = (int64_t)part * span + tid; r < hi && r < room; r += kThreads)
+      idx[off + r] = (int32_t)r;
+    if (tid == 0 && part == 0) seg_len[s] = (int32_t)keep;
+    return;
+  }
 
   // ---- radix select: 11 + 11 + 10 bits ------------------------------------
   uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)tgt;
