@@ -122,6 +122,22 @@ def test_c2_reduced_ragged(kv, layer):
                     budgets=np.full(cfg.batch * cfg.hkv, bl), layer=layer)
 
 
+def test_max_segments_per_call(kv):
+    """The largest call the boundary accepts: batch * Hkv = 2048 segments (C0's
+    shapes at batch 1024, n = 160 so every segment ends in a partial tile)
+    through score, select, compact and decode; sampled segments against the
+    oracle, every segment's length against its budget."""
+    cfg = kvsynth.get_config(0, batch=1024, n=160, budget=40)
+    S = cfg.batch * cfg.hkv
+    assert S == 2048
+    _say(cfg.name, "segments", S)
+    inputs, run = _run(kv, cfg)
+    h = _check_segments(cfg, inputs, run, [0, 1, 777, 1500, S - 2, S - 1])
+    assert np.all(h["seg_len"] == cfg.budget)
+    sc = h["scores"].reshape(S, cfg.n).astype(np.float64)
+    assert np.all(np.abs(sc.sum(1) - cfg.G * cfg.w) < 1e-3)
+
+
 def test_c2_full_layer_sampled(kv):
     cfg = kvsynth.get_config(2)
     layer = 3
