@@ -31,14 +31,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 16;
-#ifndef KVSEL_DECODE_TARGET_ITEMS
-#define KVSEL_DECODE_TARGET_ITEMS 1024
-#endif
-#ifndef KVSEL_DECODE_MAX_TPW
-#define KVSEL_DECODE_MAX_TPW 32
-#endif
-constexpr int kTargetItems = KVSEL_DECODE_TARGET_ITEMS;  // workgroups a launch aims for
-constexpr int kMaxTpw = KVSEL_DECODE_MAX_TPW;
+constexpr int kMaxTpw = 32;   // tiles per wavefront at most (very large caches)
 
 template <typename T, int D>
 struct Geom {
@@ -198,15 +191,8 @@ __device__ __forceinline__ void compute_tile(WaveState<T, D, HG>& st, const Tile
   __builtin_amdgcn_wave_barrier();
 }
 
-#ifndef KVSEL_DECODE_MIN_BLOCKS
-#define KVSEL_DECODE_MIN_BLOCKS 1
-#endif
-#ifndef KVSEL_DECODE_PREFETCH
-#define KVSEL_DECODE_PREFETCH 1
-#endif
-
 template <typename T, int D, int HG>
-__global__ __launch_bounds__(kThreads, KVSEL_DECODE_MIN_BLOCKS) void decode_split_kernel(
+__global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
     const int64_t* __restrict__ seg_off, const int32_t* __restrict__ seg_len, int64_t r_cap,
     int S, int hq, int hkv, int G, float c, int rpw, float2* __restrict__ part_ml,
@@ -277,7 +263,6 @@ __global__ __launch_bounds__(kThreads, KVSEL_DECODE_MIN_BLOCKS) void decode_spli
   if (ntiles > 0) {
     TileRegs<T, D> ra, rb;
     auto tile_lim = [&](int64_t t0) { return (int)min((int64_t)kTile - 1, wr1 - 1 - t0); };
-#if KVSEL_DECODE_PREFETCH
     // sched_barrier pins the issue order (vmcnt waits count in issue order)
     load_tile(ra, kseg + wr0 * Gm::RB, vseg + wr0 * Gm::RB, tile_lim(wr0), grp, l16);
     __builtin_amdgcn_sched_barrier(0);
@@ -293,14 +278,6 @@ __global__ __launch_bounds__(kThreads, KVSEL_DECODE_MIN_BLOCKS) void decode_spli
       __builtin_amdgcn_sched_barrier(0);
       compute_tile(st, rb, qf, c, l16 <= tile_lim(t1), sp, grp, l16);
     }
-#else
-    (void)rb;
-    for (int i = 0; i < ntiles; ++i) {
-      const int64_t t0 = wr0 + (int64_t)i * kTile;
-      load_tile(ra, kseg + t0 * Gm::RB, vseg + t0 * Gm::RB, tile_lim(t0), grp, l16);
-      compute_tile(st, ra, qf, c, l16 <= tile_lim(t0), sp, grp, l16);
-    }
-#endif
   }
 
   // fold the four key slots (lane groups) together
