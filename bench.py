@@ -102,6 +102,47 @@ def stream_ceiling(torch, kvsel, mode: int, moved: int, nb: int = 4, calls: int 
     return moved_per / ts[len(ts) // 2] / 1e9
 
 
+def serving_loop_us(torch, pipeline, kvsynth, cfg, budgets, layers: int = 4,
+                    graphs: int = 4) -> float:
+    """Decode-time loop on `layers` C2 layers (pipeline.ServingLoop): every step
+    appends the new token to the full and the compacted cache and decodes; every
+    w steps the window score over the resident full cache, the top-B selection
+    and the compaction are redone.  Each graph holds w steps of every layer (one
+    re-selection each); the first is a warm-up.  Returns µs per layer per step."""
+    W = cfg.w
+    loops = []
+    for l in range(layers):
+        run = pipeline.build_layer(cfg, kvsynth.layer_inputs(cfg, l), budget=budgets[l], slack=W)
+        run.score()
+        run.select()
+        run.compact()
+        loops.append(pipeline.ServingLoop.start(run, run.k, run.v, cfg.n, graphs * W))
+    toks = [kvsynth.step_inputs(cfg, 0, t) for t in range(W)]
+    dev = [tuple(pipeline.device_tensor(tk[name]) for name in ("k_new", "v_new", "q"))
+           for tk in toks]
+    gs = []
+    for _ in range(graphs):   # positions advance from one captured graph to the next
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for t in range(W):
+                for lp in loops:
+                    lp.step(*dev[t])
+        gs.append(g)
+    assert all(lp.reselections == graphs for lp in loops)
+    torch.cuda.synchronize()
+    gs[0].replay()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    for g in gs[1:]:
+        g.replay()
+    e[1].record()
+    torch.cuda.synchronize()
+    us = e[0].elapsed_time(e[1]) * 1e3 / ((graphs - 1) * W) / layers
+    del gs, loops
+    return us
+
+
 def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
     """HBM bytes per decode launch from two rocprofv3 --pmc runs of this
     script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by the
@@ -427,6 +468,11 @@ def main() -> int:
     log(f"[bench] C4: score {c4_us['score']:.1f} select {c4_us['select']:.1f} compact "
         f"{c4_us['compact']:.1f} decode {c4_us['decode']:.1f} us")
 
+    # serving-loop extra (f3): decode steps with periodic re-selection
+    serve_us = serving_loop_us(torch, pipeline, kvsynth, cfg, budgets)
+    log(f"[bench] serving loop: {serve_us:.1f} us per layer per step "
+        f"(re-selection every {cfg.w} steps, 4 layers)")
+
     es, d, hq, hkv, n = cfg.es, cfg.d, cfg.hq, cfg.hkv, cfg.n
     lens = pu_host(mr.seg_len).reshape(L, S)
     rows = [int(lens[l].sum()) for l in range(L)]
@@ -515,6 +561,12 @@ def main() -> int:
                                              4),
                        "note": "one C4 layer (batch 1, 131072 tokens, chunk keys of 64 dims, "
                                "chunks kept to 48 % of the tokens), outside the timed step"},
+                   "serving_loop_c2": {
+                       "us_per_layer_step": round(serve_us, 2),
+                       "note": "pipeline.ServingLoop on 4 C2 layers: every step appends the new "
+                               "token to the full and the compacted cache and decodes; every 32 "
+                               "steps score, select and compact are redone over the resident "
+                               "full cache (HIP graphs of 32 steps), outside the timed step"},
                    "layer_lmba_mean_tokens": [round(x, 1) for x in layer_lmba],
                    "attention_loss_topb_per_layer": [round(x, 5) for x in att_loss]},
         "decode_frac_of_copy_reference": round(dec_gbs / copy_gbs, 4),
