@@ -338,7 +338,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(
 // on purpose: a hand-off between workgroups of one launch needs device-scope
 // visibility of the partials across the XCDs' L2 caches, and both ways of
 // getting it (write-through atomic stores, or L2 write-back and invalidate
-// fences) measured far slower than this launch.  One single-wavefront
+// fences) measured far slower than this launch; keeping each segment's items
+// and merge inside one XCD (shared L2, arrival counters) was correct but
+// still slower, since the last item's merge sits on the critical path.  One single-wavefront
 // workgroup per (segment, query head): the head's statistics over the
 // segment's partials, then its output slice with a chunk of partial loads in
 // flight at once (lane l owns floats 2l, 2l + 1 of the head's D outputs);

@@ -1,4 +1,5 @@
-// Token selection per segment (one workgroup of 16 wavefronts per segment).
+// Token selection per segment (one workgroup of 16 wavefronts per segment;
+// CHUNK mode gives each segment several when segments are few).
 //
 // TOPB   keep the `budget` highest-score tokens (ZigZagkv page, Eq. 7 scores
 //        under the Eq. 6 layer budget).
