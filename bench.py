@@ -45,10 +45,18 @@ def log(*a):
 
 
 def src_hash(paths) -> str:
+    """Hash of the code in `paths`: comments, blank lines and trailing spaces
+    are dropped first, so that only a change to the code itself marks the
+    stored counters as stale."""
+    import re
     h = hashlib.sha256()
     for p in paths:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 
