@@ -16,9 +16,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;  // 16-byte vectors per thread in flight per tensor
 // Workgroups per CU: a grid-stride loop over fewer, longer-lived workgroups
-// amortises each one's segment-table set-up; measured best at 4 (and 4
-// vectors per thread) on a 32K-context layer: 41.7 us vs 47.1 us at 8 and 8.
-constexpr int kBlocksPerCu = 4;
+// amortises each one's segment-table set-up; measured on a 32K-context layer
+// (4 vectors per thread): 40.9 us at 3, 41.0-41.8 at 4, 42.3 at 2, 41.8-42.4
+// at 6, 47.1 at 8 (with 8 vectors).
+constexpr int kBlocksPerCu = 3;
 
 template <int CPR>  // 16-byte chunks per row
 __global__ __launch_bounds__(kThreads) void compact_kernel(
