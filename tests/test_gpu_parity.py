@@ -288,6 +288,10 @@ def test_select_chunk_exact(kv):
             want = oracle.select_chunks(cs[s].astype(np.float64), ends, keep, local, top)
             assert ln[s] == want.size, (keep, local, top, s)
             assert np.array_equal(ix[off[s]:off[s] + ln[s]], want), (keep, local, top, s)
+            # nothing written past the kept positions (the segment's workgroups each
+            # write one slice of them)
+            end = int(off[s + 1]) if s + 1 < hkv else r_cap
+            assert np.all(ix[off[s] + ln[s]:end] == -7), (keep, local, top, s)
 
 
 def test_compact_gaps_empty_and_bad_indices(kv):
