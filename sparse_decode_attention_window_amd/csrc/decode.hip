@@ -77,11 +77,15 @@ int64_t max_items(int64_t r_cap, int S) {
   return (r_cap + kWaves * kTile - 1) / (kWaves * kTile) + S;
 }
 
-// K and V rows are read exactly once per call: when rows fill whole 128-byte
-// cache lines, non-temporal loads keep them from displacing what the caches
-// hold (2 % faster at 6553 rows per segment, 6 % on 8 x 62946 rows).  Rows
-// that share lines with their neighbours (head_dim 88: 176 or 352 bytes) use
-// plain loads: streamed lines were refetched for the next row (8 % slower).
+// K and V rows are read exactly once per call.  V loads cover whole rows per
+// instruction (4 rows x 16 lanes x 16 bytes), so when rows fill whole 128-byte
+// cache lines they are non-temporal and do not displace what the caches hold.
+// K loads follow the matrix-core operand layout (16 rows x 64 bytes per
+// instruction: half of each line, the other half one instruction later), so
+// they stay plain and the line waits in the cache for its second half
+// (C2-size call 26.1 us vs 27.1 with K non-temporal too).  Rows that share
+// lines with their neighbours (head_dim 88: 176 or 352 bytes) use plain loads
+// throughout: streamed lines were refetched for the next row (8 % slower).
 template <bool STREAM>
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {
   if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -109,9 +113,9 @@ __device__ __forceinline__ void load_tile(TileRegs<T, D>& r, const char* kt, con
   for (int a = 0; a < Gm::NA; ++a) {
     const int o = 64 * a + 16 * grp;
     if (64 * (a + 1) <= Gm::RB) {
-      r.k[a] = load16_stream<Gm::RB % 128 == 0>(kt + kr + o);
+      r.k[a] = load16(kt + kr + o);
     } else {  // last, partial step (head_dim 88): lanes past the row read zeros
-      const u32x4 x = load16_stream<Gm::RB % 128 == 0>(kt + kr + min(o, Gm::RB - 16));
+      const u32x4 x = load16(kt + kr + min(o, Gm::RB - 16));
       r.k[a] = o < Gm::RB ? x : zero;
     }
   }
