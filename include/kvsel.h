@@ -43,6 +43,9 @@
  *     overlapping, chunk ends increasing) are documented, not checked; the
  *     kernels still never read or write outside the buffers described by the
  *     host-side sizes.
+ *   - Workspaces (`ws`) may hold anything on entry: each call writes what it
+ *     later reads.  A workspace serves one call at a time; calls that may
+ *     run concurrently (other streams) need workspaces of their own.
  */
 #ifndef KVSEL_H
 #define KVSEL_H
