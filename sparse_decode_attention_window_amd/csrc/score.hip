@@ -317,7 +317,11 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g4 * 4 + e], c, -kk[e]));
           if (MASKED && (int)key > lim[r0 + e]) p = 0.f;
           if (PROBS) {
-            if (r0 + e < R && key < n) scores[((int64_t)s * R + r0 + e) * n + key] = p;
+            // the rows (G*w*n floats per segment) are read once, by a later
+            // kernel: non-temporal stores keep them out of the caches
+            // (LMBA of a C2 layer 448 -> 404 us)
+            if (r0 + e < R && key < n)
+              __builtin_nontemporal_store(p, scores + ((int64_t)s * R + r0 + e) * n + key);
           } else {
             ssum += p;
           }
