@@ -7,14 +7,17 @@
 // next free slot; at the bound the slot holding the smallest position (the
 // oldest token) is found by a block-wide argmin over the segment's indices
 // and overwritten in place, so a sliding window costs one row write and one
-// read of the segment's indices per step, never a shift of the cache.
+// read of the segment's indices per step, never a shift of the cache.  The
+// argmin keeps several index loads in flight per thread: a step is a few
+// memory round trips, not one per 256 indices.
 #include "kvsel_internal.h"
 
 namespace kvsel {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kScanUnroll = 8;   // index loads in flight per thread in the argmin
 
 // (position, slot) packed so that the smaller position wins, then the lower slot
 __device__ __forceinline__ uint64_t pack(int32_t pos, int32_t slot) {
@@ -47,11 +50,22 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   if (len < bound) {
     slot = len;
   } else {
-    // oldest token: smallest position among the segment's rows
+    // oldest token: smallest position among the segment's rows, with
+    // kScanUnroll independent loads in flight per thread
     uint64_t best = ~0ull;
-    for (int64_t r = tid; r < len; r += kThreads) {
-      const uint64_t c = pack(idx[off + r], (int32_t)r);
-      best = c < best ? c : best;
+    for (int64_t r0 = tid; r0 < len; r0 += (int64_t)kThreads * kScanUnroll) {
+      int32_t p[kScanUnroll];
+#pragma unroll
+      for (int u = 0; u < kScanUnroll; ++u) {
+        const int64_t r = r0 + (int64_t)u * kThreads;
+        p[u] = r < len ? idx[off + r] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kScanUnroll; ++u) {
+        const int64_t r = r0 + (int64_t)u * kThreads;
+        const uint64_t c = r < len ? pack(p[u], (int32_t)r) : ~0ull;
+        best = c < best ? c : best;
+      }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
