@@ -164,9 +164,18 @@ __global__ __launch_bounds__(kMaskThreads) void keep_mask_kernel(
   if (off < 0 || off > r_cap) off = r_cap;
   len = len < 0 ? 0 : (len > r_cap - off ? r_cap - off : len);
   __syncthreads();
-  for (int64_t j = tid; j < len; j += kMaskThreads) {
-    const int32_t t = idx[off + j];
-    if (t >= 0 && t < n) atomicOr(&bits[t >> 5], 1u << (t & 31));
+  // eight index loads in flight per thread before their bits are set
+  constexpr int kU = 8;
+  for (int64_t j0 = tid; j0 < len; j0 += (int64_t)kMaskThreads * kU) {
+    int32_t t[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t j = j0 + (int64_t)u * kMaskThreads;
+      t[u] = j < len ? idx[off + j] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (t[u] >= 0 && t[u] < n) atomicOr(&bits[t[u] >> 5], 1u << (t[u] & 31));
   }
   __syncthreads();
   uint32_t* out = mask + (int64_t)s * words;
