@@ -82,10 +82,11 @@ int64_t max_items(int64_t r_cap, int S) {
 // cache lines they are non-temporal and do not displace what the caches hold.
 // K loads follow the matrix-core operand layout (16 rows x 64 bytes per
 // instruction: half of each line, the other half one instruction later), so
-// they stay plain and the line waits in the cache for its second half
-// (C2-size call 26.1 us vs 27.1 with K non-temporal too).  Rows that share
-// lines with their neighbours (head_dim 88: 176 or 352 bytes) use plain loads
-// throughout: streamed lines were refetched for the next row (8 % slower).
+// they stay plain and the line waits in the cache for its second half (32
+// segments of 6553 rows at d 128: 26.1 us vs 27.1 with K non-temporal too).
+// Rows that share lines with their neighbours (head_dim 88: 176 or 352
+// bytes) use plain loads throughout: streamed lines were refetched for the
+// next row (8 % slower).
 template <bool STREAM>
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {
   if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -447,7 +448,8 @@ hipError_t run(int batch, int hq, int hkv, float scale, const void* q, const voi
   // two items per CU even where three fit: an integer count per CU keeps the
   // CUs evenly loaded, and two long items beat three shorter ones (measured
   // at 6553 rows per segment: 26.8 us vs 27.7 us at three, 29.1 at one, 31.3
-  // and 30.1 at the uneven 1.5 and 2.5 per CU; C3 46.4 vs 48.7 us)
+  // and 30.1 at the uneven 1.5 and 2.5 per CU; 64 ragged segments of
+  // 32768 / 2048 / 656 rows at d 88: 46.4 vs 48.7 us)
   const int slots = device_info().cus * std::min(2, resident_blocks(decode_split_kernel<T, D, HG>));
   const int rpw = rows_per_wave(r_cap, S, slots);
   const int64_t rpi = (int64_t)kWaves * rpw;
