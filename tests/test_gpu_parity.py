@@ -394,6 +394,95 @@ def test_score_shapes(kv, dtype, d, G, w, n, q_pos0):
         pu.check_scores(s_gpu[s], ref, G * w, f"score seg {s}")
 
 
+def _drifting_logits(r, n_keys, d, n_q, slope):
+    """Keys and queries along one shared direction u, so that scale * q.k is
+    about a_j = slope * 10 * (2 j / (n_keys - 1) - 1) plus noise: the logits
+    drift by ~30 log2 units along the sequence (rising for slope > 0, falling
+    for slope < 0), so a running max changes many times (or never after the
+    first keys), and the per-tile and per-item rescaling of the online softmax
+    spans factors down to ~2^-30."""
+    u = r.standard_normal(d)
+    u /= np.linalg.norm(u)
+    a = slope * 10.0 * np.linspace(-1.0, 1.0, n_keys)
+    keys = (a[:, None] * u[None, :] + 0.3 * r.standard_normal((n_keys, d))).astype(np.float32)
+    qs = (math.sqrt(d) * u[None, :] + 0.3 * r.standard_normal((n_q, d))).astype(np.float32)
+    return keys, qs
+
+
+@pytest.mark.parametrize("dtype,d,G,w,n,slope", [("fp32", 64, 2, 8, 3000, 1.0),
+                                                 ("fp32", 128, 4, 16, 5000, -1.0),
+                                                 ("bf16", 128, 4, 32, 4100, 1.0),
+                                                 ("bf16", 88, 4, 32, 2600, -1.0)])
+def test_score_drifting_logits(kv, dtype, d, G, w, n, slope):
+    """Online-softmax statistics under logits that rise or fall by ~30 log2
+    units along the keys (window queries at the end, causal)."""
+    kvsel, pipeline, torch = kv
+    _say("score drift", dtype, d, G, w, n, slope)
+    r = np.random.default_rng(n + d + int(slope > 0))
+    B, hkv = 1, 2
+    q = np.empty((B, hkv * G, w, d), np.float32)
+    Kf = np.empty((B, hkv, n, d), np.float32)
+    for h in range(hkv):
+        keys, qs = _drifting_logits(r, n, d, G * w, slope)
+        Kf[0, h] = keys
+        q[0, h * G:(h + 1) * G] = qs.reshape(G, w, d)
+    store = (lambda x: kvsynth.f32_to_bf16_bits(x)) if dtype == "bf16" else (lambda x: x)
+    q, Kf = store(q), store(Kf)
+    shape = kvsel.make_shape(B, hkv * G, hkv, d, n, dtype, 1 / math.sqrt(d))
+    sc = torch.empty(B * hkv * n, dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvsel.kvsel_score_workspace(shape, w), dtype=torch.uint8, device="cuda")
+    kvsel.kvsel_score(shape, w, n - w, pipeline.device_tensor(q), pipeline.device_tensor(Kf), sc,
+                      ws)
+    torch.cuda.synchronize()
+    s_gpu = pu.to_host(sc).reshape(B * hkv, n)
+    for s in range(B * hkv):
+        ref = oracle.window_scores(oracle.to_f64(q[0, s * G:(s + 1) * G]), oracle.to_f64(Kf[0, s]),
+                                   1 / math.sqrt(d), n - w)
+        # the drift is real: most of the mass sits in one tenth of the keys
+        end = ref[-n // 10:] if slope > 0 else ref[:n // 10]
+        assert end.sum() > 0.8 * G * w
+        pu.check_scores(s_gpu[s], ref, G * w, f"score drift seg {s}")
+
+
+@pytest.mark.parametrize("dtype,d,G,slope", [("fp32", 128, 4, 1.0), ("fp32", 64, 2, -1.0),
+                                             ("bf16", 128, 4, -1.0), ("bf16", 88, 4, 1.0)])
+def test_decode_drifting_logits(kv, dtype, d, G, slope):
+    """Split-K decode where the logits rise or fall by ~30 log2 units along
+    each segment, so its items' partial maxima differ by up to that much and
+    the merge rescales them by factors down to ~2^-30."""
+    kvsel, pipeline, torch = kv
+    _say("decode drift", dtype, d, G, slope)
+    r = np.random.default_rng(d * 10 + G + int(slope > 0))
+    B, hkv = 1, 3
+    S = B * hkv
+    lens = np.array([20000, 7001, 333], np.int32)
+    off, r_cap = pipeline.offsets(lens.astype(np.int64))
+    Kc = np.empty((r_cap, d), np.float32)
+    q = np.empty((B, hkv * G, d), np.float32)
+    for s in range(S):
+        keys, qs = _drifting_logits(r, int(lens[s]), d, G, slope)
+        Kc[off[s]:off[s] + lens[s]] = keys
+        q[0, s * G:(s + 1) * G] = qs
+    Vc = r.standard_normal((r_cap, d)).astype(np.float32)
+    store = (lambda x: kvsynth.f32_to_bf16_bits(x)) if dtype == "bf16" else (lambda x: x)
+    Kc, Vc, q = store(Kc), store(Vc), store(q)
+    shape = kvsel.make_shape(B, hkv * G, hkv, d, int(lens.max()), dtype, 1 / math.sqrt(d))
+    out = torch.empty((B, hkv * G, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvsel.kvsel_decode_workspace(shape, r_cap), dtype=torch.uint8, device="cuda")
+    kvsel.kvsel_decode_attn(shape, pipeline.device_tensor(q), pipeline.device_tensor(Kc),
+                            pipeline.device_tensor(Vc), pipeline.device_tensor(off),
+                            pipeline.device_tensor(lens), r_cap, out, ws)
+    torch.cuda.synchronize()
+    o = pu.to_host(out)
+    for s in range(S):
+        rows = np.arange(off[s], off[s] + lens[s])
+        for g in range(G):
+            ref = oracle.decode_attention(oracle.to_f64(q[0, s * G + g]), oracle.to_f64(Kc[rows]),
+                                          oracle.to_f64(Vc[rows]), 1 / math.sqrt(d))
+            err = np.max(np.abs(o[0, s * G + g] - ref))
+            assert err <= pu.OUT_ATOL[dtype], (s, g, err)
+
+
 # ---------------------------------------------------------------------------
 # workspace state and graph replays
 # ---------------------------------------------------------------------------
