@@ -762,6 +762,41 @@ def test_lmba_and_kept_mass_match_oracle(kv, cid):
           f"mean attention loss {np.maximum(0, 0.9 - got_m).mean():.4f}", flush=True)
 
 
+@pytest.mark.parametrize("dtype,d,G,w,n,slope", [("fp32", 64, 2, 8, 3000, 1.0),
+                                                 ("bf16", 128, 4, 32, 4100, -3.0),
+                                                 ("bf16", 88, 4, 16, 2600, 3.0)])
+def test_lmba_drifting_logits(kv, dtype, d, G, w, n, slope):
+    """LMBA of rows whose weights span ~30 to ~90 log2 units (logits drifting
+    along the keys): 90 % of each row sits in about 100 to 350 keys, and at
+    slope 3 the smallest weights fall below the radix select's 2^-40 floor.
+    Per row within the float64 band of the exact answer."""
+    kvsel, pipeline, torch = kv
+    _say("lmba drift", dtype, d, G, w, n, slope)
+    r = np.random.default_rng(7 * n + d)
+    B, hkv = 1, 2
+    q = np.empty((B, hkv * G, w, d), np.float32)
+    Kf = np.empty((B, hkv, n, d), np.float32)
+    for h in range(hkv):
+        keys, qs = _drifting_logits(r, n, d, G * w, slope)
+        Kf[0, h] = keys
+        q[0, h * G:(h + 1) * G] = qs.reshape(G, w, d)
+    store = (lambda x: kvsynth.f32_to_bf16_bits(x)) if dtype == "bf16" else (lambda x: x)
+    q, Kf = store(q), store(Kf)
+    shape = kvsel.make_shape(B, hkv * G, hkv, d, n, dtype, 1 / math.sqrt(d))
+    R = G * w
+    lm = torch.empty(B * hkv * R, dtype=torch.int32, device="cuda")
+    ws = torch.empty(kvsel.kvsel_lmba_workspace(shape, w), dtype=torch.uint8, device="cuda")
+    kvsel.kvsel_lmba(shape, w, n - w, pipeline.device_tensor(q), pipeline.device_tensor(Kf), lm,
+                     ws)
+    torch.cuda.synchronize()
+    got = pu.to_host(lm).reshape(B * hkv, R)
+    for s in range(B * hkv):
+        P = oracle.window_probabilities(oracle.to_f64(q[0, s * G:(s + 1) * G]),
+                                        oracle.to_f64(Kf[0, s]), 1 / math.sqrt(d), n - w)
+        assert np.median(got[s]) < n // 8   # concentrated rows, not near-uniform ones
+        pu.check_lmba(got[s], P, f"lmba drift seg {s}")
+
+
 # ---------------------------------------------------------------------------
 # fused pair-pruned RoPE (RAP §3, Eq. 5-10): rows arrive unrotated and are
 # rotated inside the kernels; the rotation is fixed fp32 arithmetic, so the
