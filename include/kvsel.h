@@ -215,23 +215,31 @@ kvsel_status kvsel_select(const kvsel_shape* s /*host*/, const kvsel_select_para
  * ChunkLLM page, §2.3: the chunks stored in the cache are chosen by a vote
  * across layers (the page gives the rule only in words; reading taken):
  * each of `layers` layers votes for its own top_k chunks (its chunk scores in
- * TOPB order: score descending, lower index first); per (b, kvh) and chunk c
- *   key[b][kvh][c] = votes_c + 0.5 * (sum_l scores[l][b][kvh][c] / (layers * G))
- * computed in fp32 with the layers summed in order 0 .. layers-1 and a
- * correctly rounded divide.  A chunk's attention summed over its G query
- * heads is at most G, so kvsel_select CHUNK with top_chunks = top_k (and
- * local_chunks) over key keeps the chunks with the most votes, ties to the
- * larger summed attention, then to the lower index.
- *   s        shape of the chunk scores: n = chunks per sequence, G = hq/hkv
- *   scores   [layers][batch][hkv][n] fp32 (kvsel_score of each layer)
- *   key      [batch][hkv][n] fp32 (out)
- *   ws       at least kvsel_chunk_vote_workspace(s, layers, top_k) bytes
+ * TOPB order: score descending, lower index first); the kept set of each
+ * (b, kvh) is its last local_chunks chunks plus the top_k other chunks with
+ * the most votes, ties to the larger attention summed over the layers, then
+ * to the lower index.  The call writes one key per chunk such that
+ * kvsel_select CHUNK with local_chunks and top_chunks = top_k over `key`
+ * keeps exactly that set.  With V the vote count of the top_k-th best
+ * non-local chunk (0 when there are at most top_k of them):
+ *   key[b][kvh][c] = +inf  for a non-local chunk with more than V votes,
+ *                    -inf  for a non-local chunk with fewer than V votes,
+ *                    sum_l scores[l][b][kvh][c] otherwise (fp32, layers added
+ *                          in order 0 .. layers-1; local chunks get it too).
+ * The summed attention is never rounded into the vote count, so chunks whose
+ * sums differ in any fp32 bit are ordered by them.
+ *   s            shape of the chunk scores: n = chunks per sequence
+ *   local_chunks trailing chunks that the later select forces in, >= 0
+ *   scores       [layers][batch][hkv][n] fp32 (kvsel_score of each layer)
+ *   key          [batch][hkv][n] fp32 (out)
+ *   ws           at least kvsel_chunk_vote_workspace(s, layers, top_k) bytes
  * Constraints: 1 <= layers <= 255, top_k >= 1 (top_k > n votes for every
- * chunk), n bytes of vote counters must fit in one workgroup's LDS. */
+ * chunk), n bytes of vote counters plus 2 KB must fit in one workgroup's LDS
+ * (else KVSEL_EUNSUPPORTED). */
 size_t kvsel_chunk_vote_workspace(const kvsel_shape* s /*host*/, int32_t layers, int32_t top_k);
 kvsel_status kvsel_chunk_vote(const kvsel_shape* s /*host*/, int32_t layers, int32_t top_k,
-                              const float* scores, float* key, void* ws, size_t ws_bytes,
-                              hipStream_t stream);
+                              int64_t local_chunks, const float* scores, float* key, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 /* -------------------------------------------------------------- compact --
  * Packed variable-length cache: for every segment s and r < seg_len[s],

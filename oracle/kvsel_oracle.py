@@ -38,6 +38,7 @@ correct value.  bf16 inputs arrive as uint16 words and are widened exactly.
 """
 from __future__ import annotations
 
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -47,7 +48,7 @@ __all__ = [
     "zigzag_budgets", "score_order", "select_topb", "select_chunks",
     "select_policy", "compact", "decode_attention", "decode_partial",
     "combine_partials", "append_token", "window_probabilities", "attention_loss",
-    "round_bf16", "rope_pairs", "vote_key",
+    "round_bf16", "rope_pairs", "chunk_votes", "vote_chunks",
     "HEAD_GLOBAL", "HEAD_LOCAL", "HEAD_SPECIAL",
 ]
 
@@ -289,30 +290,38 @@ def select_chunks(chunk_scores: np.ndarray, chunk_end: np.ndarray, keep_tokens: 
     return np.concatenate([np.arange(starts[c], ends[c]) for c in chosen]).astype(np.int64)
 
 
-def vote_key(layer_scores, top_k: int, group: int) -> np.ndarray:
-    """Layer-wise chunk voting [CK §2.3, where the rule is given only in words;
-    the reading taken]: each of the L layers votes for its own top_k chunks
-    (select_topb on that layer's chunk scores); the shared set is then the
-    chunks with the most votes, ties to the larger chunk attention summed over
-    the layers, then to the lower index.  Expressed as one key per chunk,
-
-        key = votes + 0.5 * (sum_l s_l / (L * group))      (every step fp32,
-                                                           layers summed in order)
-
-    where each s_l <= group (a chunk's attention summed over the group's query
-    heads), so the fraction stays below the next vote count.  Keeping the
-    local chunks plus the top_k best keys is select_chunks(key, ends, 0, local,
-    top_k).  layer_scores [L][nc] are taken as fp32; returns float32 keys."""
-    S = np.asarray(layer_scores, np.float32)
+def chunk_votes(layer_scores, top_k: int):
+    """Ballots of the layer-wise chunk vote [CK §2.3, where the rule is given
+    only in words; the reading taken]: layer l votes for its own top_k chunks,
+    select_topb on its chunk scores.  layer_scores [L][nc].  Returns
+    (votes [nc] int64: how many layers voted for each chunk,
+     total [nc] float64: each chunk's attention summed over the layers)."""
+    S = np.asarray(layer_scores, np.float64)
     L, nc = S.shape
     votes = np.zeros(nc, np.int64)
     for layer in range(L):
-        votes[select_topb(S[layer].astype(np.float64), top_k)] += 1
-    acc = np.zeros(nc, np.float32)
-    for layer in range(L):
-        acc = (acc + S[layer]).astype(np.float32)
-    frac = (acc / np.float32(L * group)).astype(np.float32)
-    return (votes.astype(np.float32) + np.float32(0.5) * frac).astype(np.float32)
+        votes[select_topb(S[layer], top_k)] += 1
+    total = np.array([math.fsum(S[:, c]) for c in range(nc)], np.float64)
+    return votes, total
+
+
+def vote_chunks(layer_scores, top_k: int, chunk_end, local_chunks: int = 0) -> np.ndarray:
+    """The chunks one (batch element, KV head) keeps for all layers under the
+    layer-wise vote [CK §2.3; reading taken]: the last local_chunks chunks,
+    plus the top_k other chunks ordered by most votes, then larger attention
+    summed over the layers, then lower index.  Chunk c covers
+    [chunk_end[c-1], chunk_end[c]).  Returns the kept token positions in
+    ascending order (int64), as select_chunks does."""
+    votes, total = chunk_votes(layer_scores, top_k)
+    ends = np.asarray(chunk_end, np.int64)
+    starts = np.concatenate([[0], ends[:-1]])
+    nc = ends.size
+    n_local = max(0, min(int(local_chunks), nc))
+    others = sorted(range(nc - n_local), key=lambda c: (-int(votes[c]), -float(total[c]), c))
+    chosen = sorted(list(range(nc - n_local, nc)) + others[:int(top_k)])
+    if not chosen:
+        return np.zeros(0, np.int64)
+    return np.concatenate([np.arange(starts[c], ends[c]) for c in chosen]).astype(np.int64)
 
 
 def select_policy(kind: int, n: int, local_window: int, special_pos) -> np.ndarray:

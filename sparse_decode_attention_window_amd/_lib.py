@@ -58,8 +58,8 @@ _SIGS = {
     "kvsel_chunk_vote_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32,
                                                      ctypes.c_int32]),
     "kvsel_chunk_vote": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32,
-                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                        ctypes.c_size_t, ctypes.c_void_p]),
+                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "kvsel_select": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(SelectParams),
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
@@ -168,10 +168,11 @@ def kvsel_chunk_vote_workspace(shape: Shape, layers: int, top_k: int) -> int:
     return lib().kvsel_chunk_vote_workspace(ctypes.byref(shape), int(layers), int(top_k))
 
 
-def kvsel_chunk_vote(shape: Shape, layers: int, top_k: int, scores, key, ws, stream=None) -> None:
+def kvsel_chunk_vote(shape: Shape, layers: int, top_k: int, local_chunks: int, scores, key, ws,
+                     stream=None) -> None:
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check(lib().kvsel_chunk_vote(ctypes.byref(shape), int(layers), int(top_k), _ptr(scores),
-                                  _ptr(key), _ptr(ws), nbytes, _stream(stream)),
+    _check(lib().kvsel_chunk_vote(ctypes.byref(shape), int(layers), int(top_k), int(local_chunks),
+                                  _ptr(scores), _ptr(key), _ptr(ws), nbytes, _stream(stream)),
            "kvsel_chunk_vote")
 
 

@@ -310,21 +310,23 @@ size_t kvsel_chunk_vote_workspace(const kvsel_shape* s, int32_t layers, int32_t 
 }
 
 kvsel_status kvsel_chunk_vote(const kvsel_shape* s, int32_t layers, int32_t top_k,
-                              const float* scores, float* key, void* ws, size_t ws_bytes,
-                              hipStream_t stream) {
+                              int64_t local_chunks, const float* scores, float* key, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   int S = 0, G = 0;
   kvsel_status st = check_shape(s, &S, &G, 256);
   if (st != KVSEL_OK) return st;
   if (layers < 1 || layers > 255) return fail(KVSEL_EINVAL, "layers must be in [1, 255]");
   if (top_k < 1) return fail(KVSEL_EINVAL, "top_k must be >= 1");
+  if (local_chunks < 0) return fail(KVSEL_EINVAL, "local_chunks must be >= 0");
   if (!scores || !key) return fail(KVSEL_EINVAL, "scores and key must be non-NULL");
-  if ((size_t)((s->n + 3) / 4) * 4 + 1024 > (size_t)device_info().max_lds)
+  // vote counters (one byte per chunk) plus the kernel's static vote-count histogram
+  if ((size_t)((s->n + 3) / 4) * 4 + 2048 > (size_t)device_info().max_lds)
     return fail(KVSEL_EUNSUPPORTED, "%lld vote counters do not fit in LDS", (long long)s->n);
   const size_t need = kvsel_chunk_vote_workspace(s, layers, top_k);
   if (!ws || ws_bytes < need)
     return fail(KVSEL_ENOSPC, "chunk vote workspace needs %zu bytes, got %zu", need, ws_bytes);
-  return hip_status(launch_vote(S, s->hkv, G, layers, s->n, top_k, scores, key, ws, stream),
+  return hip_status(launch_vote(S, s->hkv, layers, s->n, top_k, local_chunks, scores, key, ws, stream),
                     "kvsel_chunk_vote launch");
 }
 

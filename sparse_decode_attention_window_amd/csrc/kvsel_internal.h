@@ -303,7 +303,7 @@ hipError_t launch_select_rank(int S, int hkv, int64_t n_items, const float* scor
 // Layer-wise chunk voting: scratch bytes and the launches (per-layer TOPB
 // selects, then the vote keys).
 size_t vote_workspace_bytes(int S, int layers, int64_t n, int32_t k);
-hipError_t launch_vote(int S, int hkv, int G, int layers, int64_t n, int32_t k,
+hipError_t launch_vote(int S, int hkv, int layers, int64_t n, int32_t k, int64_t local,
                        const float* scores, float* key, void* ws, hipStream_t stream);
 
 hipError_t launch_select_policy(int S, int hkv, int64_t n, const int8_t* head_kind,

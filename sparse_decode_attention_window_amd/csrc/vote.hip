@@ -1,14 +1,18 @@
 // ChunkLLM layer-wise chunk voting (ChunkLLM page, §2.3: the chunks kept in
 // the cache are chosen by a vote across layers; the rule is given only in
-// words).  Each layer votes for its own top-k chunks; a chunk's key is
-//   votes + 0.5 * (sum over layers of its chunk attention / (layers * G)),
-// every step in fp32 with the layers summed in order, so a CHUNK selection of
-// the k best keys (plus the local chunks) keeps the chunks with the most
-// votes, ties to the larger summed attention, then to the lower index.
+// words).  Each layer votes for its own top-k chunks; the kept set is the
+// local chunks plus the k other chunks with the most votes, ties to the
+// larger attention summed over the layers, then to the lower index.
 //
 // The per-layer top-k runs through the TOPB select over the [layers * S]
-// score rows (one segment per (layer, b, kvh)); then vote_key_kernel, one
-// workgroup per (b, kvh), counts the votes in LDS and writes the keys.
+// score rows (one segment per (layer, b, kvh)).  vote_key_kernel, one
+// workgroup per (b, kvh), counts the votes in LDS, finds the vote count V of
+// the k-th best non-local chunk, and writes a key that the CHUNK select
+// (top_chunks = k) orders exactly as the rule does: +inf for chunks with more
+// than V votes (fewer than k of them, all kept), the fp32 summed attention
+// (layers added in order) for chunks with exactly V votes (they compete for
+// the slots left), -inf for fewer than V votes.  No vote count and no
+// attention sum is rounded into another.
 #include "kvsel_internal.h"
 
 namespace kvsel {
@@ -28,14 +32,17 @@ __global__ __launch_bounds__(kThreads) void vote_setup_kernel(int n_seg, int32_t
 }
 
 // votes[c] lives in byte c of the LDS words (layers <= 255, so a byte never
-// carries into its neighbour).
+// carries into its neighbour).  Chunks c >= nl are local chunks.
 __global__ __launch_bounds__(kThreads) void vote_key_kernel(
-    const float* __restrict__ scores, int64_t n, int S, int layers, int32_t k, float lg,
+    const float* __restrict__ scores, int64_t n, int64_t nl, int S, int layers, int32_t k,
     const int32_t* __restrict__ ballots, float* __restrict__ key) {
   extern __shared__ uint32_t votes[];   // (n + 3) / 4 words
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t thresh;
   const int s = blockIdx.x, tid = threadIdx.x;
   const int64_t words = (n + 3) / 4;
   for (int64_t i = tid; i < words; i += kThreads) votes[i] = 0u;
+  hist[tid] = 0u;
   __syncthreads();
   for (int l = 0; l < layers; ++l) {
     const int32_t* b = ballots + ((int64_t)l * S + s) * k;
@@ -45,11 +52,30 @@ __global__ __launch_bounds__(kThreads) void vote_key_kernel(
     }
   }
   __syncthreads();
+  for (int64_t c = tid; c < nl; c += kThreads)
+    atomicAdd(&hist[(votes[c >> 2] >> (8 * (c & 3))) & 0xffu], 1u);
+  __syncthreads();
+  if (tid == 0) {
+    // V = the largest count such that at least min(k, nl) non-local chunks
+    // have V votes or more (0 when every non-local chunk is kept)
+    const int64_t want = k < nl ? k : nl;
+    int64_t seen = 0;
+    int v = layers;
+    for (; v > 0; --v) {
+      seen += hist[v];
+      if (seen >= want) break;
+    }
+    thresh = (uint32_t)v;
+  }
+  __syncthreads();
+  const uint32_t V = thresh;
   for (int64_t c = tid; c < n; c += kThreads) {
     float acc = 0.f;
     for (int l = 0; l < layers; ++l) acc += scores[((int64_t)l * S + s) * n + c];
     const uint32_t v = (votes[c >> 2] >> (8 * (c & 3))) & 0xffu;
-    key[(int64_t)s * n + c] = (float)v + 0.5f * (acc / lg);   // correctly rounded divide
+    float out = acc;
+    if (c < nl && v != V) out = v > V ? INFINITY : -INFINITY;
+    key[(int64_t)s * n + c] = out;
   }
 }
 
@@ -64,7 +90,7 @@ size_t vote_workspace_bytes(int S, int layers, int64_t n, int32_t k) {
   return head + segs * (size_t)kk * sizeof(int32_t);
 }
 
-hipError_t launch_vote(int S, int hkv, int G, int layers, int64_t n, int32_t k,
+hipError_t launch_vote(int S, int hkv, int layers, int64_t n, int32_t k, int64_t local,
                        const float* scores, float* key, void* ws, hipStream_t stream) {
   const int32_t kk = (int32_t)(k < n ? k : n);
   const int segs = layers * S;
@@ -91,8 +117,9 @@ hipError_t launch_vote(int S, int hkv, int G, int layers, int64_t n, int32_t k,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  vote_key_kernel<<<dim3(S), dim3(kThreads), lds, stream>>>(
-      scores, n, S, layers, kk, (float)layers * (float)G, ballots, key);
+  const int64_t nl = local < n ? n - local : 0;
+  vote_key_kernel<<<dim3(S), dim3(kThreads), lds, stream>>>(scores, n, nl, S, layers, kk,
+                                                             ballots, key);
   return hipGetLastError();
 }
 

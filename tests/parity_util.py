@@ -75,6 +75,31 @@ def check_chunk_selection(idx_gpu, cs_gpu, cs_ref, ends, keep, what, local=0, to
         assert abs(cs_ref[c] - cs_ref[last]) <= band, f"{what}: chunk {c} differs outside band"
 
 
+def check_voted_selection(idx_gpu, layer_scores, ends, local, top, what):
+    """ChunkLLM layer-wise vote: the kept tokens against the plain rule
+    (oracle.vote_chunks) on the same fp32 layer scores.  The ballots are then
+    identical; the GPU sums the layers in fp32, so a chunk may differ from
+    the oracle's choice only when it has the boundary's vote count and its
+    float64 summed attention lies within the tie band of the boundary's."""
+    sc = np.asarray(layer_scores, np.float64)
+    want = oracle.vote_chunks(sc, top, ends, local)
+    if np.array_equal(idx_gpu, want):
+        return 0
+    chunk_of = lambda toks: set(np.searchsorted(ends, toks, side="right").tolist())
+    nc = len(ends)
+    forced = set(range(nc - min(local, nc), nc))
+    votes, total = oracle.chunk_votes(sc, top)
+    cg, cr = chunk_of(idx_gpu) - forced, chunk_of(want) - forced
+    assert len(cg) == len(cr), f"{what}: kept {len(cg)} voted chunks, want {len(cr)}"
+    last = min(cr, key=lambda c: (votes[c], total[c], -c))
+    band = TIE_BAND * abs(total[last])
+    for c in cg ^ cr:
+        assert votes[c] == votes[last] and abs(total[c] - total[last]) <= band, (
+            f"{what}: chunk {c} (votes {votes[c]}, sum {total[c]!r}) differs from the rule "
+            f"outside the tie band (boundary votes {votes[last]}, sum {total[last]!r})")
+    return len(cg ^ cr)
+
+
 def check_compact(kc_gpu, vc_gpu, K, V, idx, what):
     kr, vr = oracle.compact(K, V, idx)
     assert np.array_equal(kc_gpu, kr) and np.array_equal(vc_gpu, vr), f"{what}: compaction not exact"

@@ -160,16 +160,18 @@ def test_chunk_vote_rejects_bad_args():
     need = kvsel.kvsel_chunk_vote_workspace(sh, 4, 16)
     assert need >= 4 * 2 * 16 * 4                  # the layers' ballots
 
-    def vote(layers=4, k=16, sc=FAKE, key=FAKE, ws_bytes=1 << 30):
-        return lib.kvsel_chunk_vote(ctypes.byref(sh), layers, k, sc, key, FAKE, ws_bytes, None)
+    def vote(layers=4, k=16, sc=FAKE, key=FAKE, ws_bytes=1 << 30, local=0):
+        return lib.kvsel_chunk_vote(ctypes.byref(sh), layers, k, local, sc, key, FAKE, ws_bytes,
+                                    None)
     assert vote(layers=0) == _lib.KVSEL_EINVAL
     assert vote(layers=256) == _lib.KVSEL_EINVAL
     assert vote(k=0) == _lib.KVSEL_EINVAL
+    assert vote(local=-1) == _lib.KVSEL_EINVAL
     assert vote(sc=None) == _lib.KVSEL_EINVAL
     assert vote(key=None) == _lib.KVSEL_EINVAL
     assert vote(ws_bytes=need - 1) == _lib.KVSEL_ENOSPC
     big = shape(n=1 << 20)
-    assert lib.kvsel_chunk_vote(ctypes.byref(big), 4, 16, FAKE, FAKE, FAKE, 1 << 40,
+    assert lib.kvsel_chunk_vote(ctypes.byref(big), 4, 16, 0, FAKE, FAKE, FAKE, 1 << 40,
                                 None) == _lib.KVSEL_EUNSUPPORTED
 
 

@@ -1104,10 +1104,12 @@ def test_chunk_serving_loop_reselects_at_boundaries(kv):
 @pytest.mark.parametrize("n,layers,top,local", [(3000, 4, 16, 4), (20000, 6, 64, 8)])
 def test_chunk_vote_matches_oracle(kv, n, layers, top, local):
     """Chunk scores of several layers over shared chunk boundaries (the chunk
-    adapter sits at the bottom layer), voted into one key per chunk: the key
-    equals the oracle's on the GPU's own fp32 scores bit for bit, each layer's
-    ballot differs from the float64 one only inside the tie band, and the
-    CHUNK selection over the key keeps exactly the oracle's chunks."""
+    adapter sits at the bottom layer), voted into one key per chunk: each
+    layer's ballot differs from the float64 one only inside the tie band, and
+    the CHUNK selection over the key keeps the chunks of the plain rule (most
+    votes, then larger summed attention, then lower index) up to the tie band
+    on the summed attention -- on the GPU's own fp32 scores, and end to end
+    on the float64 scores whenever the layers' ballots agree."""
     from kvsynth import gen
     kvsel, pipeline, torch = kv
     cfg = kvsynth.get_config(4, n=n)
@@ -1137,7 +1139,7 @@ def test_chunk_vote_matches_oracle(kv, n, layers, top, local):
     key = torch.empty(S * nc, dtype=torch.float32, device="cuda")
     vws = torch.empty(kvsel.kvsel_chunk_vote_workspace(sshape, layers, top), dtype=torch.uint8,
                       device="cuda")
-    kvsel.kvsel_chunk_vote(sshape, layers, top, allsc, key, vws)
+    kvsel.kvsel_chunk_vote(sshape, layers, top, local, allsc, key, vws)
     # the shared selection: local chunks + the top best keys, over the voted key
     shape = kvsel.make_shape(B, hq, hkv, cfg.d, n, cfg.dtype, cfg.scale)
     et = pipeline.device_tensor(np.stack(ends).astype(np.int64))
@@ -1151,19 +1153,71 @@ def test_chunk_vote_matches_oracle(kv, n, layers, top, local):
     kvsel.kvsel_select(shape, prm, key, pipeline.device_tensor(off), ln, idx, r_cap)
     torch.cuda.synchronize()
     sc = pu.to_host(allsc).reshape(layers, S, nc)
-    kg = pu.to_host(key).reshape(S, nc)
     lens, ig = pu.to_host(ln), pu.to_host(idx)
+    in_band = e2e = 0
     for s in range(S):
         b = s // hkv
+        agree = True
         for l in range(layers):
             pu.check_scores(sc[l, s], ref[l, s], G, f"layer {l} seg {s}")
-            pu.check_topb_selection(oracle.select_topb(sc[l, s].astype(np.float64), top),
-                                    sc[l, s], ref[l, s], top, f"ballot layer {l} seg {s}")
-        want_key = oracle.vote_key(sc[:, s], top, G)
-        assert np.array_equal(kg[s].view(np.uint32), want_key.view(np.uint32)), f"seg {s} key"
-        want = oracle.select_chunks(want_key.astype(np.float64), ends[b], 0, local, top)
+            ballot = oracle.select_topb(sc[l, s].astype(np.float64), top)
+            pu.check_topb_selection(ballot, sc[l, s], ref[l, s], top, f"ballot layer {l} seg {s}")
+            agree &= np.array_equal(ballot, oracle.select_topb(ref[l, s], top))
         got = ig[off[s]:off[s] + lens[s]]
-        assert np.array_equal(got, want), f"seg {s}: voted selection"
+        in_band += pu.check_voted_selection(got, sc[:, s], ends[b], local, top, f"seg {s}")
+        if agree:
+            e2e += 1
+            pu.check_voted_selection(got, ref[:, s], ends[b], local, top, f"seg {s} (float64)")
+    print(f"  {cfg.name}: voted selections checked on {S} segments ({e2e} also end to end), "
+          f"{in_band} chunks differ inside the tie band", flush=True)
+
+
+def test_chunk_vote_near_ties(kv):
+    """Layer-wise vote on C4-shaped chunk scores (6 layers, 4096 chunks, 4
+    query heads per KV head, top 64, 8 local chunks) drawn flat enough that
+    many chunks share the boundary vote count with summed attentions close
+    together (about 1e-3 per layer): the kept chunks follow the plain rule on
+    the same fp32 scores, up to the tie band on summed attention.  Scores are
+    uploaded directly, 96 independent segments in one call."""
+    kvsel, pipeline, torch = kv
+    L, nc, G, top, local, B, hkv = 6, 4096, 4, 64, 8, 12, 8
+    S = B * hkv
+    _say("chunk vote near ties, segments", S)
+    r = np.random.default_rng(20261203)
+    sc = np.empty((L, S, nc), np.float32)
+    for s in range(S):
+        a, b = [(0.3, 0.3), (0.1, 0.5), (1.0, 0.1), (0.5, 0.2)][s % 4]
+        z = r.standard_normal(nc)
+        for l in range(L):
+            lg = a * z + b * r.standard_normal(nc)
+            p = np.exp(lg - lg.max())
+            sc[l, s] = (G * p / p.sum()).astype(np.float32)
+    ends = np.arange(1, nc + 1, dtype=np.int64) * 32
+    n = int(ends[-1])
+    sshape = kvsel.make_shape(B, hkv * G, hkv, 64, nc, kvsel.KVSEL_BF16, 0.125)
+    allsc = pipeline.device_tensor(sc.reshape(-1))
+    key = torch.empty(S * nc, dtype=torch.float32, device="cuda")
+    vws = torch.empty(kvsel.kvsel_chunk_vote_workspace(sshape, L, top), dtype=torch.uint8,
+                      device="cuda")
+    kvsel.kvsel_chunk_vote(sshape, L, top, local, allsc, key, vws)
+    shape = kvsel.make_shape(B, hkv * G, hkv, 128, n, kvsel.KVSEL_BF16, 0.125)
+    et = pipeline.device_tensor(np.tile(ends, (B, 1)))
+    cap = pipeline.capacities(kvsel.KVSEL_SEL_CHUNK, B, hkv, n, max_chunk=32,
+                              local_chunks=local, top_chunks=top)
+    off, r_cap = pipeline.offsets(cap)
+    ln = torch.empty(S, dtype=torch.int32, device="cuda")
+    idx = torch.empty(max(r_cap, 1), dtype=torch.int32, device="cuda")
+    prm = kvsel.select_params(kvsel.KVSEL_SEL_CHUNK, n_chunks=nc, chunk_end=et,
+                              local_chunks=local, top_chunks=top)
+    kvsel.kvsel_select(shape, prm, key, pipeline.device_tensor(off), ln, idx, r_cap)
+    torch.cuda.synchronize()
+    lens, ig = pu.to_host(ln), pu.to_host(idx)
+    in_band = 0
+    for s in range(S):
+        got = ig[off[s]:off[s] + lens[s]]
+        assert lens[s] == (top + local) * 32, f"seg {s}: kept {lens[s]} tokens"
+        in_band += pu.check_voted_selection(got, sc[:, s], ends, local, top, f"seg {s}")
+    print(f"  near ties: {S} segments, {in_band} chunks differ inside the tie band", flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -1311,7 +1365,7 @@ def test_graph_replays_lmba_vote_rope(kv):
     def work():
         kvsel.kvsel_lmba(run.shape, cfg.w, cfg.n - cfg.w, run.q_win, run.k, lm, lws,
                          run.seg_off, run.seg_len, run.idx, run.r_cap, km)
-        kvsel.kvsel_chunk_vote(vsh, 3, 40, lay, key, vws)
+        kvsel.kvsel_chunk_vote(vsh, 3, 40, 0, lay, key, vws)
         kvsel.kvsel_score(fused, cfg.w, cfg.n - cfg.w, run.q_win, run.k, rsc, rws)
         kvsel.kvsel_decode_attn(fused, run.q_dec, run.k_c, run.v_c, run.seg_off, run.seg_len,
                                 run.r_cap, rout, run.ws_dec)

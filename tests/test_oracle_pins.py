@@ -605,8 +605,7 @@ def test_rope_preserves_pair_norms_and_relative_position():
 # ---------------------------------------------------------------------------
 
 def _voted_chunks(layer_scores, k, local, ends):
-    key = oracle.vote_key(layer_scores, k, group=1)
-    toks = oracle.select_chunks(key, ends, 0, local, k)
+    toks = oracle.vote_chunks(layer_scores, k, ends, local)
     return sorted(set(np.searchsorted(ends, toks, side="right").tolist()))
 
 
@@ -618,9 +617,14 @@ def test_vote_hand_worked():
          [0.3, 0.1, 0.8, 0.7, 0.0, 0.1],
          [0.6, 0.2, 0.1, 0.65, 0.05, 0.0]]
     ends = np.arange(1, 7)
+    votes, total = oracle.chunk_votes(s, 2)
+    assert votes.tolist() == [1, 1, 1, 3, 0, 0]
+    assert np.allclose(total, [1.0, 0.8, 1.1, 2.25, 0.05, 0.1], rtol=0, atol=1e-15)
     assert _voted_chunks(s, 2, 0, ends) == [2, 3]
     assert _voted_chunks(s, 2, 1, ends) == [2, 3, 5]          # chunk 5 forced (local)
     assert _voted_chunks(s, 1, 0, ends) == [3]
+    # chunk 3 forced as a local chunk: the two best others are then 2 and 0
+    assert _voted_chunks(s, 2, 3, ends) == [0, 2, 3, 4, 5]
 
 
 def test_vote_counts_beat_summed_attention():
@@ -635,33 +639,93 @@ def test_vote_counts_beat_summed_attention():
     assert _voted_chunks(s, 2, 0, ends) == [0, 1]
 
 
+def _near_tie_layers(b_sum_rel):
+    # Six layers, top-2 per layer, five chunks.  Chunk 0 is every layer's best
+    # (six votes).  Layers 0-2 also vote chunk 1 and layers 3-5 chunk 2, so
+    # both have three votes and compete for the one slot left; chunk 2's
+    # summed attention is (1 + b_sum_rel) times chunk 1's (0.0045).  Chunks 3
+    # and 4 get no votes.
+    s = np.full((6, 5), 0.0002)
+    s[:, 0] = 0.01
+    s[:3, 1], s[3:, 1] = 0.001, 0.0005
+    s[:3, 2], s[3:, 2] = 0.0005, 0.001 + 0.0045 * b_sum_rel / 3
+    return s
+
+
+def test_vote_near_tie_in_summed_attention_goes_to_the_larger():
+    # Relative differences of 1e-4 and 2e-5 are outside the 1e-5 tie band, so
+    # the larger sum (chunk 2, the higher index) must win; at 2e-6 the rule
+    # still orders them exactly.  (One fp32 key votes + 0.5 * sum / (L * G),
+    # G = 4, rounds chunks 1 and 2 to the same value at these magnitudes and
+    # would keep chunk 1.)
+    ends = np.arange(1, 6)
+    for rel in (1e-4, 2e-5, 2e-6):
+        s = _near_tie_layers(rel)
+        votes, total = oracle.chunk_votes(s, 2)
+        assert votes.tolist() == [6, 3, 3, 0, 0]
+        assert total[2] > total[1]
+        assert _voted_chunks(s, 2, 0, ends) == [0, 2]
+        # the mirror image: the larger sum on the lower index
+        m = s.copy()
+        m[:, [1, 2]] = s[:, [2, 1]]
+        assert _voted_chunks(m, 2, 0, ends) == [0, 1]
+    # exact ties in votes and in summed attention go to the lower index
+    s = _near_tie_layers(0.0)
+    s[:3, 2], s[3:, 2] = 0.0005, 0.001
+    assert _voted_chunks(s, 2, 0, ends) == [0, 1]
+
+
 def test_vote_single_layer_is_its_own_top_k():
     r = np.random.default_rng(12)
     ends = np.cumsum(r.integers(1, 9, 200))
     for k, local in [(10, 0), (17, 3), (1, 5)]:
         sc = r.random(200).astype(np.float32)
+        # one layer: the ballot is the layer's top k over all chunks, and the
+        # kept set is the locals plus the k best other chunks by score
         want = oracle.select_chunks(sc.astype(np.float64), ends, 0, local, k)
-        got = oracle.select_chunks(oracle.vote_key(sc[None], k, 1), ends, 0, local, k)
+        votes, _ = oracle.chunk_votes(sc[None], k)
+        if local == 0:
+            assert np.array_equal(np.flatnonzero(votes), np.sort(oracle.select_topb(sc, k)))
+        got = oracle.vote_chunks(sc[None], k, ends, local)
         assert np.array_equal(got, want)
         # identical layers vote as one
-        got3 = oracle.select_chunks(oracle.vote_key(np.stack([sc] * 3), k, 1), ends, 0, local, k)
+        got3 = oracle.vote_chunks(np.stack([sc] * 3), k, ends, local)
         assert np.array_equal(got3, want)
 
 
-def test_vote_key_orders_by_votes_then_attention():
+def test_vote_against_rank_counting():
+    """The vote written a second way, by counting ranks instead of sorting: a
+    chunk is on layer l's ballot iff fewer than k chunks beat it there (higher
+    score, or equal score and lower index), and a non-local chunk is kept iff
+    fewer than k other non-local chunks beat it on (votes, summed attention,
+    lower index).  Random layers with planted exact ties in scores and in
+    summed attention."""
     r = np.random.default_rng(13)
-    L, nc, k, G = 5, 300, 20, 4
-    sc = (r.random((L, nc)) * G / nc * 3).astype(np.float32)
-    key = oracle.vote_key(sc, k, G)
-    votes = np.floor(key)
-    assert votes.max() <= L and votes.sum() == L * k
-    frac = key - votes
-    assert np.all(frac >= 0) and np.all(frac <= 0.5)
-    tot = sc.astype(np.float64).sum(0)
-    for v in np.unique(votes):
-        m = votes == v
-        o = np.argsort(-key[m], kind="stable")
-        assert np.all(np.diff(tot[m][o]) <= 1e-6)     # within a vote count: summed attention
+    for trial in range(60):
+        L = int(r.integers(1, 7))
+        nc = int(r.integers(1, 40))
+        k = int(r.integers(1, nc + 3))
+        local = int(r.integers(0, 4))
+        sc = r.integers(0, 6, (L, nc)).astype(np.float64) / 8.0   # many exact ties
+        if trial % 3 == 0:
+            sc = r.random((L, nc))
+        ends = np.arange(1, nc + 1)
+        votes = np.zeros(nc, np.int64)
+        for l in range(L):
+            for c in range(nc):
+                beat = sum(1 for j in range(nc)
+                           if sc[l, j] > sc[l, c] or (sc[l, j] == sc[l, c] and j < c))
+                votes[c] += beat < k
+        tot = [sum(sorted(sc[:, c])) for c in range(nc)]   # exact: multiples of 1/8
+        nl = nc - min(local, nc)
+
+        def beats(j, c):
+            return (votes[j], tot[j], -j) > (votes[c], tot[c], -c)
+        want = [c for c in range(nc)
+                if c >= nl or sum(1 for j in range(nl) if j != c and beats(j, c)) < k]
+        got_votes, _ = oracle.chunk_votes(sc, k)
+        assert np.array_equal(got_votes, votes), trial
+        assert _voted_chunks(sc, k, local, ends) == want, trial
 
 
 def test_score_c0_against_plain_loops():
