@@ -269,6 +269,27 @@ kvsel_status kvsel_decode_attn(const kvsel_shape* s /*host*/, const void* q, con
                                int64_t r_cap, float* out, void* ws, size_t ws_bytes,
                                hipStream_t stream);
 
+/* kvsel_decode_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture that may not call hipMalloc,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * kernels and result as kvsel_decode_attn; the per-item partials go to a
+ * static device array of KVSEL_DECODE_SCRATCH_BYTES that every GPU the
+ * library runs on holds until the process ends.  Nothing is allocated or
+ * freed by the call.  Calls on one GPU share that array: calls that overlap
+ * on one GPU (other streams, other threads) race and give undefined output;
+ * serialise them.  No scratch content carries over between calls (each call
+ * writes every partial it reads).  The first call on a device looks up the
+ * array's address there.
+ * Errors: as kvsel_decode_attn, and KVSEL_ENOSPC when the call's partials
+ * exceed the scratch (about r_cap / 2048 + batch * hkv items of
+ * 2080 bytes at head_dim 128 with 4 query heads per KV head; 8 MiB holds
+ * r_cap up to about 7.8 million rows). */
+#define KVSEL_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
+kvsel_status kvsel_decode_attn_noalloc(const kvsel_shape* s /*host*/, const void* q,
+                                       const void* k_c, const void* v_c, const int64_t* seg_off,
+                                       const int32_t* seg_len, int64_t r_cap, float* out,
+                                       hipStream_t stream);
+
 /* --------------------------------------------------------------- append --
  * Decode-time maintenance of the packed cache (FastGen page, core claim and
  * method: the per-head eviction rule keeps holding during generation --

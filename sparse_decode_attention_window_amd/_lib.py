@@ -67,6 +67,10 @@ _SIGS = {
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                      ctypes.c_void_p]),
+    "kvsel_decode_attn_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                                 ctypes.c_void_p, ctypes.c_void_p]),
     "kvsel_decode_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int64]),
     "kvsel_decode_attn": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -200,6 +204,13 @@ def kvsel_decode_attn(shape: Shape, q, k_c, v_c, seg_off, seg_len, r_cap: int, o
     _check(lib().kvsel_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k_c), _ptr(v_c),
                                    _ptr(seg_off), _ptr(seg_len), int(r_cap), _ptr(out), _ptr(ws),
                                    nbytes, _stream(stream)), "kvsel_decode_attn")
+
+
+def kvsel_decode_attn_noalloc(shape: Shape, q, k_c, v_c, seg_off, seg_len, r_cap: int, out,
+                              stream=None) -> None:
+    _check(lib().kvsel_decode_attn_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k_c), _ptr(v_c),
+                                           _ptr(seg_off), _ptr(seg_len), int(r_cap), _ptr(out),
+                                           _stream(stream)), "kvsel_decode_attn_noalloc")
 
 
 def kvsel_lmba_workspace(shape: Shape, w: int) -> int:

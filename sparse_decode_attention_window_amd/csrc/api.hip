@@ -357,4 +357,33 @@ kvsel_status kvsel_decode_attn(const kvsel_shape* s, const void* q, const void* 
                     "kvsel_decode_attn launch");
 }
 
+kvsel_status kvsel_decode_attn_noalloc(const kvsel_shape* s, const void* q, const void* k_c,
+                                       const void* v_c, const int64_t* seg_off,
+                                       const int32_t* seg_len, int64_t r_cap, float* out,
+                                       hipStream_t stream) {
+  g_err[0] = 0;
+  int S = 0, G = 0;
+  kvsel_status st = check_shape(s, &S, &G, 4);
+  if (st != KVSEL_OK) return st;
+  if (!q || !seg_off || !seg_len || !out) return fail(KVSEL_EINVAL, "q, seg_off, seg_len, out must be non-NULL");
+  if (r_cap > 0 && (!k_c || !v_c)) return fail(KVSEL_EINVAL, "k_c and v_c must be non-NULL");
+  if (r_cap < 0 || r_cap > 0x7fffffffLL) return fail(KVSEL_EINVAL, "r_cap must be in [0, 2^31)");
+  const size_t need = decode_noalloc_bytes(s->dtype, s->head_dim, S, G, r_cap);
+  if (need > (size_t)KVSEL_DECODE_SCRATCH_BYTES)
+    return fail(KVSEL_ENOSPC,
+                "decode without allocation needs %zu bytes of scratch for %d segments and %lld "
+                "rows; the library's static scratch holds %zu",
+                need, S, (long long)r_cap, (size_t)KVSEL_DECODE_SCRATCH_BYTES);
+  RopeDev rope;
+  const int64_t q_pos = s->rope ? s->rope->q_pos : 0;
+  if ((st = rope_of(s, q_pos, q_pos, &rope)) != KVSEL_OK) return st;
+  void* ws = nullptr;
+  if ((st = hip_status(decode_scratch(&ws), "kvsel_decode_attn_noalloc scratch address")) !=
+      KVSEL_OK)
+    return st;
+  return hip_status(launch_decode(s->dtype, s->head_dim, s->batch, s->hq, s->hkv, s->scale, q, k_c,
+                                  v_c, seg_off, seg_len, r_cap, out, ws, rope, q_pos, stream),
+                    "kvsel_decode_attn_noalloc launch");
+}
+
 }  // extern "C"

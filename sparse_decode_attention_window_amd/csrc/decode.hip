@@ -22,7 +22,9 @@
 // in the log2 domain with the scale folded into one multiply.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
+#include "../../include/kvsel.h"
 #include "kvsel_internal.h"
 
 namespace kvsel {
@@ -440,22 +442,36 @@ int resident_blocks(K kernel) {
   return v;
 }
 
+// Launch plan: rows per wavefront and the number of items launched (two items
+// per CU even where three fit: an integer count per CU keeps the CUs evenly
+// loaded, and two long items beat three shorter ones (measured at 6553 rows
+// per segment: 26.8 us vs 27.7 us at three, 29.1 at one, 31.3 and 30.1 at the
+// uneven 1.5 and 2.5 per CU; 64 ragged segments of 32768 / 2048 / 656 rows at
+// d 88: 46.4 vs 48.7 us)).
+template <typename T, int D, int HG>
+int64_t plan_items(int S, int64_t r_cap, int* rpw_out) {
+  const int slots = device_info().cus * std::min(2, resident_blocks(decode_split_kernel<T, D, HG>));
+  const int rpw = rows_per_wave(r_cap, S, slots);
+  const int64_t rpi = (int64_t)kWaves * rpw;
+  *rpw_out = rpw;
+  return (r_cap + rpi - 1) / rpi + S;   // <= max_items(r_cap, S)
+}
+
+// Partials of `items` items: (max, sum) pairs, then the unnormalised outputs.
+template <int HG, int D>
+size_t partial_bytes(int64_t items) {
+  return (size_t)items * HG * (sizeof(float2) + sizeof(float) * D);
+}
+
 template <typename T, int D, int HG>
 hipError_t run(int batch, int hq, int hkv, float scale, const void* q, const void* k_c,
                const void* v_c, const int64_t* seg_off, const int32_t* seg_len, int64_t r_cap,
                float* out, void* ws, const RopeDev& rope, int64_t q_pos, hipStream_t stream) {
   const int S = batch * hkv, G = hq / hkv;
-  // two items per CU even where three fit: an integer count per CU keeps the
-  // CUs evenly loaded, and two long items beat three shorter ones (measured
-  // at 6553 rows per segment: 26.8 us vs 27.7 us at three, 29.1 at one, 31.3
-  // and 30.1 at the uneven 1.5 and 2.5 per CU; 64 ragged segments of
-  // 32768 / 2048 / 656 rows at d 88: 46.4 vs 48.7 us)
-  const int slots = device_info().cus * std::min(2, resident_blocks(decode_split_kernel<T, D, HG>));
-  const int rpw = rows_per_wave(r_cap, S, slots);
-  const int64_t rpi = (int64_t)kWaves * rpw;
-  const int64_t items = (r_cap + rpi - 1) / rpi + S;   // launched; <= max_items
+  int rpw = 0;
+  const int64_t items = plan_items<T, D, HG>(S, r_cap, &rpw);
   auto* ml = static_cast<float2*>(ws);
-  auto* po = reinterpret_cast<float*>(ml + max_items(r_cap, S) * HG);
+  auto* po = reinterpret_cast<float*>(ml + items * HG);
   const float c = scale * kLog2e;
   decode_split_kernel<T, D, HG><<<dim3((unsigned)items), dim3(kThreads), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(k_c),
@@ -481,7 +497,57 @@ hipError_t run_d(int batch, int hq, int hkv, float scale, const void* q, const v
 #undef KVSEL_HG
 }
 
+// Scratch of kvsel_decode_attn_noalloc: the per-item partials in a file-scope
+// device array instead of a caller workspace, for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy until the
+// process ends; host code uses the address hipGetSymbolAddress gives on that
+// device, never the array's name.
+static __device__ __align__(256) char scratch[KVSEL_DECODE_SCRATCH_BYTES];
+
+template <typename T, int D>
+size_t noalloc_need_d(int S, int G, int64_t r_cap) {
+  int rpw = 0;
+  switch (hg_for(G)) {
+    case 1: return partial_bytes<1, D>(plan_items<T, D, 1>(S, r_cap, &rpw));
+    case 2: return partial_bytes<2, D>(plan_items<T, D, 2>(S, r_cap, &rpw));
+    default: return partial_bytes<4, D>(plan_items<T, D, 4>(S, r_cap, &rpw));
+  }
+}
+
 }  // namespace
+
+size_t decode_noalloc_bytes(int dtype, int head_dim, int S, int G, int64_t r_cap) {
+  if (dtype == 1) {
+    if (head_dim == 64) return noalloc_need_d<bf16_t, 64>(S, G, r_cap);
+    if (head_dim == 88) return noalloc_need_d<bf16_t, 88>(S, G, r_cap);
+    return noalloc_need_d<bf16_t, 128>(S, G, r_cap);
+  }
+  if (head_dim == 64) return noalloc_need_d<float, 64>(S, G, r_cap);
+  if (head_dim == 88) return noalloc_need_d<float, 88>(S, G, r_cap);
+  return noalloc_need_d<float, 128>(S, G, r_cap);
+}
+
+// The current device's address of `scratch`, looked up once per device (with
+// that device current) and kept.
+hipError_t decode_scratch(void** out) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
 
 size_t decode_workspace_bytes(int S, int head_dim, int G, int64_t r_cap) {
   const int HG = hg_for(G);

@@ -317,6 +317,8 @@ constexpr int kProbeBlocks = 2048;
 hipError_t launch_probe(int mode, const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
 size_t decode_workspace_bytes(int S, int head_dim, int G, int64_t r_cap);
+size_t decode_noalloc_bytes(int dtype, int head_dim, int S, int G, int64_t r_cap);
+hipError_t decode_scratch(void** out);
 hipError_t launch_decode(int dtype, int head_dim, int batch, int hq, int hkv, float scale,
                          const void* q, const void* k_c, const void* v_c,
                          const int64_t* seg_off, const int32_t* seg_len, int64_t r_cap,

@@ -279,3 +279,22 @@ def test_hbm_probe_rejects_bad_arguments():
         assert st == 1, (mode, src, dst, nbytes, st)   # KVSEL_EINVAL
         assert kvsel.kvsel_last_error()
     assert kvsel.KVSEL_PROBE_BLOCKS == 2048
+
+
+def test_decode_noalloc_rejects_bad_args():
+    """The allocation-free decode checks its arguments like kvsel_decode_attn
+    and refuses, before anything is enqueued, a call whose partials exceed
+    the static scratch."""
+    sh = shape(dtype="bf16", head_dim=128, batch=4, hq=32, hkv=8, n=32768)
+    lib = kvsel.lib()
+
+    def call(s=sh, q=FAKE, kc=FAKE, out=FAKE, r_cap=1000):
+        return lib.kvsel_decode_attn_noalloc(ctypes.byref(s), q, kc, FAKE, FAKE, FAKE, r_cap, out,
+                                             None)
+    assert call(q=None) == _lib.KVSEL_EINVAL
+    assert call(out=None) == _lib.KVSEL_EINVAL
+    assert call(kc=None) == _lib.KVSEL_EINVAL
+    assert call(r_cap=-1) == _lib.KVSEL_EINVAL
+    assert call(s=shape(hq=16, hkv=2)) == _lib.KVSEL_EUNSUPPORTED
+    assert call(r_cap=(1 << 31) - 1) == _lib.KVSEL_ENOSPC
+    assert "static scratch" in kvsel.kvsel_last_error()
