@@ -4,18 +4,25 @@
 //
 // A softmax weight needs its row's max and normaliser before it is final, so
 // the score runs in two passes over the keys (each reading K once):
-//   stats   per 512-key tile, per query row: running max and sum of 2^(x-max)
+//   stats   per run of keys, per query row: running max and sum of 2^(x-max)
 //           (x = scale * log2(e) * q.k, the log2-domain logit)
-//   reduce  per query row: K_r = max + log2(sum) over all tiles
+//   reduce  per query row: K_r = max + log2(sum) over all runs
 //   final   per key: sum over rows of 2^(x - K_r)
 // Both heavy passes put Q K^T on the matrix cores (32x32 tiles): in the
 // stats pass keys are the M operand so a lane owns one query row (row
 // statistics stay in-lane); in the final pass queries are the M operand so a
-// lane owns one key (column sums stay in-lane).  Q of the segment is staged
-// once per workgroup in LDS; K fragments go straight from HBM to registers
-// and serve as A or B operand unchanged (both operands share one per-lane
-// layout).  Causal masking (query row i at position q_pos0 + i) is only
-// evaluated on tiles that reach past q_pos0.
+// lane owns one key (column sums stay in-lane).  K fragments go straight from
+// HBM to registers and serve as A or B operand unchanged (both operands share
+// one per-lane layout).
+//
+// Two forms of the passes.  Up to 128 query rows (bf16; one row block in
+// fp32): one wavefront per workgroup keeps every row's Q fragments in its
+// registers for a long run of keys and interleaves the MFMA chain of one row
+// block with the exponentials of the previous one (score_*_reg_kernel).
+// Otherwise (more rows, or the attention rows written out for LMBA): four
+// wavefronts share Q staged once per workgroup in LDS (score_stats_kernel,
+// score_final_kernel).  Causal masking (query row i at position q_pos0 + i)
+// is only evaluated on blocks that reach past q_pos0.
 #include <type_traits>
 
 #include "kvsel_internal.h"
@@ -339,6 +346,259 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
   });
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident query rows (up to 128 rows): one wavefront per workgroup
+// holds the Q fragments of every row block in registers for its whole run of
+// keys, so no LDS traffic carries Q; K fragments stream from HBM straight into
+// the operand registers, the next 32-key block in flight while the current
+// one is multiplied and reduced.  Each K fragment feeds RBN MFMA chains.
+// Keys per wavefront: the query rows come from L2 once per wavefront, so long
+// runs amortise them, but a call needs enough wavefronts to fill the chip
+// (two per SIMD) several times over.  The largest power of two in [512, 4096]
+// that still gives four rounds of wavefronts (C2 bench, 32 layers in one call,
+// per layer: 111.7 us at 512, 105.1 at 1024, 101.9 at 2048, 99.2 at 4096,
+// 100.1 at 8192; a single 32-segment layer fills one round at 512).
+int reg_keys_per_wave(int S, int64_t n) {
+  const int64_t slots = (int64_t)device_info().cus * 4 * 2;
+  int kpw = 4096;
+  while (kpw > 512 && (int64_t)S * ((n + kpw - 1) / kpw) < 4 * slots) kpw /= 2;
+  return kpw;
+}
+constexpr int kValuPerMfma = 8;       // VALU instructions scheduled after each MFMA
+
+template <typename T>
+struct MfmaPerStep { static constexpr int value = 1; };     // bf16: one 32x32x16
+template <>
+struct MfmaPerStep<float> { static constexpr int value = 4; };   // fp32: four 32x32x2
+
+// Blocks of a wavefront's run (32 keys each from kb on) that need no mask:
+// the leading ones that end below n and at or before q_pos0 (the first
+// window row's position), so every row sees all of their keys.
+__device__ __forceinline__ int free_blocks(int64_t kb, int nblk, int64_t n, int64_t q_pos0) {
+  const int64_t lim = min(n - 1, q_pos0);   // last key every row sees
+  const int64_t f = lim < kb + 31 ? 0 : (lim - kb - 31) / 32 + 1;
+  return (int)min((int64_t)nblk, f);
+}
+
+template <typename T, int D, int RBN>
+__device__ __forceinline__ void load_q_regs(const char* __restrict__ qw, int b, int kvh, int hq,
+                                            int G, int w, int R, int lane,
+                                            u32x4 (&qf)[RBN][SGeom<T, D>::NA]) {
+  using Gm = SGeom<T, D>;
+  const char* src = qw + ((int64_t)b * hq + (int64_t)kvh * G) * w * Gm::RB;
+  const int half = lane >> 5, l32 = lane & 31;
+  const u32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+  for (int rb = 0; rb < RBN; ++rb) {
+    const int r = rb * 32 + l32;
+    const int rc = r < R ? r : R - 1;
+#pragma unroll
+    for (int a = 0; a < Gm::NA; ++a) {
+      const int o = 32 * a + 16 * half;
+      const u32x4 x = load16(src + (int64_t)rc * Gm::RB + (o < Gm::RB ? o : Gm::RB - 16));
+      qf[rb][a] = (r < R && o < Gm::RB) ? x : zero;
+    }
+  }
+}
+
+template <typename T, int D, int RBN>
+__global__ __launch_bounds__(64, 2) void score_stats_reg_kernel(
+    const char* __restrict__ qw, const char* __restrict__ k, int64_t n, int hq, int hkv, int G,
+    int w, int R, int64_t q_pos0, float c, float2* __restrict__ stats, int tiles, int kpw) {
+  using Gm = SGeom<T, D>;
+  constexpr int RP = RBN * 32;
+  const int s = blockIdx.y, tile = blockIdx.x;
+  const int b = s / hkv, kvh = s % hkv;
+  const int lane = threadIdx.x, half = lane >> 5, l32 = lane & 31;
+  const char* kseg = k + (int64_t)s * n * Gm::RB;
+  const int64_t kb = (int64_t)tile * kpw;
+  const int nblk = (int)((min(n - kb, (int64_t)kpw) + 31) / 32);
+  auto row_of = [&](int i) { return min(kb + 32 * i + l32, n - 1); };
+
+  u32x4 kf[2][Gm::NA];
+  load_k<T, D>(kseg, row_of(0), half, kf[0]);
+  u32x4 qf[RBN][Gm::NA];
+  load_q_regs<T, D, RBN>(qw, b, kvh, hq, G, w, R, lane, qf);
+  float Mr[RBN], Lr[RBN];
+#pragma unroll
+  for (int rb = 0; rb < RBN; ++rb) {
+    Mr[rb] = -INFINITY;
+    Lr[rb] = 0.f;
+  }
+  // row r sees keys <= its limit (computed in masked blocks only, to save registers)
+  auto row_lim = [&](int rb) {
+    const int r = rb * 32 + l32;
+    const int64_t p = q_pos0 + (r % w);
+    return r < R ? (int)(p < n - 1 ? p : n - 1) : -1;
+  };
+
+  // One 32-key block.  The MFMA chain of row block rb + 1 is issued before
+  // the softmax statistics of row block rb, and the scheduler is asked to
+  // interleave the two (one MFMA, then VALU work), so the matrix core and
+  // the VALU of this wavefront run at once.
+  auto block = [&](const u32x4* kf_, int64_t key0, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const int kb0 = (int)key0;
+    f32x16 acc[2];
+    acc[0] = f32x16{};
+#pragma unroll
+    for (int a = 0; a < Gm::NA; ++a) acc[0] = mma_step(kf_[a], qf[0][a], acc[0], T{});
+#pragma unroll
+    for (int rb = 0; rb < RBN; ++rb) {
+      if (rb + 1 < RBN) {
+        acc[(rb + 1) & 1] = f32x16{};
+#pragma unroll
+        for (int a = 0; a < Gm::NA; ++a)
+          acc[(rb + 1) & 1] = mma_step(kf_[a], qf[rb + 1][a], acc[(rb + 1) & 1], T{});
+      }
+      f32x16& x = acc[rb & 1];
+      // lane owns query row rb*32 + lane%32 and the 16 keys key0 + acc_row(j)
+      float tm = -INFINITY;
+      const int lr = MASKED ? row_lim(rb) : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (MASKED && kb0 + acc_row(j, lane) > lr) x[j] = -INFINITY;
+        tm = fmaxf(tm, x[j]);
+      }
+      const float mn = fmaxf(Mr[rb], tm * c);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};   // four running partials: no stall on each add
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ps[j & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -ms));
+      Lr[rb] = Lr[rb] * __builtin_amdgcn_exp2f(Mr[rb] - ms) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+      Mr[rb] = mn;
+      if (rb + 1 < RBN) {
+#pragma unroll
+        for (int a = 0; a < Gm::NA * MfmaPerStep<T>::value; ++a) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);   // VALU
+        }
+      }
+    }
+  };
+  // blocks [0, nfree) need no mask (every key below n and visible to every
+  // row); they run double-buffered, the few masked ones after them
+  const int nfree = free_blocks(kb, nblk, n, q_pos0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < nfree; i += 2) {
+    load_k<T, D>(kseg, row_of(min(i + 1, nblk - 1)), half, kf[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    block(kf[0], kb + 32 * i, std::false_type{});
+    if (i + 1 >= nfree) break;
+    load_k<T, D>(kseg, row_of(min(i + 2, nblk - 1)), half, kf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    block(kf[1], kb + 32 * (i + 1), std::false_type{});
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = nfree; i < nblk; ++i) {
+    load_k<T, D>(kseg, row_of(i), half, kf[0]);
+    block(kf[0], kb + 32 * i, std::true_type{});
+  }
+  // merge the two half-waves (same row, other 16 keys of each block)
+#pragma unroll
+  for (int rb = 0; rb < RBN; ++rb) {
+    const float mo = __shfl_xor(Mr[rb], 32), lo = __shfl_xor(Lr[rb], 32);
+    const float mn = fmaxf(Mr[rb], mo);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    const float L = Lr[rb] * exp2f(Mr[rb] - ms) + lo * exp2f(mo - ms);
+    if (half == 0) stats[((int64_t)s * tiles + tile) * RP + rb * 32 + l32] = make_float2(mn, L);
+  }
+}
+
+template <typename T, int D, int RBN>
+__global__ __launch_bounds__(64, 2) void score_final_reg_kernel(
+    const char* __restrict__ qw, const char* __restrict__ k, int64_t n, int hq, int hkv, int G,
+    int w, int R, int64_t q_pos0, float c, const float* __restrict__ rowc,
+    float* __restrict__ scores, int kpw) {
+  using Gm = SGeom<T, D>;
+  constexpr int RP = RBN * 32;
+  __shared__ float krow[RP];
+  __shared__ int lim[RP];
+  const int s = blockIdx.y, tile = blockIdx.x;
+  const int b = s / hkv, kvh = s % hkv;
+  const int lane = threadIdx.x, half = lane >> 5, l32 = lane & 31;
+  const char* kseg = k + (int64_t)s * n * Gm::RB;
+  const int64_t kb = (int64_t)tile * kpw;
+  const int nblk = (int)((min(n - kb, (int64_t)kpw) + 31) / 32);
+  auto row_of = [&](int i) { return min(kb + 32 * i + l32, n - 1); };
+
+  u32x4 kf[2][Gm::NA];
+  load_k<T, D>(kseg, row_of(0), half, kf[0]);
+  u32x4 qf[RBN][Gm::NA];
+  load_q_regs<T, D, RBN>(qw, b, kvh, hq, G, w, R, lane, qf);
+  for (int r = lane; r < RP; r += 64) {
+    krow[r] = rowc[(int64_t)s * RP + r];
+    const int64_t p = q_pos0 + (r % w);
+    lim[r] = r < R ? (int)(p < n - 1 ? p : n - 1) : -1;
+  }
+  __syncthreads();
+
+  // One 32-key block, pipelined as in the statistics pass: the MFMA chain of
+  // row block rb + 1 runs while the exponentials of row block rb are summed.
+  auto block = [&](const u32x4* kf_, int64_t key0, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const int64_t key = key0 + l32;
+    float ssum = 0.f;
+    f32x16 acc[2];
+    acc[0] = f32x16{};
+#pragma unroll
+    for (int a = 0; a < Gm::NA; ++a) acc[0] = mma_step(qf[0][a], kf_[a], acc[0], T{});
+#pragma unroll
+    for (int rb = 0; rb < RBN; ++rb) {
+      if (rb + 1 < RBN) {
+        acc[(rb + 1) & 1] = f32x16{};
+#pragma unroll
+        for (int a = 0; a < Gm::NA; ++a)
+          acc[(rb + 1) & 1] = mma_step(qf[rb + 1][a], kf_[a], acc[(rb + 1) & 1], T{});
+      }
+      const f32x16& x = acc[rb & 1];
+      // lane owns key `key` and the 16 query rows rb*32 + acc_row(j)
+      float part[4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = rb * 32 + g4 * 8 + half * 4;
+        const float4 kr = *reinterpret_cast<const float4*>(&krow[r0]);
+        const float kk[4] = {kr.x, kr.y, kr.z, kr.w};
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g4 * 4 + e], c, -kk[e]));
+          if (MASKED && (int)key > lim[r0 + e]) p[e] = 0.f;
+        }
+        part[g4] = (p[0] + p[1]) + (p[2] + p[3]);
+      }
+      ssum += (part[0] + part[1]) + (part[2] + part[3]);
+      if (rb + 1 < RBN) {
+#pragma unroll
+        for (int a = 0; a < Gm::NA * MfmaPerStep<T>::value; ++a) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);   // VALU
+        }
+      }
+    }
+    ssum += __shfl_xor(ssum, 32);
+    if (half == 0 && key < n) scores[(int64_t)s * n + key] = ssum;
+  };
+  // blocks [0, nfree) need no mask (every key below n and visible to every
+  // row); they run double-buffered, the few masked ones after them
+  const int nfree = free_blocks(kb, nblk, n, q_pos0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < nfree; i += 2) {
+    load_k<T, D>(kseg, row_of(min(i + 1, nblk - 1)), half, kf[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    block(kf[0], kb + 32 * i, std::false_type{});
+    if (i + 1 >= nfree) break;
+    load_k<T, D>(kseg, row_of(min(i + 2, nblk - 1)), half, kf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    block(kf[1], kb + 32 * (i + 1), std::false_type{});
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = nfree; i < nblk; ++i) {
+    load_k<T, D>(kseg, row_of(i), half, kf[0]);
+    block(kf[0], kb + 32 * i, std::true_type{});
+  }
+}
+
 template <typename T, int D, int RBN, bool PROBS = false>
 hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int64_t q_pos0,
                     float c, const char* qp, const char* kp, float* scores, float2* stats,
@@ -354,6 +614,22 @@ hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int6
     if (e != hipSuccess) return e;
   }
   const dim3 grid(tiles, S);
+  // register-resident query rows: the Q fragments of all row blocks must fit
+  // in 128 VGPRs (bf16 up to 128 rows of 128 dims; fp32 one row block)
+  constexpr bool kRegFits = RBN <= 4 && RBN * Gm::NA <= 32 && (sizeof(T) == 2 || RBN == 1);
+  if constexpr (kRegFits && !PROBS) {
+    {
+      const int kpw = reg_keys_per_wave(S, n);
+      const int rt = (int)((n + kpw - 1) / kpw);
+      const dim3 rgrid(rt, S);
+      score_stats_reg_kernel<T, D, RBN><<<rgrid, dim3(64), 0, stream>>>(
+          qp, kp, n, hq, hkv, G, w, R, q_pos0, c, stats, rt, kpw);
+      score_reduce_kernel<<<dim3(S), dim3(kReduceThreads), 0, stream>>>(stats, rt, R, rowc);
+      score_final_reg_kernel<T, D, RBN><<<rgrid, dim3(64), 0, stream>>>(
+          qp, kp, n, hq, hkv, G, w, R, q_pos0, c, rowc, scores, kpw);
+      return hipGetLastError();
+    }
+  }
   score_stats_kernel<T, D, RBN><<<grid, dim3(kThreads), lds, stream>>>(
       qp, kp, n, hq, hkv, G, w, R, q_pos0, c, stats, tiles);
   score_reduce_kernel<<<dim3(S), dim3(kReduceThreads), 0, stream>>>(stats, tiles, R, rowc);
