@@ -77,18 +77,18 @@ def copy_reference(torch, reps: int = 5) -> float:
     return 2 * COPY_BYTES / t / 1e9
 
 
-def stream_ceiling(torch, kvsel, mode: int, moved: int, nb: int = 4, calls: int = 8) -> float:
-    """GB/s of the library's non-temporal HBM stream (kvsel_hbm_probe) at one
+def stream_ceiling(torch, probe, mode: int, moved: int, nb: int = 4, calls: int = 8) -> float:
+    """GB/s of the benchmark's non-temporal HBM stream (libkvsel_probe.so) at one
     call's size: `moved` bytes per call (read, or read + write for a copy), in
     a graph of `calls` back-to-back calls over `nb` rotating buffers."""
-    per = (moved if mode == kvsel.KVSEL_PROBE_READ else moved // 2) // 16 * 16
+    per = (moved if mode == probe.PROBE_READ else moved // 2) // 16 * 16
     srcs = [torch.ones(per // 2, dtype=torch.bfloat16, device="cuda") for _ in range(nb)]
-    dst_bytes = kvsel.KVSEL_PROBE_BLOCKS * 16 if mode == kvsel.KVSEL_PROBE_READ else per
+    dst_bytes = probe.PROBE_BLOCKS * 16 if mode == probe.PROBE_READ else per
     dsts = [torch.empty(dst_bytes, dtype=torch.uint8, device="cuda") for _ in range(nb)]
 
     def run():
         for i in range(calls):
-            kvsel.kvsel_hbm_probe(mode, srcs[i % nb], dsts[i % nb], per)
+            probe.probe_stream(mode, srcs[i % nb], dsts[i % nb], per)
     run()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -106,7 +106,7 @@ def stream_ceiling(torch, kvsel, mode: int, moved: int, nb: int = 4, calls: int 
         ts.append(e[0].elapsed_time(e[1]) * 1e-3 / calls)
     del g, srcs, dsts
     ts.sort()
-    moved_per = per if mode == kvsel.KVSEL_PROBE_READ else 2 * per
+    moved_per = per if mode == probe.PROBE_READ else 2 * per
     return moved_per / ts[len(ts) // 2] / 1e9
 
 
@@ -502,8 +502,9 @@ def main() -> int:
     dec_gbs = gbs(dec_bytes, us["decode"])
     cmp_gbs = gbs(cmp_bytes, us["compact"])
     # what a plain non-temporal stream of the same size per call reaches here
-    read_ceiling = stream_ceiling(torch, kvsel, kvsel.KVSEL_PROBE_READ, int(dec_bytes))
-    copy_ceiling = stream_ceiling(torch, kvsel, kvsel.KVSEL_PROBE_COPY, int(cmp_bytes))
+    from sparse_decode_attention_window_amd import _probe as probe
+    read_ceiling = stream_ceiling(torch, probe, probe.PROBE_READ, int(dec_bytes))
+    copy_ceiling = stream_ceiling(torch, probe, probe.PROBE_COPY, int(cmp_bytes))
     log(f"[bench] stream ceilings at the call sizes: read {read_ceiling:.0f} GB/s, "
         f"copy {copy_ceiling:.0f} GB/s")
     traffic = None
@@ -595,7 +596,7 @@ def main() -> int:
         "hbm_stream_ceilings": {
             "read_GBps": round(read_ceiling, 1), "read_bytes_per_call": int(dec_bytes),
             "copy_GBps": round(copy_ceiling, 1), "copy_bytes_per_call": int(cmp_bytes),
-            "method": "kvsel_hbm_probe non-temporal read / copy streams at the decode and "
+            "method": "libkvsel_probe.so non-temporal read / copy streams at the decode and "
                       "compact call sizes, graph of 8 back-to-back calls over 4 rotating "
                       "buffers"},
         "decode_frac_of_read_ceiling": round(dec_gbs / read_ceiling, 4),

@@ -160,8 +160,10 @@ kvsel_status kvsel_score(const kvsel_shape* s /*host*/, int32_t w, int64_t q_pos
  *   ws         at least kvsel_lmba_workspace(s, w) bytes (it holds the
  *              attention rows: batch*hkv*G*w*n floats)
  * Constraints as for kvsel_score; with kept_mass, n/8 bytes of position
- * mask plus 32 KB must fit in one workgroup's LDS (n up to about 1M on
- * gfx950), else KVSEL_EUNSUPPORTED. */
+ * mask plus the row kernel's own LDS (about 41 KB, or 45 KB for rows longer
+ * than 32768 keys or not a multiple of 4) must fit in one workgroup's LDS:
+ * n up to about 930 K keys on gfx950 (160 KB), else KVSEL_EUNSUPPORTED with
+ * nothing enqueued. */
 size_t kvsel_lmba_workspace(const kvsel_shape* s /*host*/, int32_t w);
 kvsel_status kvsel_lmba(const kvsel_shape* s /*host*/, int32_t w, int64_t q_pos0,
                         const void* q_win, const void* k, int32_t* lmba, const int64_t* seg_off,
@@ -326,23 +328,6 @@ kvsel_status kvsel_append(const kvsel_shape* s /*host*/, const void* k_new, cons
  * Errors: EINVAL unless 0 <= floor_budget <= avg_budget <= n and L >= 1. */
 kvsel_status kvsel_zigzag_budgets(const double* profile, int32_t L, int64_t n,
                                   int64_t avg_budget, int64_t floor_budget, int32_t* out);
-
-/* ------------------------------------------------------ measurement aid --
- * Not part of the method: a plain HBM stream that sets the rate a call of a
- * given size can reach on this GPU, for the bandwidth figures beside each
- * kernel's own.  16-byte non-temporal accesses over a fixed grid of
- * KVSEL_PROBE_BLOCKS workgroups; asynchronous on `stream`.
- *   mode   KVSEL_PROBE_READ: read src; dst receives one 16-byte XOR fold per
- *          workgroup, dst[KVSEL_PROBE_BLOCKS][16 bytes] (the XOR of those
- *          words is the XOR of all of src's 16-byte words);
- *          KVSEL_PROBE_COPY: copy `bytes` of src to dst (not overlapping).
- *   src, dst  device pointers, 16-byte aligned; bytes > 0, a multiple of 16.
- * Errors: EINVAL for another mode, NULL or misaligned pointers, or bytes not
- * a positive multiple of 16. */
-#define KVSEL_PROBE_BLOCKS 2048
-typedef enum { KVSEL_PROBE_READ = 0, KVSEL_PROBE_COPY = 1 } kvsel_probe_mode;
-kvsel_status kvsel_hbm_probe(int32_t mode, const void* src, void* dst, int64_t bytes,
-                             hipStream_t stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* kvsel_last_error(void);

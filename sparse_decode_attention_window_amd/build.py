@@ -18,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvsel.so")
+PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libkvsel_probe.so")   # the benchmark's HBM stream, not the method
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -67,5 +69,14 @@ def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD,
     return out
 
 
+def build_probe(out: str = PROBE_LIB) -> str:
+    """The benchmark's HBM stream probe, a library of its own."""
+    tmp = out + ".tmp"
+    _run([HIPCC, *HIP_FLAGS, "-shared", PROBE_SRC, "-o", tmp])
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe())

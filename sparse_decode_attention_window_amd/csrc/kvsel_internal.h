@@ -311,10 +311,6 @@ hipError_t launch_select_policy(int S, int hkv, int64_t n, const int8_t* head_ki
                                 int64_t n_special, const int64_t* seg_off, int32_t* seg_len,
                                 int32_t* idx, int64_t r_cap, hipStream_t stream);
 
-// Measurement aid: HBM read (mode 0, one 16-byte fold per workgroup into dst)
-// or copy (mode 1) stream over a fixed grid of kProbeBlocks workgroups.
-constexpr int kProbeBlocks = 2048;
-hipError_t launch_probe(int mode, const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
 size_t decode_workspace_bytes(int S, int head_dim, int G, int64_t r_cap);
 size_t decode_noalloc_bytes(int dtype, int head_dim, int S, int G, int64_t r_cap);
@@ -355,5 +351,7 @@ hipError_t launch_lmba_rows(const float* probs, int S, int R, int64_t n, int32_t
                             hipStream_t stream);
 // bytes of the per-segment kept-position masks launch_lmba_rows needs
 size_t lmba_mask_bytes(int S, int64_t n);
+// LDS of one LMBA row workgroup for rows of n keys (with or without the kept mask)
+size_t lmba_row_lds_bytes(int64_t n, bool kept);
 
 }  // namespace kvsel

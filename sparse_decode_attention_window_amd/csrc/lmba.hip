@@ -357,6 +357,19 @@ hipError_t launch_rows(const float* probs, int S, int R, int64_t n, int32_t* lmb
 
 size_t lmba_mask_bytes(int S, int64_t n) { return (size_t)S * (size_t)((n + 31) / 32) * 4; }
 
+// LDS one row workgroup takes: its static arrays (the kernel's own, for the
+// instantiation launch_lmba_rows picks for n; an upper bound built from the
+// same declarations) plus, with kept_mass, the n-bit position mask.
+size_t lmba_row_lds_bytes(int64_t n, bool kept) {
+  const int64_t npt = (n % 4) ? kMaxNpt + 1 : (n + kThreads - 1) / kThreads;
+  const bool packed = npt <= kMaxNpt;
+  const size_t bins = packed ? sizeof(Bins<true>) : sizeof(Bins<false>);
+  const size_t fixed = bins + sizeof(float) * kMaxCand + 2 * sizeof(unsigned long long) * kWaves +
+                       sizeof(uint32_t) * kWaves + sizeof(unsigned long long) +
+                       2 * sizeof(uint32_t) + 256;   // + alignment slack
+  return fixed + (kept ? (size_t)((n + 31) / 32) * 4 : 0);
+}
+
 hipError_t launch_lmba_rows(const float* probs, int S, int R, int64_t n, int32_t* lmba,
                             const int64_t* seg_off, const int32_t* seg_len, const int32_t* idx,
                             int64_t r_cap, float* kept_mass, uint32_t* mask,

@@ -154,6 +154,26 @@ def test_lmba_rejects_bad_args():
     assert lm(ws_bytes=need - 1) == _lib.KVSEL_ENOSPC
 
 
+def test_lmba_kept_mass_lds_limit():
+    """With kept_mass, the n-bit position mask and the row kernel's own LDS
+    (its bins, candidate list and block-scan words: 45,488 bytes with slack for
+    rows longer than 32768 keys) must fit one workgroup's LDS.  At the limit
+    the call passes the check (and fails on the too-small workspace); one
+    mask word more is refused as unsupported, before anything is enqueued."""
+    import torch
+    max_lds = 163840 if torch.cuda.is_available() else 65536   # gfx950, or no device
+    words = (max_lds - 45488) // 4
+    lib = kvsel.lib()
+
+    def lm(n):
+        sh = shape(n=n)
+        return lib.kvsel_lmba(ctypes.byref(sh), 8, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                              FAKE, FAKE, 16, None)
+    assert lm(32 * words) == _lib.KVSEL_ENOSPC
+    assert lm(32 * words + 32) == _lib.KVSEL_EUNSUPPORTED
+    assert "position mask" in kvsel.kvsel_last_error()
+
+
 def test_chunk_vote_rejects_bad_args():
     sh = shape(n=100)
     lib = kvsel.lib()
@@ -256,29 +276,6 @@ def test_budgets_reject():
         kvsel.kvsel_zigzag_budgets([1.0, -2.0], 100, 10, 1)
     with pytest.raises(kvsel.KvselError):
         kvsel.kvsel_zigzag_budgets([], 100, 10, 1)
-
-
-def test_hbm_probe_rejects_bad_arguments():
-    """The measurement stream checks mode, pointers, alignment and size on the
-    host and enqueues nothing when a check fails."""
-    probe = kvsel.lib().kvsel_hbm_probe
-    ok_src, ok_dst = FAKE, FAKE + 0x100000
-    cases = [
-        (2, ok_src, ok_dst, 1024),          # unknown mode
-        (-1, ok_src, ok_dst, 1024),
-        (0, None, ok_dst, 1024),            # NULL source
-        (1, ok_src, None, 1024),            # NULL destination
-        (1, ok_src + 8, ok_dst, 1024),      # misaligned source
-        (0, ok_src, ok_dst + 4, 1024),      # misaligned destination
-        (1, ok_src, ok_dst, 0),             # empty
-        (1, ok_src, ok_dst, -16),
-        (0, ok_src, ok_dst, 1000),          # not a multiple of 16
-    ]
-    for mode, src, dst, nbytes in cases:
-        st = probe(mode, src, dst, nbytes, None)
-        assert st == 1, (mode, src, dst, nbytes, st)   # KVSEL_EINVAL
-        assert kvsel.kvsel_last_error()
-    assert kvsel.KVSEL_PROBE_BLOCKS == 2048
 
 
 def test_decode_noalloc_rejects_bad_args():
