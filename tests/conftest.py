@@ -26,3 +26,19 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # the parity margins the GPU tests reached, for the record
+    util = sys.modules.get("tests.parity_util")
+    if util is None or not util.MARGINS:
+        return
+    import json
+    path = os.environ.get("KVSEL_PARITY_MARGINS",
+                          os.path.join(ROOT, "gpurun_out", "parity_margins.json"))
+    try:
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w") as f:
+            json.dump(util.MARGINS, f, indent=1, sort_keys=True)
+    except OSError:
+        pass

@@ -1,6 +1,8 @@
 """Helpers for the GPU-vs-oracle parity tests (imported by tests only)."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 import kvsynth
@@ -10,6 +12,19 @@ import oracle
 SCORE_RTOL = 1e-5
 TIE_BAND = 1e-5
 OUT_ATOL = {"fp32": 1e-5, "bf16": 1e-2}
+
+
+# Largest margin each test reached, per kind (written out by conftest at the
+# end of a session that ran GPU tests): score relative error, decode max-abs
+# error per dtype, selection entries that differ inside the tie band, LMBA
+# counts off the float64 row's own count (inside the band).
+MARGINS: dict = {}
+
+
+def record(kind: str, value) -> None:
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    d = MARGINS.setdefault(test, {})
+    d[kind] = max(d.get(kind, 0), value)
 
 
 def to_host(t) -> np.ndarray:
@@ -35,7 +50,9 @@ def check_scores(s_gpu: np.ndarray, s_ref: np.ndarray, rows: int, what: str) -> 
                            f"ref={s_ref[bad[0]]!r}")
     assert abs(s_gpu.sum() - rows) < 1e-4 * rows, f"{what}: mass {s_gpu.sum()} != {rows}"
     nz = s_ref > 0
-    return float(np.max(err[nz] / s_ref[nz])) if nz.any() else 0.0
+    rel = float(np.max(err[nz] / s_ref[nz])) if nz.any() else 0.0
+    record("score_rel", rel)
+    return rel
 
 
 def check_topb_selection(idx_gpu: np.ndarray, s_gpu: np.ndarray, s_ref: np.ndarray, budget: int,
@@ -56,6 +73,7 @@ def check_topb_selection(idx_gpu: np.ndarray, s_gpu: np.ndarray, s_ref: np.ndarr
         sB = np.sort(s_ref)[::-1][B - 1]
         out = diff[np.abs(s_ref[diff] - sB) > TIE_BAND * abs(sB)]
         assert out.size == 0, f"{what}: {out.size} selections differ outside the tie band"
+        record("tie_band_diffs", int(diff.size))
 
 
 def check_chunk_selection(idx_gpu, cs_gpu, cs_ref, ends, keep, what, local=0, top=0):
@@ -73,6 +91,7 @@ def check_chunk_selection(idx_gpu, cs_gpu, cs_ref, ends, keep, what, local=0, to
     band = TIE_BAND * abs(cs_ref[last])
     for c in cg ^ cr:
         assert abs(cs_ref[c] - cs_ref[last]) <= band, f"{what}: chunk {c} differs outside band"
+    record("tie_band_diffs", len(cg ^ cr))
 
 
 def check_voted_selection(idx_gpu, layer_scores, ends, local, top, what):
@@ -97,6 +116,7 @@ def check_voted_selection(idx_gpu, layer_scores, ends, local, top, what):
         assert votes[c] == votes[last] and abs(total[c] - total[last]) <= band, (
             f"{what}: chunk {c} (votes {votes[c]}, sum {total[c]!r}) differs from the rule "
             f"outside the tie band (boundary votes {votes[last]}, sum {total[last]!r})")
+    record("tie_band_diffs", len(cg ^ cr))
     return len(cg ^ cr)
 
 
@@ -114,6 +134,7 @@ def check_decode(out_gpu, q_dec, K, V, idx, scale, dtype, what) -> float:
         ref = oracle.decode_attention(qd[g], Kc, Vc, scale)
         err = max(err, float(np.max(np.abs(out_gpu[g].astype(np.float64) - ref))) if ref.size else 0)
     assert err <= OUT_ATOL[dtype], f"{what}: decode max-abs error {err}"
+    record(f"decode_abs_{dtype}", err)
     return err
 
 
@@ -121,9 +142,14 @@ def check_lmba(k_gpu, P_rows, what, eps=1e-5):
     """GPU per-row LMBA against float64 attention rows: the count must lie in
     the band of counts whose top-k mass reaches 0.9 of the row within a
     relative eps (fp32 rows and fixed-point masses on the GPU)."""
+    off_center = 0
     for r, row in enumerate(np.asarray(P_rows)):
         cum = np.cumsum(np.sort(row)[::-1])
         tot = cum[-1]
         lo = int(np.searchsorted(cum, 0.9 * (1 - eps) * tot)) + 1
         hi = int(np.searchsorted(cum, 0.9 * (1 + eps) * tot)) + 1
         assert lo <= int(k_gpu[r]) <= hi, f"{what} row {r}: lmba {k_gpu[r]} outside [{lo}, {hi}]"
+        exact = int(np.searchsorted(cum, 0.9 * tot)) + 1
+        off_center += int(int(k_gpu[r]) != exact)
+    record("lmba_rows", len(P_rows))
+    record("lmba_off_center", off_center)

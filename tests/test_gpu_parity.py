@@ -1274,7 +1274,8 @@ def test_c2_model_full_sampled(kv):
     Every segment: kept count = its layer's budget, indices strictly ascending
     inside [0, n).  Sampled segments across the layers: scores, selection
     (tie band), compaction (bit-exact) and decode against the oracle; one
-    layer's LMBA rows (float64 band) and kept mass on two of them."""
+    layer's LMBA rows (float64 band) and kept mass on two of them.  Then the
+    whole step runs again over poisoned outputs and must give the same bits."""
     kvsel, pipeline, torch = kv
     cfg = kvsynth.get_config(2)
     _say(cfg.name, "full model, one compression call per phase")
@@ -1330,6 +1331,19 @@ def test_c2_model_full_sampled(kv):
         g = l * S + s
         kept = idx[off[g]:off[g] + lens[l, s]].astype(np.int64)
         assert np.max(np.abs(kmh[s] - P[:, kept].sum(axis=1))) <= 1e-5
+    # determinism at full size: the whole model's score, select, compact and
+    # per-layer decode run a second time give the same bits everywhere
+    first = {k: getattr(mr, k).clone() for k in ("scores", "seg_len", "idx", "k_c", "v_c", "out")}
+    for t in (mr.scores, mr.idx, mr.k_c, mr.v_c, mr.out):
+        t.view(torch.uint8).fill_(0xA5)
+    mr.score(); mr.select(); mr.compact()
+    for l in range(L):
+        mr.decode(l)
+    torch.cuda.synchronize()
+    for k, t in first.items():
+        assert torch.equal(getattr(mr, k).view(torch.uint8), t.view(torch.uint8)), k
+    print(f"  {cfg.name}: second full-model run bit-identical (scores, selection, compacted "
+          f"K/V, decode outputs)", flush=True)
 
 
 def test_graph_replays_lmba_vote_rope(kv):
