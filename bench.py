@@ -151,6 +151,49 @@ def serving_loop_us(torch, pipeline, kvsynth, cfg, budgets, layers: int = 4,
     return us
 
 
+def model_serving_loop_us(torch, pipeline, kvsynth, cfg, budgets, layers: int = 4,
+                          graphs: int = 4) -> float:
+    """The same decode-time loop on `layers` C2 layers with every layer's
+    re-selection batched (pipeline.ModelServingLoop: one score, one select
+    and one compact call over all layers' segments every w steps).  Each graph
+    holds w steps of every layer; the first is a warm-up.  Returns µs per
+    layer per step."""
+    W = cfg.w
+    ins = [kvsynth.layer_inputs(cfg, l) for l in range(layers)]
+    k = torch.cat([pipeline.device_tensor(x["K"]) for x in ins])
+    v = torch.cat([pipeline.device_tensor(x["V"]) for x in ins])
+    q_win = torch.cat([pipeline.device_tensor(x["q_win"]) for x in ins])
+    del ins
+    mc = kvsynth.get_config(cfg.cid, layers=layers)
+    ml = pipeline.ModelServingLoop.start(mc, budgets[:layers], k, v, q_win, graphs * W)
+    del k, v, q_win
+    toks = [kvsynth.step_inputs(cfg, 0, t) for t in range(W)]
+    dev = [tuple(pipeline.device_tensor(tk[name]) for name in ("k_new", "v_new", "q"))
+           for tk in toks]
+    gs = []
+    for _ in range(graphs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for t in range(W):
+                for l in range(layers):
+                    ml.step_layer(l, *dev[t])
+                ml.end_step()
+        gs.append(g)
+    assert ml.reselections == graphs
+    torch.cuda.synchronize()
+    gs[0].replay()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    for g in gs[1:]:
+        g.replay()
+    e[1].record()
+    torch.cuda.synchronize()
+    us = e[0].elapsed_time(e[1]) * 1e3 / ((graphs - 1) * W) / layers
+    del gs, ml
+    return us
+
+
 def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
     """HBM bytes per decode launch from two rocprofv3 --pmc runs of this
     script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by the
@@ -490,9 +533,12 @@ def main() -> int:
     # compaction left dirty in the caches are written back while it reads;
     # here the first (untimed) replay has already paid for them
     dec_alone_us = timed(phases["decode"], reps=4)
-    serve_us = serving_loop_us(torch, pipeline, kvsynth, cfg, budgets)
-    log(f"[bench] serving loop: {serve_us:.1f} us per layer per step "
-        f"(re-selection every {cfg.w} steps, 4 layers)")
+    serve_layer_us = serving_loop_us(torch, pipeline, kvsynth, cfg, budgets)
+    torch.cuda.empty_cache()
+    serve_us = model_serving_loop_us(torch, pipeline, kvsynth, cfg, budgets)
+    log(f"[bench] serving loop: {serve_us:.1f} us per layer per step with the 4 layers' "
+        f"re-selection batched, {serve_layer_us:.1f} with one loop per layer (re-selection "
+        f"every {cfg.w} steps)")
 
     es, d, hq, hkv, n = cfg.es, cfg.d, cfg.hq, cfg.hkv, cfg.n
     lens = pu_host(mr.seg_len).reshape(L, S)
@@ -598,10 +644,14 @@ def main() -> int:
                                "dirty in the caches"},
                    "serving_loop_c2": {
                        "us_per_layer_step": round(serve_us, 2),
-                       "note": "pipeline.ServingLoop on 4 C2 layers: every step appends the new "
-                               "token to the full and the compacted cache and decodes; every 32 "
-                               "steps score, select and compact are redone over the resident "
-                               "full cache (HIP graphs of 32 steps), outside the timed step"},
+                       "us_per_layer_step_one_loop_per_layer": round(serve_layer_us, 2),
+                       "note": "pipeline.ModelServingLoop on 4 C2 layers: every step appends "
+                               "the new token to each layer's full and compacted cache and "
+                               "decodes it, layer by layer; every 32 steps score, select and "
+                               "compact are redone over the resident full caches, one call "
+                               "each for all 4 layers (HIP graphs of 32 steps); beside it the "
+                               "same loop as one pipeline.ServingLoop per layer; outside the "
+                               "timed step"},
                    "layer_lmba_mean_tokens": [round(x, 1) for x in layer_lmba],
                    "attention_loss_topb_per_layer": [round(x, 5) for x in att_loss]},
         "decode_frac_of_copy_reference": round(dec_gbs / copy_gbs, 4),

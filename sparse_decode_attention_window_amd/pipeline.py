@@ -532,3 +532,136 @@ class ModelRun:
         r = self._rows(l)
         K.kvsel_append(self.layer_shape, k_new, v_new, pos, self.seg_off[r], self.seg_cap[r],
                        limit, self.seg_len[r], self.idx, self.k_c, self.v_c, self.r_cap, stream)
+
+
+@dataclass
+class ModelServingLoop:
+    """ServingLoop for every layer of a top-B model at once (the same reading of
+    ZigZagkv Eq. 7 and FastGen's rules as ServingLoop).  Each step runs layer
+    by layer, as a model does: the new token joins layer l's full and
+    compacted caches and layer l decodes.  Every `period` steps the
+    re-selection of all layers is one score, one select and one compact call
+    over the L*b*hkv segments (the layout of ModelRun), so it fills the chip
+    where one layer's b*hkv segments do not.  Same kernels and data as one
+    ServingLoop per layer, so the same bits."""
+    L: int
+    B: int
+    S: int
+    n0: int
+    period: int
+    layer_shape: K.Shape = None      # one layer, compacted cache
+    full_layer_shape: K.Shape = None  # one layer, full cache (n = capacity)
+    full_shape: K.Shape = None       # every layer's full cache (batch L*b)
+    k_full: object = None            # [L*b][hkv][n_cap][d]
+    v_full: object = None
+    full_off: object = None
+    full_cap: object = None
+    full_len: object = None
+    full_idx: object = None
+    q_buf: object = None             # [L*b][hq][w][d]
+    params: K.SelectParams = None
+    budget: object = None
+    seg_off: object = None           # [L*S] absolute rows of the packed cache
+    seg_cap: object = None
+    seg_len: object = None
+    idx: object = None
+    k_c: object = None
+    v_c: object = None
+    r_cap: int = 0
+    base: list = field(default_factory=list)
+    r_caps: list = field(default_factory=list)
+    seg_off_rel: list = field(default_factory=list)
+    scores: object = None
+    ws_score: object = None
+    ws_dec: object = None
+    out: object = None               # [L][b][hq][d]
+    t: int = 0
+    reselections: int = 0
+
+    @staticmethod
+    def start(cfg, budgets, k, v, q_win, steps: int, device="cuda") -> "ModelServingLoop":
+        """k, v [L*b][hkv][n0][d], q_win [L*b][hq][w][d] (the prompt's last w
+        queries of every layer); room for `steps` decoded tokens.  The first
+        selection of every layer is made here from q_win."""
+        import torch
+        L, B, hq, hkv, d, w = cfg.layers, cfg.batch, cfg.hq, cfg.hkv, cfg.d, cfg.w
+        n0 = k.shape[2]
+        S = B * hkv
+        n_cap = n0 + steps
+        kf = torch.zeros((L * B, hkv, n_cap, d), dtype=k.dtype, device=device)
+        vf = torch.zeros_like(kf)
+        kf[:, :, :n0] = k
+        vf[:, :, :n0] = v
+        lp = ModelServingLoop(L, B, S, n0, w)
+        lp.layer_shape = K.make_shape(B, hq, hkv, d, n_cap, cfg.dtype, cfg.scale)
+        lp.full_layer_shape = lp.layer_shape
+        lp.full_shape = K.make_shape(L * B, hq, hkv, d, n_cap, cfg.dtype, cfg.scale)
+        lp.k_full, lp.v_full = kf, vf
+        lp.full_off = device_tensor(np.arange(L * S, dtype=np.int64) * n_cap, device)
+        lp.full_cap = device_tensor(np.full(L * S, n_cap, np.int64), device)
+        lp.full_len = device_tensor(np.full(L * S, n0, np.int32), device)
+        lp.full_idx = device_tensor(np.tile(np.arange(n_cap, dtype=np.int32), L * S), device)
+        lp.q_buf = q_win.clone()
+        bud = np.repeat(np.asarray(budgets, np.int32), S)
+        cap = capacities(K.KVSEL_SEL_TOPB, L * B, hkv, n_cap, budget=bud) + w
+        off, r_cap = offsets(cap)
+        lp.base = [int(off[l * S]) for l in range(L)]
+        lp.r_caps = [int(cap[l * S:(l + 1) * S].sum()) for l in range(L)]
+        lp.seg_off_rel = [device_tensor(off[l * S:(l + 1) * S] - lp.base[l], device)
+                          for l in range(L)]
+        lp.budget = device_tensor(bud, device)
+        lp.params = K.select_params(K.KVSEL_SEL_TOPB, budget=lp.budget)
+        lp.seg_off = device_tensor(off, device)
+        lp.seg_cap = device_tensor(cap.astype(np.int64), device)
+        lp.r_cap = r_cap
+        lp.seg_len = torch.empty(L * S, dtype=torch.int32, device=device)
+        lp.idx = torch.empty(max(r_cap, 1), dtype=torch.int32, device=device)
+        lp.k_c = torch.empty((max(r_cap, 1), d), dtype=k.dtype, device=device)
+        lp.v_c = torch.empty_like(lp.k_c)
+        lp.scores = torch.empty(L * S * n_cap, dtype=torch.float32, device=device)
+        lp.ws_score = torch.empty(max(K.kvsel_score_workspace(lp.full_shape, w), 1),
+                                  dtype=torch.uint8, device=device)
+        nb = max(K.kvsel_decode_workspace(lp.layer_shape, rc) for rc in lp.r_caps)
+        lp.ws_dec = torch.zeros(max(nb, 1), dtype=torch.uint8, device=device)
+        lp.out = torch.empty((L, B, hq, d), dtype=torch.float32, device=device)
+        lp.reselect(n0 - w)
+        lp.reselections = 0
+        return lp
+
+    def reselect(self, q_pos0: int, stream=None):
+        """Score every layer's keys from its window buffer, select and compact:
+        one call each for all L*b*hkv segments."""
+        K.kvsel_score(self.full_shape, self.period, q_pos0, self.q_buf, self.k_full,
+                      self.scores, self.ws_score, stream)
+        K.kvsel_select(self.full_shape, self.params, self.scores, self.seg_off, self.seg_len,
+                       self.idx, self.r_cap, stream)
+        K.kvsel_compact(self.full_shape, self.k_full, self.v_full, self.seg_off, self.seg_len,
+                        self.idx, self.k_c, self.v_c, self.r_cap, stream)
+        self.reselections += 1
+
+    def step_layer(self, l: int, k_new, v_new, q, stream=None):
+        """Layer l of the decode step at position n0 + t: k_new, v_new
+        [b][hkv][d], q [b][hq][d]."""
+        sh = self.layer_shape
+        S, B, d = self.S, self.B, sh.head_dim
+        pos = self.n0 + self.t
+        r = slice(l * S, (l + 1) * S)
+        K.kvsel_append(sh, k_new, v_new, pos, self.full_off[r], self.full_cap[r], None,
+                       self.full_len[r], self.full_idx, self.k_full.view(-1, d),
+                       self.v_full.view(-1, d), self.full_len.numel() * sh.n, stream)
+        K.kvsel_append(sh, k_new, v_new, pos, self.seg_off[r], self.seg_cap[r], None,
+                       self.seg_len[r], self.idx, self.k_c, self.v_c, self.r_cap, stream)
+        self.q_buf[l * B:(l + 1) * B, :, self.t % self.period].copy_(q.view(B, sh.hq, d))
+        b0 = self.base[l]
+        K.kvsel_decode_attn(sh, q, self.k_c[b0:], self.v_c[b0:], self.seg_off_rel[l],
+                            self.seg_len[r], self.r_caps[l], self.out[l], self.ws_dec, stream)
+
+    def end_step(self, stream=None) -> bool:
+        """After every layer's step_layer: advance; every `period` steps redo
+        every layer's selection.  Returns True when it did."""
+        pos = self.n0 + self.t
+        self.t += 1
+        if self.t % self.period:
+            return False
+        self.reselect(pos - self.period + 1, stream)
+        return True

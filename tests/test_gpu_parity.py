@@ -1019,6 +1019,70 @@ def test_serving_loop_periodic_reselection(kv, cid, over, steps):
           flush=True)
 
 
+def test_model_serving_loop_matches_layer_loops(kv):
+    """The serving loop for three layers at once (re-selection of every layer
+    in one score, one select and one compact call) gives, step by step, the
+    same bits as one ServingLoop per layer (checked against the oracle in
+    test_serving_loop_periodic_reselection): decode outputs every step, and
+    at each re-selection the scores, kept rows and compacted K/V of every
+    segment."""
+    kvsel, pipeline, torch = kv
+    cfg = kvsynth.get_config(2, n=3000, layers=3, batch=2)
+    L, S, w, n = cfg.layers, cfg.batch * cfg.hkv, cfg.w, cfg.n
+    steps = 2 * w + 5
+    _say(cfg.name, "model serving loop, layers", L, "n", n, "steps", steps)
+    budgets = kvsel.kvsel_zigzag_budgets(kvsynth.zigzag_profile(cfg), n, 600, 150)
+    ins = [kvsynth.layer_inputs(cfg, l) for l in range(L)]
+    loops = []
+    for l in range(L):
+        run = pipeline.build_layer(cfg, ins[l], budget=budgets[l], slack=w)
+        run.score(); run.select(); run.compact()
+        loops.append(pipeline.ServingLoop.start(run, run.k, run.v, n, steps))
+    dt = lambda a: pipeline.device_tensor(a)
+    k = torch.cat([dt(x["K"]) for x in ins])
+    v = torch.cat([dt(x["V"]) for x in ins])
+    q_win = torch.cat([dt(x["q_win"]) for x in ins])
+    ml = pipeline.ModelServingLoop.start(cfg, budgets, k, v, q_win, steps)
+    torch.cuda.synchronize()
+
+    def same(a, b, what):
+        assert np.array_equal(pu.to_host(a).view(np.uint8), pu.to_host(b).view(np.uint8)), what
+
+    def same_selection(t):
+        for l in range(L):
+            run = loops[l].run
+            r = slice(l * S, (l + 1) * S)
+            same(ml.seg_len[r], run.seg_len, f"t={t} layer {l} seg_len")
+            off_m, off_l = pu.to_host(ml.seg_off[r]), pu.to_host(run.seg_off)
+            lens = pu.to_host(run.seg_len)
+            for s in range(S):
+                a, b, ln = int(off_m[s]), int(off_l[s]), int(lens[s])
+                what = f"t={t} layer {l} seg {s}"
+                same(ml.idx[a:a + ln], run.idx[b:b + ln], what + " idx")
+                same(ml.k_c[a:a + ln], run.k_c[b:b + ln], what + " k_c")
+                same(ml.v_c[a:a + ln], run.v_c[b:b + ln], what + " v_c")
+    same_selection(-1)
+    for t in range(steps):
+        for l in range(L):
+            st = kvsynth.step_inputs(cfg, l, t)
+            kn, vn, q = dt(st["k_new"]), dt(st["v_new"]), dt(st["q"])
+            loops[l].step(kn, vn, q)
+            ml.step_layer(l, kn, vn, q)
+        redone = ml.end_step()
+        torch.cuda.synchronize()
+        for l in range(L):
+            same(ml.out[l], loops[l].run.out, f"t={t} layer {l} decode")
+        if redone:
+            for l in range(L):
+                nc = ml.full_shape.n
+                same(ml.scores[l * S * nc:(l + 1) * S * nc], loops[l].run.scores,
+                     f"t={t} layer {l} scores")
+            same_selection(t)
+    assert ml.reselections == steps // w and all(lp.reselections == steps // w for lp in loops)
+    print(f"  {cfg.name}: {L} layers, {steps} steps, {ml.reselections} batched re-selections "
+          f"identical to per-layer loops", flush=True)
+
+
 def test_chunk_serving_loop_reselects_at_boundaries(kv):
     """ChunkLLM decode loop on a reduced C4 layer (§2.3, ICAC): 4 local chunks
     + the 16 best others; the selection is redone only at the steps whose token
