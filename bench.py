@@ -232,7 +232,138 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
                         "bytes_per_launch": launch_kib * 1024 * factor}
         per_launch += launch_kib * 1024 * factor
     out["hbm_bytes_per_launch"] = int(per_launch)
+    out["_table"] = traffic_table(fetch_csv, write_csv,
+                                  {k: out[k]["scale_factor"] for k in ("FETCH_SIZE", "WRITE_SIZE")})
     return out
+
+
+def _kernel_key(name: str, grid: str) -> str:
+    import re
+    m = re.search(r"\(anonymous namespace\)::(\w+)(<[^()]*>)?", name)
+    short = (m.group(1) + (m.group(2) or "")) if m else name[:40]
+    return f"`{short}` (grid {grid})"
+
+
+def _dispatches(path: str):
+    """Per-dispatch counter values of a rocprofv3 --pmc CSV: [(kernel key,
+    kernel name, {counter: value})] in dispatch order (values summed over
+    the counter's instances)."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = out.setdefault(int(r["Dispatch_Id"]), [_kernel_key(r["Kernel_Name"],
+                                                                   r.get("Grid_Size", "?")),
+                                                      r["Kernel_Name"], {}])
+            d[2][r["Counter_Name"]] = d[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [tuple(out[k]) for k in sorted(out)]
+
+
+def traffic_table(fetch_csv: str, write_csv: str, factors: dict) -> str:
+    """Markdown table: mean FETCH / WRITE MB per dispatch of every library
+    kernel, separately for the C2 step (before the first LMBA dispatch) and
+    for the extras measured after it."""
+    import re
+    rows = {}
+    lmba_kernels = ("lmba_row_kernel", "keep_mask_kernel", "score_stats_kernel<",
+                    "score_final_kernel<")
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        ds = _dispatches(path)
+        # the extras open with the LMBA calls (attention rows, masks, row selects)
+        end = next((i for i, d in enumerate(ds) if any(k in d[1] for k in lmba_kernels)),
+                   len(ds))
+        for i, (key, name, c) in enumerate(ds):
+            if "kvsel" not in name and "probe" not in name:
+                continue
+            phase = "C2 step" if i < end else "after"
+            if phase == "C2 step":   # per-layer launches differ only in grid size
+                key = re.sub(r" \(grid \d+\)$", "", key)
+            r = rows.setdefault((phase, key), {"n": 0})
+            r[counter] = r.get(counter, 0.0) + c[counter] * 1024 * factors[counter] / 1e6
+            if counter == "FETCH_SIZE":
+                r["n"] += 1
+    lines = ["| phase | kernel | dispatches | fetch MB | write MB |", "|---|---|---|---|---|"]
+    for (phase, key), r in sorted(rows.items(), key=lambda kv: (kv[0][0] != "C2 step", kv[0][1])):
+        n = max(r["n"], 1)
+        lines.append(f"| {phase} | {key} | {r['n']} | {r.get('FETCH_SIZE', 0) / n:.2f} | "
+                     f"{r.get('WRITE_SIZE', 0) / n:.2f} |")
+    return "\n".join(lines)
+
+
+def sq_table(path: str) -> str:
+    """Markdown table from one rocprofv3 --pmc pass of SQ counters (with
+    GRBM_GUI_ACTIVE): per library kernel, the launch's cycles, the waves
+    resident per SIMD, the share of cycles the matrix cores are busy, the VALU
+    issues, both at once, and instructions per wave.  Instance sums are
+    divided by the 8 XCDs (cycles) and the 1024 SIMDs (per-SIMD shares);
+    SQ_WAVE_CYCLES and SQ_ACTIVE_INST_VALU count in units of four cycles."""
+    agg = {}
+    for key, name, c in _dispatches(path):
+        if "kvsel" not in name:
+            continue
+        a = agg.setdefault(key, {"n": 0})
+        a["n"] += 1
+        for k, v in c.items():
+            a[k] = a.get(k, 0.0) + v
+    lines = ["| kernel | dispatches | cycles per dispatch | waves per SIMD | MFMA busy | "
+             "VALU issuing | both | VALU insts per wave | MFMA insts per wave |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for key, a in agg.items():
+        n = a["n"]
+        cyc = a.get("GRBM_GUI_ACTIVE", 0.0) / n / 8
+        simd = max(cyc, 1.0) * 1024
+        waves = max(a.get("SQ_WAVES", 0.0) / n, 1.0)
+        lines.append(
+            f"| {key} | {n} | {cyc:.0f} | {4 * a.get('SQ_WAVE_CYCLES', 0) / n / simd:.2f} | "
+            f"{a.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / n / simd:.2f} | "
+            f"{4 * a.get('SQ_ACTIVE_INST_VALU', 0) / n / simd:.2f} | "
+            f"{a.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0) / n / simd:.2f} | "
+            f"{a.get('SQ_INSTS_VALU', 0) / n / waves:.0f} | {a.get('SQ_INSTS_MFMA', 0) / n / waves:.0f} |")
+    return "\n".join(lines)
+
+
+def trace_tables(trace_csv: str, layers: int = 32) -> str:
+    """Markdown tables from a rocprofv3 --kernel-trace CSV of this script:
+    every library kernel over the whole run (dispatches, mean / min / max µs),
+    then the C2 step alone -- the dispatches before the first LMBA call, of
+    which the last replay of each phase's graph is averaged (the step runs
+    score, select and compact once for all layers and decode once per layer)."""
+    import csv
+    import re
+    ds = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            m = re.search(r"\(anonymous namespace\)::(\w+)(<[^()]*>)?", r["Kernel_Name"])
+            if not m or ("kvsel" not in r["Kernel_Name"] and "probe" not in r["Kernel_Name"]):
+                continue
+            ds.append((int(r["Start_Timestamp"]), m.group(1) + (m.group(2) or ""),
+                       (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    ds.sort()
+    agg = {}
+    for _, k, us in ds:
+        agg.setdefault(k, []).append(us)
+    out = ["| kernel | dispatches | mean µs | min µs | max µs |", "|---|---|---|---|---|"]
+    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{k}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    lmba = ("lmba_row_kernel", "keep_mask_kernel", "score_stats_kernel<", "score_final_kernel<")
+    end = next((i for i, d in enumerate(ds) if any(d[1].startswith(x) for x in lmba)), len(ds))
+    step = ds[:end]
+    out += ["", "C2 step, last graph replay of each phase (µs per dispatch; per layer for the "
+            "calls that cover all layers):", "",
+            "| kernel | dispatches in the replay | µs per dispatch | µs per layer |",
+            "|---|---|---|---|"]
+    last = {}
+    for k in dict.fromkeys(d[1] for d in step):
+        us = [d[2] for d in step if d[1] == k]
+        per_step = layers if k.startswith("decode") else 1
+        rep = us[-per_step:]
+        mean = sum(rep) / len(rep)
+        per_layer = mean if per_step == layers else mean / layers
+        last[k] = per_layer
+        out.append(f"| `{k}` | {len(rep)} | {mean:.2f} | {per_layer:.2f} |")
+    dec = sum(v for k, v in last.items() if k.startswith("decode"))
+    out += ["", f"Decode launch (split + combine) in the last replay: {dec:.2f} µs per layer."]
+    return "\n".join(out)
 
 
 def pu_host(t):
@@ -306,14 +437,27 @@ def main() -> int:
     ap.add_argument("--no-layerwise", action="store_true",
                     help="skip the one-call-per-layer comparison of the compression step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
+                    help="print kernel-time tables from a rocprofv3 --kernel-trace CSV and exit")
+    ap.add_argument("--summarize-sq", metavar="PMC_CSV",
+                    help="print a table of SQ counters per library kernel from one "
+                         "rocprofv3 --pmc pass and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the decode traffic file from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
     if args.summarize_counters:
         res = summarize_counters(*args.summarize_counters)
+        table = res.pop("_table")
         with open(COUNTERS, "w") as f:
             json.dump(res, f, indent=1)
         print(json.dumps(res, indent=1))
+        print(table)
+        return 0
+    if args.summarize_sq:
+        print(sq_table(args.summarize_sq))
+        return 0
+    if args.summarize_trace:
+        print(trace_tables(args.summarize_trace))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

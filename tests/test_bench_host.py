@@ -55,6 +55,33 @@ def test_summarize_counters_calibrates_and_keeps_c2_dispatches(tmp_path):
     want = (200.0 + 20.0) * 1024 * 2.0 + (6.0 + 2.0) * 1024 * 1.0
     assert res["hbm_bytes_per_launch"] == int(want)
     assert res["source_sha256_16"] == bench.src_hash(bench.DECODE_SRCS)
+    # the per-kernel table: the C2 step's split dispatches (mean of 100 and 300
+    # KiB, doubled, in MB) and those after the first LMBA dispatch apart
+    table = res["_table"].splitlines()
+    c2 = [ln for ln in table if ln.startswith("| C2 step") and "decode_split" in ln]
+    assert len(c2) == 1 and f"| 2 | {400.0 * 1024 / 1e6:.2f} | {6.0 * 1024 / 1e6:.2f} |" in c2[0]
+    assert any(ln.startswith("| after") and "decode_split" in ln for ln in table)
+
+
+def test_sq_table_per_kernel_shares(tmp_path):
+    """One dispatch of 1000 cycles per XCD on 1024 SIMDs: 2 resident waves per
+    SIMD, matrix cores busy half the cycles, VALU issuing a quarter."""
+    p = tmp_path / "sq.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size",
+                                          "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        name = "void kvsel::(anonymous namespace)::score_stats_reg_kernel<kvsel::bf16_t, 128, 4>(x)"
+        vals = {"GRBM_GUI_ACTIVE": 8000.0, "SQ_WAVE_CYCLES": 2 * 1000 * 1024 / 4,
+                "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * 1000 * 1024,
+                "SQ_ACTIVE_INST_VALU": 0.25 * 1000 * 1024 / 4, "SQ_WAVES": 2048.0,
+                "SQ_INSTS_VALU": 2048.0 * 300, "SQ_INSTS_MFMA": 2048.0 * 32}
+        for k, v in vals.items():
+            w.writerow({"Dispatch_Id": 7, "Kernel_Name": name, "Grid_Size": 131072,
+                        "Counter_Name": k, "Counter_Value": v})
+    row = bench.sq_table(str(p)).splitlines()[2]
+    assert "score_stats_reg_kernel<kvsel::bf16_t, 128, 4>" in row
+    assert "| 1 | 1000 | 2.00 | 0.50 | 0.25 | 0.00 | 300 | 32 |" in row
 
 
 def test_more_than_one_gpu_is_refused():
