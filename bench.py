@@ -256,6 +256,8 @@ def _dispatches(path: str):
                                                                    r.get("Grid_Size", "?")),
                                                       r["Kernel_Name"], {}])
             d[2][r["Counter_Name"]] = d[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if "Start_Timestamp" in r:
+                d[2]["_dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
     return [tuple(out[k]) for k in sorted(out)]
 
 
@@ -296,7 +298,10 @@ def sq_table(path: str) -> str:
     resident per SIMD, the share of cycles the matrix cores are busy, the VALU
     issues, both at once, and instructions per wave.  Instance sums are
     divided by the 8 XCDs (cycles) and the 1024 SIMDs (per-SIMD shares);
-    SQ_WAVE_CYCLES and SQ_ACTIVE_INST_VALU count in units of four cycles."""
+    SQ_WAVE_CYCLES and SQ_ACTIVE_INST_VALU count in units of four cycles.  The
+    clock column is the launch's cycles over its duration; for dispatches of a
+    few microseconds the counter window is wider than the kernel and it reads
+    high."""
     agg = {}
     for key, name, c in _dispatches(path):
         if "kvsel" not in name:
@@ -305,16 +310,20 @@ def sq_table(path: str) -> str:
         a["n"] += 1
         for k, v in c.items():
             a[k] = a.get(k, 0.0) + v
-    lines = ["| kernel | dispatches | cycles per dispatch | waves per SIMD | MFMA busy | "
-             "VALU issuing | both | VALU insts per wave | MFMA insts per wave |",
-             "|---|---|---|---|---|---|---|---|---|"]
+    lines = ["| kernel | dispatches | cycles per dispatch | µs per dispatch | clock GHz | "
+             "waves per SIMD | MFMA busy | VALU issuing | both | VALU insts per wave | "
+             "MFMA insts per wave |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for key, a in agg.items():
         n = a["n"]
         cyc = a.get("GRBM_GUI_ACTIVE", 0.0) / n / 8
         simd = max(cyc, 1.0) * 1024
         waves = max(a.get("SQ_WAVES", 0.0) / n, 1.0)
+        dur = a.get("_dur_us", 0.0) / n
+        ghz = f"{cyc / dur / 1e3:.2f}" if dur > 0 else "?"
         lines.append(
-            f"| {key} | {n} | {cyc:.0f} | {4 * a.get('SQ_WAVE_CYCLES', 0) / n / simd:.2f} | "
+            f"| {key} | {n} | {cyc:.0f} | {dur:.1f} | {ghz} | "
+            f"{4 * a.get('SQ_WAVE_CYCLES', 0) / n / simd:.2f} | "
             f"{a.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / n / simd:.2f} | "
             f"{4 * a.get('SQ_ACTIVE_INST_VALU', 0) / n / simd:.2f} | "
             f"{a.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0) / n / simd:.2f} | "
