@@ -64,12 +64,14 @@ def test_summarize_counters_calibrates_and_keeps_c2_dispatches(tmp_path):
 
 
 def test_sq_table_per_kernel_shares(tmp_path):
-    """One dispatch of 1000 cycles per XCD on 1024 SIMDs: 2 resident waves per
-    SIMD, matrix cores busy half the cycles, VALU issuing a quarter."""
+    """One dispatch of 1000 cycles per XCD in 0.5 us (2 GHz) on 1024 SIMDs: 2
+    resident waves per SIMD, matrix cores busy half the cycles, VALU issuing a
+    quarter."""
     p = tmp_path / "sq.csv"
     with open(p, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size",
-                                          "Counter_Name", "Counter_Value"])
+                                          "Counter_Name", "Counter_Value",
+                                          "Start_Timestamp", "End_Timestamp"])
         w.writeheader()
         name = "void kvsel::(anonymous namespace)::score_stats_reg_kernel<kvsel::bf16_t, 128, 4>(x)"
         vals = {"GRBM_GUI_ACTIVE": 8000.0, "SQ_WAVE_CYCLES": 2 * 1000 * 1024 / 4,
@@ -78,10 +80,11 @@ def test_sq_table_per_kernel_shares(tmp_path):
                 "SQ_INSTS_VALU": 2048.0 * 300, "SQ_INSTS_MFMA": 2048.0 * 32}
         for k, v in vals.items():
             w.writerow({"Dispatch_Id": 7, "Kernel_Name": name, "Grid_Size": 131072,
-                        "Counter_Name": k, "Counter_Value": v})
+                        "Counter_Name": k, "Counter_Value": v,
+                        "Start_Timestamp": 1000, "End_Timestamp": 1500})
     row = bench.sq_table(str(p)).splitlines()[2]
     assert "score_stats_reg_kernel<kvsel::bf16_t, 128, 4>" in row
-    assert "| 1 | 1000 | 2.00 | 0.50 | 0.25 | 0.00 | 300 | 32 |" in row
+    assert "| 1 | 1000 | 0.5 | 2.00 | 2.00 | 0.50 | 0.25 | 0.00 | 300 | 32 |" in row
 
 
 def test_more_than_one_gpu_is_refused():
