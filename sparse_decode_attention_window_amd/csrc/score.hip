@@ -357,15 +357,29 @@ __global__ __launch_bounds__(kThreads) void score_final_kernel(
 // (two per SIMD) several times over.  The largest power of two in [512, 4096]
 // that still gives four rounds of wavefronts (C2 bench, 32 layers in one call,
 // per layer: 111.7 us at 512, 105.1 at 1024, 101.9 at 2048, 99.2 at 4096,
-// 100.1 at 8192; a single 32-segment layer fills one round at 512).
-int reg_keys_per_wave(int S, int64_t n) {
-  const int64_t slots = (int64_t)device_info().cus * 4 * 2;
+// 100.1 at 8192; a single 32-segment layer fills one round at 512).  A call
+// too small for one round at 512 (a short layer, chunk keys) goes down to one
+// key per query row (32 to 128 keys) to spread its latency over the chip.  It
+// depends only on the call's shape (256 CUs) so that the workspace query can
+// size the statistics for it.
+int reg_keys_per_wave(int S, int64_t n, int rp) {
+  constexpr int64_t kSlots = 256 * 4 * 2;
+  auto waves = [&](int k) { return (int64_t)S * ((n + k - 1) / k); };
   int kpw = 4096;
-  while (kpw > 512 && (int64_t)S * ((n + kpw - 1) / kpw) < 4 * slots) kpw /= 2;
+  while (kpw > 512 && waves(kpw) < 4 * kSlots) kpw /= 2;
+  while (kpw > 32 && kpw > rp && waves(kpw) < kSlots) kpw /= 2;
   return kpw;
 }
-constexpr int kValuPerMfma = 8;       // VALU instructions scheduled after each MFMA
 
+// Statistics tiles per segment in the workspace: enough for the LDS-staged
+// passes (one per 512 keys) and for the register-resident ones.
+int64_t stat_tiles(int S, int64_t n, int rp) {
+  const int64_t lds = (n + kTileKeys - 1) / kTileKeys;
+  const int k = reg_keys_per_wave(S, n, rp);
+  const int64_t reg = (n + k - 1) / k;
+  return lds > reg ? lds : reg;
+}
+constexpr int kValuPerMfma = 8;       // VALU instructions scheduled after each MFMA
 template <typename T>
 struct MfmaPerStep { static constexpr int value = 1; };     // bf16: one 32x32x16
 template <>
@@ -619,7 +633,7 @@ hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int6
   constexpr bool kRegFits = RBN <= 4 && RBN * Gm::NA <= 32 && (sizeof(T) == 2 || RBN == 1);
   if constexpr (kRegFits && !PROBS) {
     {
-      const int kpw = reg_keys_per_wave(S, n);
+      const int kpw = reg_keys_per_wave(S, n, RBN * 32);
       const int rt = (int)((n + kpw - 1) / kpw);
       const dim3 rgrid(rt, S);
       score_stats_reg_kernel<T, D, RBN><<<rgrid, dim3(64), 0, stream>>>(
@@ -646,7 +660,7 @@ hipError_t run(int batch, int hq, int hkv, int w, int64_t n, int64_t q_pos0, flo
   const int RP = padded_rows(R);
   const int tiles = (int)((n + kTileKeys - 1) / kTileKeys);
   auto* stats = static_cast<float2*>(ws);
-  auto* rowc = reinterpret_cast<float*>(stats + (size_t)S * tiles * RP);
+  auto* rowc = reinterpret_cast<float*>(stats + (size_t)S * stat_tiles(S, n, RP) * RP);
   const float c = scale * kLog2e;
   auto qp = static_cast<const char*>(q_win);
   auto kp = static_cast<const char*>(k);
@@ -674,7 +688,7 @@ hipError_t run(int batch, int hq, int hkv, int w, int64_t n, int64_t q_pos0, flo
 
 size_t score_rope_offset(int S, int64_t n, int rows) {
   const int RP = padded_rows(rows);
-  const int64_t tiles = (n + kTileKeys - 1) / kTileKeys;
+  const int64_t tiles = stat_tiles(S, n, RP);
   const size_t stats = (size_t)S * tiles * RP * sizeof(float2) + (size_t)S * RP * sizeof(float);
   return (stats + 255) & ~(size_t)255;
 }
@@ -682,7 +696,7 @@ size_t score_rope_offset(int S, int64_t n, int rows) {
 size_t score_workspace_bytes(int S, int64_t n, int rows, size_t rope_bytes) {
   if (!rope_bytes) {
     const int RP = padded_rows(rows);
-    const int64_t tiles = (n + kTileKeys - 1) / kTileKeys;
+    const int64_t tiles = stat_tiles(S, n, RP);
     return (size_t)S * tiles * RP * sizeof(float2) + (size_t)S * RP * sizeof(float);
   }
   return score_rope_offset(S, n, rows) + rope_bytes;
