@@ -379,11 +379,54 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
   const int64_t span = ((int64_t)kept_total + parts - 1) / parts;
   const int64_t out_lo = (int64_t)part * span;
   const int64_t out_hi = min((int64_t)kept_total, out_lo + span);
-  // 3) write the kept chunks' token ranges that fall in this part's output
-  // positions.  The 64 chunks of a wavefront (fixed k) are consecutive, so
-  // their kept tokens fill one contiguous run of the output; the wavefront
-  // walks its kept chunks (set bits of a ballot) and writes each chunk's
-  // range with all lanes, coalesced.
+  // 3) write the kept chunks' token positions that fall in this part's output
+  // positions [out_lo, out_hi).
+  if constexpr (2 * KPT * kThreads <= kRReps * kRPitch) {
+    // Every chunk's first output position (dense in index order: a chunk that
+    // is not kept starts where the next kept one does) and first token go to
+    // LDS, in place of the histogram; each thread then finds the chunk of each
+    // of its output positions by binary search, so consecutive threads store
+    // consecutive positions.
+    uint32_t* ostart = hist;
+    uint32_t* otok = hist + KPT * kThreads;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const uint32_t kw = kept_tokens(k);
+      const uint32_t before = wave_incl_scan_u32(kw) - kw;
+      const int j = k * kThreads + tid;
+      ostart[j] = j < N ? blk_b[k * kWaves + wid] + before : 0xffffffffu;
+      otok[j] = first_tok[k];
+    }
+    __syncthreads();
+    // thread t takes a run of consecutive positions: one search for the run's
+    // first position, then a walk forward over the (few) chunk boundaries
+    const int64_t hi = min(out_hi, room);
+    const int64_t run = (out_hi - out_lo + kThreads - 1) / kThreads;
+    const int64_t p0 = out_lo + (int64_t)tid * run;
+    if (p0 >= hi) return;
+    uint32_t pu = (uint32_t)p0;
+    uint32_t lo = 0, len = KPT * kThreads;   // first chunk starting past p0
+    while (len) {
+      const uint32_t half = len >> 1;
+      if (ostart[lo + half] <= pu) {
+        lo += half + 1;
+        len -= half + 1;
+      } else {
+        len = half;
+      }
+    }
+    uint32_t c = lo - 1;   // ostart[0] == 0 <= p0
+    const int64_t p1 = min(hi, p0 + run);
+    for (int64_t p = p0; p < p1; ++p, ++pu) {
+      while (c + 1 < KPT * kThreads && ostart[c + 1] <= pu) ++c;
+      idx[off + p] = (int32_t)(otok[c] + (pu - ostart[c]));
+    }
+    return;
+  }
+  // More chunks than LDS holds: the 64 chunks of a wavefront (fixed k) are
+  // consecutive, so their kept tokens fill one contiguous run of the output;
+  // the wavefront walks its kept chunks (set bits of a ballot) and writes each
+  // chunk's range with all lanes.
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const int blk = k * kWaves + wid;
