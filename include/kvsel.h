@@ -103,7 +103,7 @@ typedef struct kvsel_rope {
  *   batch, hq, hkv : batch size, query heads, KV heads; hq % hkv == 0;
  *                    query head h reads KV head h / G with group size
  *                    G = hq / hkv.  kvsel_score needs G * w <= 256 and
- *                    kvsel_decode_attn G <= 4 (EUNSUPPORTED otherwise);
+ *                    kvsel_decode_attn G <= 8 (EUNSUPPORTED otherwise);
  *                    batch * hkv <= 2048 segments.
  *   head_dim       : 64, 88 or 128 (88 = RAP pair-pruned layout).
  *   n              : cached keys per (batch, KV head); for chunk scoring the

@@ -330,7 +330,7 @@ kvsel_status kvsel_decode_attn(const kvsel_shape* s, const void* q, const void* 
                                hipStream_t stream) {
   g_err[0] = 0;
   int S = 0, G = 0;
-  kvsel_status st = check_shape(s, &S, &G, 4);
+  kvsel_status st = check_shape(s, &S, &G, 8);
   if (st != KVSEL_OK) return st;
   if (!q || !seg_off || !seg_len || !out) return fail(KVSEL_EINVAL, "q, seg_off, seg_len, out must be non-NULL");
   if (r_cap > 0 && (!k_c || !v_c)) return fail(KVSEL_EINVAL, "k_c and v_c must be non-NULL");
@@ -352,7 +352,7 @@ kvsel_status kvsel_decode_attn_noalloc(const kvsel_shape* s, const void* q, cons
                                        hipStream_t stream) {
   g_err[0] = 0;
   int S = 0, G = 0;
-  kvsel_status st = check_shape(s, &S, &G, 4);
+  kvsel_status st = check_shape(s, &S, &G, 8);
   if (st != KVSEL_OK) return st;
   if (!q || !seg_off || !seg_len || !out) return fail(KVSEL_EINVAL, "q, seg_off, seg_len, out must be non-NULL");
   if (r_cap > 0 && (!k_c || !v_c)) return fail(KVSEL_EINVAL, "k_c and v_c must be non-NULL");

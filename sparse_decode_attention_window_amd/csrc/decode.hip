@@ -12,8 +12,9 @@
 // one is computed:
 //   QK^T  on the matrix cores: A = the G query heads of the KV head
 //         replicated over 16 rows, B = 16 keys; every lane ends up with the
-//         logits of one key for all heads.  The tile max is a DPP row
-//         reduction; probabilities reach the value lanes through LDS.
+//         logits of one key for all heads (for G > 4 half of them come from
+//         the lane 16 apart).  The tile max is a DPP row reduction;
+//         probabilities reach the value lanes through LDS.
 //   PV    on the vector ALUs in fp32: lane (slot g, chunk c) owns 16 bytes
 //         of value row 4t+g and accumulates heads x elements.
 // Each item keeps (running max, sum of exponentials, unnormalised output) in
@@ -148,12 +149,31 @@ __device__ __forceinline__ void compute_tile(WaveState<T, D, HG>& st, const Tile
   f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int a = 0; a < Gm::NA; ++a) sacc = qk_step(qf[a], r.k[a], sacc, T{});
+  // accumulator row 4*grp + i holds head (4*grp + i) % HG: up to four heads
+  // every lane has all of them; with eight, lanes of odd slots hold heads
+  // 4..7 and the other four come from the lane 16 apart
+  float lg[HG];
+  if constexpr (HG <= 4) {
+#pragma unroll
+    for (int h = 0; h < HG; ++h) lg[h] = sacc[h];
+  } else {
+    const bool odd = grp & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float o = __shfl_xor(sacc[i], 16);
+      lg[i] = odd ? o : sacc[i];
+      lg[4 + i] = odd ? sacc[i] : o;
+    }
+  }
 
-  float p[4] = {0.f, 0.f, 0.f, 0.f}, alpha[HG];
+  constexpr int NP = HG > 4 ? 8 : 4;
+  float p[NP], alpha[HG];
+#pragma unroll
+  for (int h = 0; h < NP; ++h) p[h] = 0.f;
   bool rescale = false;
 #pragma unroll
   for (int h = 0; h < HG; ++h) {
-    const float x = kok ? sacc[h] * c : -INFINITY;
+    const float x = kok ? lg[h] * c : -INFINITY;
     const float mn = fmaxf(st.m[h], row_max16(x));
     const float ms = mn == -INFINITY ? 0.f : mn;
     alpha[h] = __builtin_amdgcn_exp2f(st.m[h] - ms);
@@ -161,8 +181,14 @@ __device__ __forceinline__ void compute_tile(WaveState<T, D, HG>& st, const Tile
     p[h] = __builtin_amdgcn_exp2f(x - ms);
     st.m[h] = mn;
   }
-  // probabilities of the tile's 16 keys to every lane through LDS (4 heads per key)
-  if (grp == 0) sp[l16] = make_float4(p[0], p[1], p[2], p[3]);
+  // probabilities of the tile's 16 keys to every lane through LDS (4 heads
+  // per float4; with eight heads the second four follow the first 16)
+  if constexpr (HG <= 4) {
+    if (grp == 0) sp[l16] = make_float4(p[0], p[1], p[2], p[3]);
+  } else {
+    if (grp < 2) sp[16 * grp + l16] = make_float4(p[4 * grp], p[4 * grp + 1], p[4 * grp + 2],
+                                                  p[4 * grp + 3]);
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -180,7 +206,14 @@ __device__ __forceinline__ void compute_tile(WaveState<T, D, HG>& st, const Tile
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const float4 pv = sp[4 * t + grp];
-    const float pk[4] = {pv.x, pv.y, pv.z, pv.w};
+    float pk[NP] = {pv.x, pv.y, pv.z, pv.w};
+    if constexpr (HG > 4) {
+      const float4 pw = sp[16 + 4 * t + grp];
+      pk[4] = pw.x;
+      pk[5] = pw.y;
+      pk[6] = pw.z;
+      pk[7] = pw.w;
+    }
 #pragma unroll
     for (int h = 0; h < HG; ++h) st.l[h] += pk[h];
 #pragma unroll
@@ -204,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(
     int S, int hq, int hkv, int G, float c, int rpw, float2* __restrict__ part_ml,
     float* __restrict__ part_o, RopeDev rope, int64_t q_pos) {
   using Gm = Geom<T, D>;
-  __shared__ float4 sp_all[kWaves][kTile];
+  __shared__ float4 sp_all[kWaves][HG > 4 ? 2 * kTile : kTile];
   __shared__ float sm_o[kWaves][HG][D];
   __shared__ float sm_m[kWaves][HG], sm_l[kWaves][HG];
 
@@ -420,7 +453,7 @@ __global__ __launch_bounds__(64) void decode_combine_head_kernel(
   if (mine) *reinterpret_cast<float2*>(o + 2 * lane) = acc;
 }
 
-int hg_for(int G) { return G <= 1 ? 1 : (G <= 2 ? 2 : 4); }
+int hg_for(int G) { return G <= 1 ? 1 : (G <= 2 ? 2 : (G <= 4 ? 4 : 8)); }
 
 // Workgroups of `kernel` that one compute unit holds at once (cached per device).
 template <typename K>
@@ -491,7 +524,8 @@ hipError_t run_d(int batch, int hq, int hkv, float scale, const void* q, const v
   switch (hg_for(hq / hkv)) {
     case 1: KVSEL_HG(1);
     case 2: KVSEL_HG(2);
-    default: KVSEL_HG(4);
+    case 4: KVSEL_HG(4);
+    default: KVSEL_HG(8);
   }
 #undef KVSEL_HG
 }
@@ -509,7 +543,8 @@ size_t noalloc_need_d(int S, int G, int64_t r_cap) {
   switch (hg_for(G)) {
     case 1: return partial_bytes<1, D>(plan_items<T, D, 1>(S, r_cap, &rpw));
     case 2: return partial_bytes<2, D>(plan_items<T, D, 2>(S, r_cap, &rpw));
-    default: return partial_bytes<4, D>(plan_items<T, D, 4>(S, r_cap, &rpw));
+    case 4: return partial_bytes<4, D>(plan_items<T, D, 4>(S, r_cap, &rpw));
+    default: return partial_bytes<8, D>(plan_items<T, D, 8>(S, r_cap, &rpw));
   }
 }
 

@@ -132,9 +132,10 @@ def test_compact_and_decode_reject_bad_args():
     assert need > 0
     assert lib.kvsel_decode_attn(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE,
                                  need - 1, None) == _lib.KVSEL_ENOSPC
-    big_group = shape(hq=16, hkv=2)
+    big_group = shape(hq=32, hkv=2)   # G = 16: decode is built for groups of up to 8
     assert lib.kvsel_decode_attn(ctypes.byref(big_group), FAKE, FAKE, FAKE, FAKE, FAKE, 100, FAKE,
                                  FAKE, 1 << 30, None) == _lib.KVSEL_EUNSUPPORTED
+    assert "exceeds 8" in kvsel.kvsel_last_error()
 
 
 def test_lmba_rejects_bad_args():
@@ -292,6 +293,6 @@ def test_decode_noalloc_rejects_bad_args():
     assert call(out=None) == _lib.KVSEL_EINVAL
     assert call(kc=None) == _lib.KVSEL_EINVAL
     assert call(r_cap=-1) == _lib.KVSEL_EINVAL
-    assert call(s=shape(hq=16, hkv=2)) == _lib.KVSEL_EUNSUPPORTED
+    assert call(s=shape(hq=32, hkv=2)) == _lib.KVSEL_EUNSUPPORTED
     assert call(r_cap=(1 << 31) - 1) == _lib.KVSEL_ENOSPC
     assert "static scratch" in kvsel.kvsel_last_error()

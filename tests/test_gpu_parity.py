@@ -112,6 +112,18 @@ def test_c1_llama_layer_full(kv):
     _check_segments(cfg, inputs, run, range(cfg.batch * cfg.hkv))
 
 
+def test_eight_head_groups_end_to_end(kv):
+    """C1's layer with 64 query heads over 8 KV heads (G = 8: 256 window rows
+    per KV head, the LDS-staged score passes; the decode's largest head
+    group) and a ragged n: score, select, compact and decode of every segment
+    against the oracle."""
+    cfg = kvsynth.get_config(1, hq=64, n=3000 + 37, budget=333)
+    assert cfg.G == 8 and cfg.G * cfg.w == 256
+    _say(cfg.name, "G", cfg.G, "n", cfg.n)
+    inputs, run = _run(kv, cfg)
+    _check_segments(cfg, inputs, run, range(cfg.batch * cfg.hkv))
+
+
 @pytest.mark.parametrize("layer", [0, 9])
 def test_c2_reduced_ragged(kv, layer):
     cfg = kvsynth.get_config(2, batch=2, n=5000 + 77)
@@ -334,7 +346,8 @@ def test_compact_gaps_empty_and_bad_indices(kv):
 
 @pytest.mark.parametrize("dtype,d,G", [("bf16", 128, 4), ("bf16", 88, 4), ("bf16", 64, 2),
                                        ("fp32", 64, 2), ("fp32", 128, 3), ("bf16", 128, 1),
-                                       ("fp32", 88, 4)])
+                                       ("fp32", 88, 4), ("bf16", 128, 8), ("bf16", 88, 6),
+                                       ("fp32", 64, 5), ("fp32", 128, 8), ("bf16", 64, 7)])
 def test_decode_ragged_segments(kv, dtype, d, G):
     kvsel, pipeline, torch = kv
     _say("decode", dtype, d, G)
@@ -863,7 +876,8 @@ def test_rope_score_and_lmba_fused(kv, dtype, d, half, G, w, n):
 
 
 @pytest.mark.parametrize("dtype,d,half,G", [("bf16", 88, 64, 4), ("bf16", 128, 64, 4),
-                                           ("fp32", 88, 64, 2), ("bf16", 64, 64, 1)])
+                                           ("fp32", 88, 64, 2), ("bf16", 64, 64, 1),
+                                           ("bf16", 128, 64, 8)])
 def test_rope_decode_fused(kv, dtype, d, half, G):
     kvsel, pipeline, torch = kv
     _say("rope decode", dtype, d, half, G)
