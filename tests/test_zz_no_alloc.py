@@ -1,8 +1,8 @@
 """kvsel_decode_attn_noalloc against kvsel_decode_attn through the C ABI (needs
 an MI355X): the allocation-free entry point runs the same kernels with its
 partials in the library's static scratch, so its output must equal the
-workspace entry point's bit for bit; two calls in a row, the second smaller,
-show that nothing left in the shared scratch leaks into the next call."""
+workspace entry point's bit for bit; calls in a row, each smaller than the one
+before, show that nothing left in the shared scratch leaks into the next call."""
 import sys
 
 import numpy as np
@@ -33,8 +33,11 @@ def test_decode_noalloc_matches_workspace_entry():
     import sparse_decode_attention_window_amd as kvsel
     assert torch.cuda.is_available()
     kvsel.lib()
-    cases = [kvsynth.get_config(2, batch=2, n=5000 + 77), kvsynth.get_config(0)]
-    for cfg in cases:   # the second call is smaller than the first
+    # each call smaller than the one before; the middle one has eight query heads
+    # per KV head (the decode's largest head group)
+    cases = [kvsynth.get_config(2, batch=2, n=5000 + 77),
+             kvsynth.get_config(1, hq=64, n=3000 + 37, budget=333), kvsynth.get_config(0)]
+    for cfg in cases:
         _say("decode noalloc", cfg.name, "n", cfg.n, "batch", cfg.batch)
         bl = pu.zigzag_layer_budgets(cfg)[3] if cfg.mode == "topb" and cfg.layers > 1 else None
         run = _layer(cfg, budget=bl)
