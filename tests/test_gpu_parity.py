@@ -265,12 +265,16 @@ def test_select_topb_exact_with_ties(kv, n):
         assert np.array_equal(got[s], want), f"row {s}"
 
 
-def test_select_chunk_exact(kv):
+@pytest.mark.parametrize("n,count", [(5000, 600), (120000, 7000), (240000, 14000)])
+def test_select_chunk_exact(kv, n, count):
+    """Crafted chunk selections (ties, all-equal scores, forced local chunks,
+    fixed counts, targets of 0 and past n) at about 250, 6 000 and 12 000
+    chunks: one, eight and sixteen chunks per thread (the gathered write of
+    the kept positions up to 8192 chunks, the per-chunk loop above)."""
     kvsel, pipeline, torch = kv
-    _say("select chunk crafted")
-    r = np.random.default_rng(7)
-    n = 5000
-    lens_c = r.geometric(1 / 20, size=600)
+    _say("select chunk crafted", n, count)
+    r = np.random.default_rng(7 + n)
+    lens_c = r.geometric(1 / 20, size=count)
     ends = np.minimum(np.cumsum(lens_c), n)
     ends = np.unique(ends)
     if ends[-1] != n:
@@ -278,7 +282,7 @@ def test_select_chunk_exact(kv):
     nc = ends.size
     hkv = 3
     cs = np.stack([r.random(nc), r.integers(0, 3, nc), np.full(nc, 1.0)]).astype(np.float32)
-    cases = [(keep, 0, 0) for keep in [1, 777, 2400, n, n + 10, 0]]
+    cases = [(keep, 0, 0) for keep in [1, 777, 2400, n // 2, n, n + 10, 0]]
     cases += [(777, 5, 0), (0, 16, 0), (n, 3, 0), (0, 16, 50), (0, 0, 1), (0, 3, nc), (0, nc + 4, 2)]
     for keep, local, top in cases:
         shape = kvsel.make_shape(1, hkv, hkv, 64, n, "bf16", 1.0)
