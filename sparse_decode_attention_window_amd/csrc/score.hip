@@ -380,6 +380,7 @@ int64_t stat_tiles(int S, int64_t n, int rp) {
   return lds > reg ? lds : reg;
 }
 constexpr int kValuPerMfma = 8;       // VALU instructions scheduled after each MFMA
+
 template <typename T>
 struct MfmaPerStep { static constexpr int value = 1; };     // bf16: one 32x32x16
 template <>

@@ -384,9 +384,8 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(
   if constexpr (2 * KPT * kThreads <= kRReps * kRPitch) {
     // Every chunk's first output position (dense in index order: a chunk that
     // is not kept starts where the next kept one does) and first token go to
-    // LDS, in place of the histogram; each thread then finds the chunk of each
-    // of its output positions by binary search, so consecutive threads store
-    // consecutive positions.
+    // LDS, in place of the histogram; each thread then writes a run of
+    // consecutive output positions, finding their chunks by binary search.
     uint32_t* ostart = hist;
     uint32_t* otok = hist + KPT * kThreads;
 #pragma unroll
