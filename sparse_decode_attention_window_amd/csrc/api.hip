@@ -86,7 +86,7 @@ kvsel_status rope_of(const kvsel_shape* s, int64_t pos_lo, int64_t pos_hi, RopeD
 
 void set_last_error(const char* msg) { snprintf(g_err, sizeof(g_err), "%s", msg); }
 
-const DeviceInfo& device_info() {
+DeviceInfo device_info() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   std::lock_guard<std::mutex> lk(g_dev_mu);

@@ -287,7 +287,7 @@ struct DeviceInfo {
   int cus;
   int max_lds;  // bytes of LDS one workgroup may allocate
 };
-const DeviceInfo& device_info();
+DeviceInfo device_info();   // by value: the per-device table may grow under other threads
 
 hipError_t launch_compact(int dtype, int head_dim, const void* k, const void* v,
                           const int64_t* seg_off, const int32_t* seg_len, const int32_t* idx,
