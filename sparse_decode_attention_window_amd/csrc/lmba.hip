@@ -47,8 +47,13 @@ constexpr uint32_t kKeyHi = 0x3FFFFFFFu;    // just below 2
 constexpr int kSplit = 20;                  // 64-bit scans as two 32-bit scans
 constexpr double kUnfix = 1.0 / 1099511627776.0;
 
+// floor(p * 2^40) for a key in [2^-40, 2), the only keys that are ever
+// binned: the 24-bit significand shifted by the exponent (left by 0..40 bits,
+// then right by 23), in integer steps instead of a float-to-64-bit conversion.
 __device__ __forceinline__ uint64_t fixed_mass(float p) {
-  return (uint64_t)(p * 1099511627776.0f);  // * 2^40 is exact; truncation = floor
+  const uint32_t b = __float_as_uint(p);
+  const uint64_t sig = (b & 0x7FFFFFu) | 0x800000u;
+  return (sig << ((b >> 23) - 87u)) >> 23;
 }
 
 // Inclusive wavefront scan of values below 2^41 (a row's fixed-point mass):

@@ -451,8 +451,19 @@ __global__ __launch_bounds__(64, 2) void score_stats_reg_kernel(
   // the softmax statistics of row block rb, and the scheduler is asked to
   // interleave the two (one MFMA, then VALU work), so the matrix core and
   // the VALU of this wavefront run at once.
-  auto block = [&](const u32x4* kf_, int64_t key0, auto masked_c) {
+  //
+  // The pair (M, L) only has to satisfy L = sum 2^(x - M); M need not be the
+  // maximum.  The exact form (running maximum, rescaled sum) runs on a run's
+  // first block and on masked blocks; every other block sums against the
+  // first block's maximum held fixed (FIXED), which drops the per-logit max
+  // and the per-block rescale.  L >= 2^(max - M), so L < 2^24 bounds the
+  // largest exponent argument by 24 (a relative error of at most about
+  // 1e-6 per term from rounding the argument); a run whose sum reaches 2^24,
+  // overflows or turns NaN is summed again in the exact form.
+  auto block = [&](const u32x4* kf_, int64_t key0, auto masked_c, auto fixed_c) {
     constexpr bool MASKED = decltype(masked_c)::value;
+    constexpr bool FIXED = decltype(fixed_c)::value;
+    static_assert(!(MASKED && FIXED), "masked blocks take the exact form");
     const int kb0 = (int)key0;
     f32x16 acc[2];
     acc[0] = f32x16{};
@@ -468,20 +479,34 @@ __global__ __launch_bounds__(64, 2) void score_stats_reg_kernel(
       }
       f32x16& x = acc[rb & 1];
       // lane owns query row rb*32 + lane%32 and the 16 keys key0 + acc_row(j)
-      float tm = -INFINITY;
-      const int lr = MASKED ? row_lim(rb) : 0;
+      if constexpr (FIXED) {
+        const float ms = Mr[rb];
+        float ps[4];   // four running partials: no stall on each add
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (MASKED && kb0 + acc_row(j, lane) > lr) x[j] = -INFINITY;
-        tm = fmaxf(tm, x[j]);
+        for (int j = 0; j < 4; ++j) ps[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -ms));
+#pragma unroll
+        for (int j = 4; j < 16; ++j)
+          ps[j & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -ms));
+        Lr[rb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      } else {
+        float tm = -INFINITY;
+        const int lr = MASKED ? row_lim(rb) : 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (MASKED && kb0 + acc_row(j, lane) > lr) x[j] = -INFINITY;
+          tm = fmaxf(tm, x[j]);
+        }
+        const float mn = fmaxf(Mr[rb], tm * c);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        float ps[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ps[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -ms));
+#pragma unroll
+        for (int j = 4; j < 16; ++j)
+          ps[j & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -ms));
+        Lr[rb] = Lr[rb] * __builtin_amdgcn_exp2f(Mr[rb] - ms) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+        Mr[rb] = mn;
       }
-      const float mn = fmaxf(Mr[rb], tm * c);
-      const float ms = mn == -INFINITY ? 0.f : mn;
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};   // four running partials: no stall on each add
-#pragma unroll
-      for (int j = 0; j < 16; ++j) ps[j & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -ms));
-      Lr[rb] = Lr[rb] * __builtin_amdgcn_exp2f(Mr[rb] - ms) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
-      Mr[rb] = mn;
       if (rb + 1 < RBN) {
 #pragma unroll
         for (int a = 0; a < Gm::NA * MfmaPerStep<T>::value; ++a) {
@@ -492,22 +517,43 @@ __global__ __launch_bounds__(64, 2) void score_stats_reg_kernel(
     }
   };
   // blocks [0, nfree) need no mask (every key below n and visible to every
-  // row); they run double-buffered, the few masked ones after them
+  // row); they run double-buffered, the first in the exact form and the rest
+  // against its maximum, the few masked ones after them in the exact form
   const int nfree = free_blocks(kb, nblk, n, q_pos0);
   __builtin_amdgcn_sched_barrier(0);
-  for (int i = 0; i < nfree; i += 2) {
-    load_k<T, D>(kseg, row_of(min(i + 1, nblk - 1)), half, kf[1]);
+  if (nfree > 0) {
+    load_k<T, D>(kseg, row_of(min(1, nblk - 1)), half, kf[1]);
     __builtin_amdgcn_sched_barrier(0);
-    block(kf[0], kb + 32 * i, std::false_type{});
-    if (i + 1 >= nfree) break;
-    load_k<T, D>(kseg, row_of(min(i + 2, nblk - 1)), half, kf[0]);
+    block(kf[0], kb, std::false_type{}, std::false_type{});
+    for (int i = 1; i < nfree; i += 2) {
+      load_k<T, D>(kseg, row_of(min(i + 1, nblk - 1)), half, kf[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      block(kf[1], kb + 32 * i, std::false_type{}, std::true_type{});
+      if (i + 1 >= nfree) break;
+      load_k<T, D>(kseg, row_of(min(i + 2, nblk - 1)), half, kf[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      block(kf[0], kb + 32 * (i + 1), std::false_type{}, std::true_type{});
+    }
     __builtin_amdgcn_sched_barrier(0);
-    block(kf[1], kb + 32 * (i + 1), std::false_type{});
+    bool redo = false;
+#pragma unroll
+    for (int rb = 0; rb < RBN; ++rb) redo |= !(Lr[rb] < 0x1p24f);
+    if (__builtin_amdgcn_ballot_w64(redo)) {   // wave-uniform: sum the run again exactly
+#pragma unroll
+      for (int rb = 0; rb < RBN; ++rb) {
+        Mr[rb] = -INFINITY;
+        Lr[rb] = 0.f;
+      }
+      for (int i = 0; i < nfree; ++i) {
+        load_k<T, D>(kseg, row_of(i), half, kf[0]);
+        block(kf[0], kb + 32 * i, std::false_type{}, std::false_type{});
+      }
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   for (int i = nfree; i < nblk; ++i) {
     load_k<T, D>(kseg, row_of(i), half, kf[0]);
-    block(kf[0], kb + 32 * i, std::true_type{});
+    block(kf[0], kb + 32 * i, std::true_type{}, std::false_type{});
   }
   // merge the two half-waves (same row, other 16 keys of each block)
 #pragma unroll
@@ -630,20 +676,24 @@ hipError_t run_rows(int S, int hq, int hkv, int G, int w, int R, int64_t n, int6
   }
   const dim3 grid(tiles, S);
   // register-resident query rows: the Q fragments of all row blocks must fit
-  // in 128 VGPRs (bf16 up to 128 rows of 128 dims; fp32 one row block)
+  // in 128 VGPRs (bf16 up to 128 rows of 128 dims; fp32 one row block).  The
+  // statistics pass is the same when the attention rows are written out, so
+  // it takes the register form there too.
   constexpr bool kRegFits = RBN <= 4 && RBN * Gm::NA <= 32 && (sizeof(T) == 2 || RBN == 1);
-  if constexpr (kRegFits && !PROBS) {
-    {
-      const int kpw = reg_keys_per_wave(S, n, RBN * 32);
-      const int rt = (int)((n + kpw - 1) / kpw);
-      const dim3 rgrid(rt, S);
-      score_stats_reg_kernel<T, D, RBN><<<rgrid, dim3(64), 0, stream>>>(
-          qp, kp, n, hq, hkv, G, w, R, q_pos0, c, stats, rt, kpw);
-      score_reduce_kernel<<<dim3(S), dim3(kReduceThreads), 0, stream>>>(stats, rt, R, rowc);
+  if constexpr (kRegFits) {
+    const int kpw = reg_keys_per_wave(S, n, RBN * 32);
+    const int rt = (int)((n + kpw - 1) / kpw);
+    const dim3 rgrid(rt, S);
+    score_stats_reg_kernel<T, D, RBN><<<rgrid, dim3(64), 0, stream>>>(
+        qp, kp, n, hq, hkv, G, w, R, q_pos0, c, stats, rt, kpw);
+    score_reduce_kernel<<<dim3(S), dim3(kReduceThreads), 0, stream>>>(stats, rt, R, rowc);
+    if constexpr (PROBS)
+      score_final_kernel<T, D, RBN, PROBS><<<grid, dim3(kThreads), lds, stream>>>(
+          qp, kp, n, hq, hkv, G, w, R, q_pos0, c, rowc, scores);
+    else
       score_final_reg_kernel<T, D, RBN><<<rgrid, dim3(64), 0, stream>>>(
           qp, kp, n, hq, hkv, G, w, R, q_pos0, c, rowc, scores, kpw);
-      return hipGetLastError();
-    }
+    return hipGetLastError();
   }
   score_stats_kernel<T, D, RBN><<<grid, dim3(kThreads), lds, stream>>>(
       qp, kp, n, hq, hkv, G, w, R, q_pos0, c, stats, tiles);

@@ -461,6 +461,44 @@ def test_score_drifting_logits(kv, dtype, d, G, w, n, slope):
         pu.check_scores(s_gpu[s], ref, G * w, f"score drift seg {s}")
 
 
+@pytest.mark.parametrize("dtype,d,G,w,n", [("bf16", 128, 4, 32, 6000), ("fp32", 64, 2, 8, 3000),
+                                           ("bf16", 88, 4, 32, 2600)])
+def test_score_late_spikes(kv, dtype, d, G, w, n):
+    """Window statistics when a key far above the others appears after the
+    first key block of a wavefront's run: 1 % of the keys carry a spike of
+    8, 16, 23, 30 or 45 log2 units over a flat background, so some runs keep
+    their first block's maximum as the reference (sums up to 2^23) and
+    others exceed 2^24 and are summed again in the exact form."""
+    kvsel, pipeline, torch = kv
+    _say("score spikes", dtype, d, G, w, n)
+    r = np.random.default_rng(7 * n + d)
+    B, hkv = 1, 2
+    q = np.empty((B, hkv * G, w, d), np.float32)
+    Kf = np.empty((B, hkv, n, d), np.float32)
+    for h in range(hkv):
+        u = r.standard_normal(d)
+        u /= np.linalg.norm(u)
+        a = np.zeros(n)
+        pos = r.choice(np.arange(1, n - w), size=max(4, n // 100), replace=False)
+        a[pos] = r.choice([8.0, 16.0, 23.0, 30.0, 45.0], size=pos.size) / math.log2(math.e)
+        Kf[0, h] = a[:, None] * u[None, :] + 0.3 * r.standard_normal((n, d))
+        q[0, h * G:(h + 1) * G] = (math.sqrt(d) * u[None, :]
+                                   + 0.3 * r.standard_normal((G * w, d))).reshape(G, w, d)
+    store = (lambda x: kvsynth.f32_to_bf16_bits(x)) if dtype == "bf16" else (lambda x: x)
+    q, Kf = store(q), store(Kf)
+    shape = kvsel.make_shape(B, hkv * G, hkv, d, n, dtype, 1 / math.sqrt(d))
+    sc = torch.empty(B * hkv * n, dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvsel.kvsel_score_workspace(shape, w), dtype=torch.uint8, device="cuda")
+    kvsel.kvsel_score(shape, w, n - w, pipeline.device_tensor(q), pipeline.device_tensor(Kf), sc,
+                      ws)
+    torch.cuda.synchronize()
+    s_gpu = pu.to_host(sc).reshape(B * hkv, n)
+    for s in range(B * hkv):
+        ref = oracle.window_scores(oracle.to_f64(q[0, s * G:(s + 1) * G]), oracle.to_f64(Kf[0, s]),
+                                   1 / math.sqrt(d), n - w)
+        pu.check_scores(s_gpu[s], ref, G * w, f"score spikes seg {s}")
+
+
 @pytest.mark.parametrize("dtype,d,G,slope", [("fp32", 128, 4, 1.0), ("fp32", 64, 2, -1.0),
                                              ("bf16", 128, 4, -1.0), ("bf16", 88, 4, 1.0)])
 def test_decode_drifting_logits(kv, dtype, d, G, slope):
