@@ -244,6 +244,20 @@ def _kernel_key(name: str, grid: str) -> str:
     return f"`{short}` (grid {grid})"
 
 
+def _extras_start(names) -> int:
+    """Index of the first dispatch of the extras in a dispatch-ordered list of
+    kernel names: the first LMBA call opens them with its own statistics pass
+    (`score_stats_reg_kernel`, `score_reduce_kernel`) before the kernels only
+    LMBA runs (the probability-writing final pass, the mask, the row select)."""
+    names = list(names)
+    only = ("lmba_row_kernel", "keep_mask_kernel", "score_stats_kernel<", "score_final_kernel<")
+    end = next((i for i, k in enumerate(names) if any(x in k for x in only)), len(names))
+    for prev in ("score_reduce_kernel", "score_stats_reg_kernel<"):
+        if end > 0 and prev in names[end - 1]:
+            end -= 1
+    return end
+
+
 def _dispatches(path: str):
     """Per-dispatch counter values of a rocprofv3 --pmc CSV: [(kernel key,
     kernel name, {counter: value})] in dispatch order (values summed over
@@ -267,13 +281,10 @@ def traffic_table(fetch_csv: str, write_csv: str, factors: dict) -> str:
     for the extras measured after it."""
     import re
     rows = {}
-    lmba_kernels = ("lmba_row_kernel", "keep_mask_kernel", "score_stats_kernel<",
-                    "score_final_kernel<")
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         ds = _dispatches(path)
         # the extras open with the LMBA calls (attention rows, masks, row selects)
-        end = next((i for i, d in enumerate(ds) if any(k in d[1] for k in lmba_kernels)),
-                   len(ds))
+        end = _extras_start(d[1] for d in ds)
         for i, (key, name, c) in enumerate(ds):
             if "kvsel" not in name and "probe" not in name:
                 continue
@@ -354,8 +365,7 @@ def trace_tables(trace_csv: str, layers: int = 32) -> str:
     out = ["| kernel | dispatches | mean µs | min µs | max µs |", "|---|---|---|---|---|"]
     for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         out.append(f"| `{k}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
-    lmba = ("lmba_row_kernel", "keep_mask_kernel", "score_stats_kernel<", "score_final_kernel<")
-    end = next((i for i, d in enumerate(ds) if any(d[1].startswith(x) for x in lmba)), len(ds))
+    end = _extras_start(d[1] for d in ds)
     step = ds[:end]
     out += ["", "C2 step, last graph replay of each phase (µs per dispatch; per layer for the "
             "calls that cover all layers):", "",

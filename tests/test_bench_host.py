@@ -92,3 +92,20 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_extras_start_includes_the_first_lmba_statistics_pass():
+    """The extras open with LMBA, whose statistics pass uses the same kernels as
+    the step's score: the cut steps back over that pass, and only that pass."""
+    k = "void kvsel::(anonymous namespace)::"
+    step = [k + "score_stats_reg_kernel<kvsel::bf16_t, 128, 4>(...)", k + "score_reduce_kernel(...)",
+            k + "score_final_reg_kernel<kvsel::bf16_t, 128, 4>(...)", k + "select_topb_kernel<32>(...)",
+            k + "compact_kernel<16>(...)", k + "decode_split_kernel<kvsel::bf16_t, 128, 4>(...)",
+            k + "decode_combine_head_kernel<4, 128>(...)"]
+    lmba = [k + "score_stats_reg_kernel<kvsel::bf16_t, 128, 4>(...)", k + "score_reduce_kernel(...)",
+            k + "score_final_kernel<kvsel::bf16_t, 128, 4, true>(...)", k + "keep_mask_kernel(...)",
+            k + "lmba_row_kernel<64>(...)"]
+    assert bench._extras_start(step + lmba) == len(step)
+    assert bench._extras_start(step) == len(step)
+    # an LMBA call without its own statistics pass in front: nothing is taken back
+    assert bench._extras_start(step + lmba[2:]) == len(step)
