@@ -721,8 +721,12 @@ def main() -> int:
     from sparse_decode_attention_window_amd import _probe as probe
     read_ceiling = stream_ceiling(torch, probe, probe.PROBE_READ, int(dec_bytes))
     copy_ceiling = stream_ceiling(torch, probe, probe.PROBE_COPY, int(cmp_bytes))
+    # the step compacts all L layers in one call: the same bytes as one long copy
+    copy_ceiling_all = stream_ceiling(torch, probe, probe.PROBE_COPY, int(cmp_bytes * L),
+                                      nb=2, calls=2)
     log(f"[bench] stream ceilings at the call sizes: read {read_ceiling:.0f} GB/s, "
-        f"copy {copy_ceiling:.0f} GB/s")
+        f"copy {copy_ceiling:.0f} GB/s (one layer's bytes per call), "
+        f"{copy_ceiling_all:.0f} GB/s (all layers' bytes in one call)")
     traffic = None
     if os.path.exists(COUNTERS):
         with open(COUNTERS) as f:
@@ -803,8 +807,8 @@ def main() -> int:
                        "GBps": round(gbs(dec_bytes, dec_alone_us), 1),
                        "note": "the same 32-layer decode graph replayed back to back, outside "
                                "the timed step; inside the step the decode follows the "
-                               "compaction and also pays the write-back of the lines it left "
-                               "dirty in the caches"},
+                               "compaction, whose non-temporal stores leave no dirty lines "
+                               "for it to write back"},
                    "serving_loop_c2": {
                        "us_per_layer_step": round(serve_us, 2),
                        "us_per_layer_step_one_loop_per_layer": round(serve_layer_us, 2),
@@ -822,11 +826,15 @@ def main() -> int:
         "hbm_stream_ceilings": {
             "read_GBps": round(read_ceiling, 1), "read_bytes_per_call": int(dec_bytes),
             "copy_GBps": round(copy_ceiling, 1), "copy_bytes_per_call": int(cmp_bytes),
+            "copy_GBps_all_layers_one_call": round(copy_ceiling_all, 1),
+            "copy_bytes_all_layers_one_call": int(cmp_bytes * L),
             "method": "libkvsel_probe.so non-temporal read / copy streams at the decode and "
                       "compact call sizes, graph of 8 back-to-back calls over 4 rotating "
-                      "buffers"},
+                      "buffers; the all-layers copy (the step's compaction is one call for "
+                      "every layer) as 2 calls over 2 buffers"},
         "decode_frac_of_read_ceiling": round(dec_gbs / read_ceiling, 4),
         "compact_frac_of_copy_ceiling": round(cmp_gbs / copy_ceiling, 4),
+        "compact_frac_of_copy_ceiling_all_layers_one_call": round(cmp_gbs / copy_ceiling_all, 4),
         "stages_roofline": {
             "score": {"bound": "hbm", "GB/s": round(gbs(sc_bytes, us["score"]), 1),
                       "frac": round(gbs(sc_bytes, us["score"]) / PEAK_HBM_GBS, 4),
