@@ -199,8 +199,14 @@ __device__ __forceinline__ void compute_tile(WaveState<T, D, HG>& st, const Tile
     }
   }
 #pragma unroll
-  for (int h = 0; h < HG; ++h)
+  for (int h = 0; h < HG; ++h) {
     p[h] = __builtin_amdgcn_exp2f(x[h] - (st.m[h] == -INFINITY ? 0.f : st.m[h]));
+    st.l[h] += p[h];   // this lane's key; summed over the row's 16 keys at the end
+  }
+  // (the sums of exponentials are kept per key slot, one add per head per
+  // tile, and reduced over the row's 16 lanes once at the end: 27.5 -> 27.3
+  // us per layer in the 32-layer step against summing the four broadcast
+  // probabilities in every lane)
   // probabilities of the tile's 16 keys to every lane through LDS (4 heads
   // per float4; with eight heads the second four follow the first 16)
   if constexpr (HG <= 4) {
@@ -224,8 +230,6 @@ __device__ __forceinline__ void compute_tile(WaveState<T, D, HG>& st, const Tile
       pk[6] = pw.z;
       pk[7] = pw.w;
     }
-#pragma unroll
-    for (int h = 0; h < HG; ++h) st.l[h] += pk[h];
 #pragma unroll
     for (int x = 0; x < Gm::CPL; ++x) {
       float v[Gm::EPV];
@@ -351,8 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(
   // fold the four key slots (lane groups) together
 #pragma unroll
   for (int h = 0; h < HG; ++h) {
-    st.l[h] += __shfl_xor(st.l[h], 16);
-    st.l[h] += __shfl_xor(st.l[h], 32);
+    st.l[h] = row_sum16(st.l[h]);   // every lane group holds the same keys' sums
 #pragma unroll
     for (int x = 0; x < Gm::CPL; ++x)
 #pragma unroll

@@ -190,6 +190,16 @@ __device__ __forceinline__ float row_max16(float v) {
   return v;
 }
 
+// Sum over the 16 lanes of a DPP row, in every lane of the row (each step
+// adds the lane that holds the other half's partial sum).
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);   // row_half_mirror
+  v += dpp_mov<0x140>(v);   // row_mirror
+  return v;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wavefront, DPP only (no LDS).
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
   int x = (int)v;
