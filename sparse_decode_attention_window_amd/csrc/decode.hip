@@ -262,7 +262,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(
   const int64_t item = blockIdx.x;
   const int64_t rows_per_item = (int64_t)kWaves * rpw;
   const uint32_t rpi = (uint32_t)rows_per_item;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // wid through readfirstlane: every row bound and tile base derived from it
+  // is then known to be wave-uniform and kept in scalar registers instead of
+  // being recomputed per lane (26.6 -> 25.95 us per layer in the 32-layer
+  // step, same outputs)
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4, l16 = lane & 15;
   // The first tile's loads go out before the segment lookup returns, on the
   // guess that the segments are equal, r_cap / S rows each back to back (a
