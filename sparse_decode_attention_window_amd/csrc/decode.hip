@@ -286,6 +286,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(
   const int64_t gabs = gs * glen + grow0;
   const int glim = spec ? (int)min((int64_t)kTile - 1, grow1 - 1 - grow0) : 0;
   if (spec) load_tile(ra, kc + gabs * Gm::RB, vc + gabs * Gm::RB, glim, grp, l16);
+  // the guessed segment's query rows too (plain queries only; 26.0 -> 25.7 us
+  // per layer in the 32-layer step, C4 52.3 -> 51.6 us)
+  u32x4 qf[Gm::NA];
+  const int hl = l16 % HG;
+  const bool qspec = !rope.cs;
+  if (qspec) {
+    const int bg = (int)gs / hkv, kg = (int)gs - ((int)gs / hkv) * hkv;
+    const char* qrow = q + ((int64_t)bg * hq + (int64_t)kg * G + hl) * Gm::RB;
+#pragma unroll
+    for (int a = 0; a < Gm::NA; ++a) {
+      const int o = 64 * a + 16 * grp;
+      qf[a] = (hl < G && o < Gm::RB) ? load16(qrow + o) : u32x4{0, 0, 0, 0};
+    }
+  }
   const SegLoc loc = wave_locate(seg_off, seg_len, S, r_cap, item, true,
                                  [=](uint32_t l) { return (l + rpi - 1) / rpi; });
   if (loc.s < 0) return;  // same answer in every wave of the block
@@ -301,9 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(
   float4* sp = sp_all[wid];
 
   // A operand: query head (l16 % HG) of this KV head, 16 bytes per 64-byte step
-  u32x4 qf[Gm::NA];
-  {
-    const int hl = l16 % HG;
+  if (!(qspec && s == (int)gs)) {
     const char* qrow = q + ((int64_t)b * hq + (int64_t)kvh * G + hl) * Gm::RB;
     if (rope.cs) {
       // unrotated queries: rotate the G rows at q_pos once into LDS (sm_o is
