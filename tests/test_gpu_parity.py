@@ -538,6 +538,56 @@ def test_decode_drifting_logits(kv, dtype, d, G, slope):
             assert err <= pu.OUT_ATOL[dtype], (s, g, err)
 
 
+@pytest.mark.parametrize("dtype,d,G", [("fp32", 128, 4), ("bf16", 128, 4), ("bf16", 88, 4),
+                                       ("bf16", 128, 8)])
+def test_decode_late_spikes(kv, dtype, d, G):
+    """Split-K decode whose exponent reference is set by an ordinary bulk of
+    keys (logits spread about 1.4 log2 units around zero) and then overtaken
+    late in each segment: keys aligned with a query head lift its logit to
+    7.5, 8.5, 14, 22 and 40 log2 units at positions past most of the
+    segment's tiles, so a wavefront either keeps a reference that a logit
+    passes by less than its margin or moves it (and rescales its sums) after
+    many tiles."""
+    kvsel, pipeline, torch = kv
+    _say("decode spikes", dtype, d, G)
+    r = np.random.default_rng(7000 + d + G)
+    B, hkv = 1, 2
+    S = B * hkv
+    lens = np.array([9000, 2500], np.int32)
+    off, r_cap = pipeline.offsets(lens.astype(np.int64))
+    c = math.log2(math.e) / math.sqrt(d)             # log2 units per unit of q.k
+    Kc = r.standard_normal((r_cap, d)).astype(np.float32)
+    q = r.standard_normal((B, hkv * G, d)).astype(np.float32)
+    for s in range(S):
+        n = int(lens[s])
+        for j, (frac, lift) in enumerate([(0.55, 7.5), (0.62, 8.5), (0.71, 14.0), (0.83, 22.0),
+                                          (0.97, 40.0)]):
+            h = (j % G)
+            qh = q[0, s * G + h]
+            Kc[off[s] + int(frac * n)] = qh * (lift / c / float(qh @ qh))
+    Vc = r.standard_normal((r_cap, d)).astype(np.float32)
+    store = (lambda x: kvsynth.f32_to_bf16_bits(x)) if dtype == "bf16" else (lambda x: x)
+    Kc, Vc, q = store(Kc), store(Vc), store(q)
+    shape = kvsel.make_shape(B, hkv * G, hkv, d, int(lens.max()), dtype, 1 / math.sqrt(d))
+    out = torch.empty((B, hkv * G, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvsel.kvsel_decode_workspace(shape, r_cap), dtype=torch.uint8, device="cuda")
+    kvsel.kvsel_decode_attn(shape, pipeline.device_tensor(q), pipeline.device_tensor(Kc),
+                            pipeline.device_tensor(Vc), pipeline.device_tensor(off),
+                            pipeline.device_tensor(lens), r_cap, out, ws)
+    torch.cuda.synchronize()
+    o = pu.to_host(out)
+    worst = 0.0
+    for s in range(S):
+        rows = np.arange(off[s], off[s] + lens[s])
+        for g in range(G):
+            ref = oracle.decode_attention(oracle.to_f64(q[0, s * G + g]), oracle.to_f64(Kc[rows]),
+                                          oracle.to_f64(Vc[rows]), 1 / math.sqrt(d))
+            err = float(np.max(np.abs(o[0, s * G + g] - ref)))
+            worst = max(worst, err)
+            assert err <= pu.OUT_ATOL[dtype], (s, g, err)
+    pu.record(f"decode_abs_{dtype}", worst)
+
+
 # ---------------------------------------------------------------------------
 # workspace state and graph replays
 # ---------------------------------------------------------------------------
