@@ -259,8 +259,9 @@ kvsel_status kvsel_compact(const kvsel_shape* s /*host*/, const void* k, const v
  *   out[b][h] = sum_{r < len} softmax_r(scale q[b][h] . k_c[off + r]) v_c[off + r]
  * with off = seg_off[b*hkv + h/G], len = seg_len[...] (clipped at r_cap).
  * Split-K: every segment is cut into row chunks processed in parallel; each
- * chunk keeps (running max, sum of exponentials, weighted value sum) and a
- * second pass merges them.  An empty segment gives a zero output row.
+ * chunk keeps (an exponent reference at or within 8 log2 units below its
+ * largest logit, sum of exponentials, weighted value sum) and a second pass
+ * merges them.  An empty segment gives a zero output row.
  *   q    [batch][hq][head_dim]
  *   k_c, v_c [r_cap][head_dim]
  *   out  [batch][hq][head_dim] fp32 (out)
